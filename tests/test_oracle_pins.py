@@ -1,0 +1,373 @@
+"""Pins of the float64 oracle against facts that do not come from the oracle.
+
+Each test pins the oracle to something outside it: numbers the pages print
+(golden fixtures with citations), closed forms, invariants, library routines
+the oracle does not call (torch's LayerNorm, GELU, scaled-dot-product
+attention, post-norm TransformerEncoderLayer, and the Hugging Face ALBERT
+model with one shared layer group), and a loop-by-loop brute force.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+import oracle
+from oracle import brute
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+K = synth.KOKORO
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _w64(cfg=K, seed=synth.WEIGHT_SEED, dtype="f32"):
+    return oracle.prepare_weights(synth.make_weights(cfg, seed), dtype)
+
+
+# ---------------------------------------------------------------- shapes ----
+
+def test_param_counts_match_printed_arithmetic():
+    g = _golden("param_counts.json")
+    c = oracle.param_counts(K)
+    for key, val in g["factorized"].items():
+        assert c[key] == val, key
+    assert c["unfactorized_total"] == g["unfactorized"]["unfactorized_total"]
+    assert c["savings"] == g["savings"]
+    # ~65 % saving as printed
+    assert round(100 * c["savings"] / c["unfactorized_total"]) == 65
+
+
+def test_config_matches_pages():
+    g = _golden("kokoro_config.json")
+    for key in ("vocab", "max_pos", "n_types", "emb", "hidden", "heads",
+                "head_dim", "ffn", "n_iter", "out_dim", "ln_eps"):
+        assert getattr(K, key) == g[key], key
+    assert K.heads * K.head_dim == K.hidden
+    shapes = K.shapes()
+    w = synth.make_weights()
+    for name in synth.TENSOR_NAMES:
+        assert w[name].shape == shapes[name]
+
+
+# ------------------------------------------------------------ primitives ----
+
+def test_bf16_round_matches_torch():
+    rng = np.random.default_rng(5)
+    x = np.concatenate([
+        rng.normal(0, 0.02, 4096), rng.normal(0, 30, 4096),
+        rng.uniform(-1e-30, 1e-30, 512)]).astype(np.float32)
+    # exact halves between two bf16 neighbours: both tie directions
+    base = rng.normal(0, 1, 512).astype(np.float32).view(np.uint32) & np.uint32(0xFFFF0000)
+    ties = (base | np.uint32(0x8000)).view(np.float32)
+    x = np.concatenate([x, ties, np.array([0.0, -0.0, 1.0, -3.5], np.float32)])
+    want = torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
+    got = oracle.bf16_round(x)
+    assert np.array_equal(got, want)
+
+
+def test_softmax_rows_sum_to_one():
+    rng = np.random.default_rng(1)
+    s = rng.normal(0, 5, (64, 37))
+    p = oracle.softmax(s)
+    assert np.all(p > 0)
+    assert np.max(np.abs(p.sum(-1) - 1.0)) < 1e-14
+    # shift invariance of a row softmax
+    assert np.allclose(oracle.softmax(s + 100.0), p, rtol=1e-12, atol=0)
+
+
+def test_layer_norm_moments_and_torch():
+    rng = np.random.default_rng(2)
+    x = rng.normal(3.0, 2.0, (50, 768))
+    y = oracle.layer_norm(x, np.ones(768), np.zeros(768), 1e-12)
+    assert np.max(np.abs(y.mean(-1))) < 1e-13
+    var = y.var(-1)
+    assert np.max(np.abs(var - 1.0)) < 1e-12
+    g = rng.normal(1, 0.1, 768)
+    b = rng.normal(0, 0.1, 768)
+    ref = torch.nn.functional.layer_norm(torch.from_numpy(x), (768,), torch.from_numpy(g),
+                                         torch.from_numpy(b), eps=1e-12).numpy()
+    assert np.max(np.abs(oracle.layer_norm(x, g, b, 1e-12) - ref)) < 1e-12
+
+
+def test_layer_norm_epsilon_inside_sqrt():
+    # a constant row has zero variance: the output is exactly the shift b,
+    # and a tiny-variance row is scaled by 1/sqrt(var + eps)
+    x = np.array([[0.5, 0.5, 0.5, 0.5], [1.0, -1.0, 1.0, -1.0]]) * np.array([[1.0], [1e-6]])
+    y = oracle.layer_norm(x, np.ones(4), np.full(4, 0.25), 1e-12)
+    assert np.array_equal(y[0], np.full(4, 0.25))
+    expect = 1e-6 / math.sqrt(1e-12 + 1e-12)
+    assert abs(y[1, 0] - (expect + 0.25)) < 1e-12
+
+
+def test_gelu_tanh_identities_and_torch():
+    rng = np.random.default_rng(3)
+    x = np.concatenate([rng.normal(0, 3, 10000), np.linspace(-12, 12, 2001)])
+    g = oracle.gelu_tanh(x)
+    assert np.max(np.abs(g - oracle.gelu_tanh(-x) - x)) < 1e-14
+    assert oracle.gelu_tanh(np.array([0.0]))[0] == 0.0
+    ref = torch.nn.functional.gelu(torch.from_numpy(x), approximate="tanh").numpy()
+    assert np.max(np.abs(g - ref)) < 1e-14
+    # the erf form is a different function (the variant matters)
+    erf = torch.nn.functional.gelu(torch.from_numpy(x)).numpy()
+    assert np.max(np.abs(g - erf)) > 1e-4
+
+
+def test_dense_orientation():
+    # y[j] = b[j] + sum_i x[i] W[j, i]: a non-square W fixes the orientation
+    x = np.array([[1.0, 2.0, 3.0]])
+    W = np.array([[1.0, 0.0, 0.0], [0.0, 10.0, 100.0]])
+    b = np.array([0.5, -0.5])
+    assert np.array_equal(oracle.dense(x, W, b), np.array([[1.5, 319.5]]))
+
+
+def test_attention_matches_torch_sdpa_with_mask():
+    rng = np.random.default_rng(4)
+    L, H, heads, T = 9, 768, 12, 16
+    q, k, v = (rng.normal(0, 1, (L, H)) for _ in range(3))
+    got = oracle.attention(q, k, v, heads)
+    # the same sequence inside a padded block of T with an additive -inf mask
+    pad = lambda a: np.concatenate([a, rng.normal(0, 5, (T - L, H))])
+    th = lambda a: torch.from_numpy(pad(a)).view(T, heads, 64).transpose(0, 1)[None]
+    mask = torch.zeros(1, 1, T, T, dtype=torch.float64)
+    mask[..., L:] = -math.inf
+    ref = torch.nn.functional.scaled_dot_product_attention(th(q), th(k), th(v), attn_mask=mask)
+    ref = ref[0].transpose(0, 1).reshape(T, H).numpy()[:L]
+    assert np.max(np.abs(got - ref)) < 1e-13
+
+
+def test_attention_single_key_is_value():
+    rng = np.random.default_rng(6)
+    q, k, v = (rng.normal(0, 1, (1, 768)) for _ in range(3))
+    assert np.array_equal(oracle.attention(q, k, v, 12), v)
+
+
+def test_zero_query_key_gives_mean_of_values():
+    W = _w64()
+    for name in ("q.w", "q.b", "k.w", "k.b"):
+        W[name] = np.zeros_like(W[name])
+    rng = np.random.default_rng(7)
+    h = rng.normal(0, 1, (11, 768))
+    taps = {}
+    oracle.shared_layer(h, W, K, taps)
+    mean_v = taps["v"].mean(axis=0)
+    assert np.max(np.abs(taps["ctx"] - mean_v[None, :])) < 1e-14
+
+
+# ------------------------------------------------- whole-layer / encoder ----
+
+def test_layer_matches_torch_post_norm_encoder_layer():
+    W = _w64()
+    rng = np.random.default_rng(8)
+    L = 13
+    h = rng.normal(0, 1, (L, 768))
+    layer = torch.nn.TransformerEncoderLayer(
+        768, 12, 2048, dropout=0.0,
+        activation=lambda t: torch.nn.functional.gelu(t, approximate="tanh"),
+        layer_norm_eps=1e-12, batch_first=True, norm_first=False).double().eval()
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a))
+    with torch.no_grad():
+        layer.self_attn.in_proj_weight.copy_(t(np.concatenate([W["q.w"], W["k.w"], W["v.w"]])))
+        layer.self_attn.in_proj_bias.copy_(t(np.concatenate([W["q.b"], W["k.b"], W["v.b"]])))
+        layer.self_attn.out_proj.weight.copy_(t(W["o.w"]))
+        layer.self_attn.out_proj.bias.copy_(t(W["o.b"]))
+        layer.linear1.weight.copy_(t(W["ffn1.w"]))
+        layer.linear1.bias.copy_(t(W["ffn1.b"]))
+        layer.linear2.weight.copy_(t(W["ffn2.w"]))
+        layer.linear2.bias.copy_(t(W["ffn2.b"]))
+        layer.norm1.weight.copy_(t(W["attn_ln.g"]))
+        layer.norm1.bias.copy_(t(W["attn_ln.b"]))
+        layer.norm2.weight.copy_(t(W["ffn_ln.g"]))
+        layer.norm2.bias.copy_(t(W["ffn_ln.b"]))
+        ref = layer(t(h)[None])[0].numpy()
+    got = oracle.shared_layer(h, W, K)
+    assert np.max(np.abs(got - ref)) < 1e-11
+
+
+def _hf_albert(W, n_iter=12):
+    transformers = pytest.importorskip("transformers")
+    cfg = transformers.AlbertConfig(
+        vocab_size=178, embedding_size=128, hidden_size=768, num_hidden_layers=n_iter,
+        num_hidden_groups=1, num_attention_heads=12, intermediate_size=2048,
+        inner_group_num=1, hidden_act="gelu_new", hidden_dropout_prob=0.0,
+        attention_probs_dropout_prob=0.0, max_position_embeddings=512,
+        type_vocab_size=2, layer_norm_eps=1e-12)
+    cfg._attn_implementation = "eager"
+    m = transformers.AlbertModel(cfg, add_pooling_layer=False).double().eval()
+    sd = {
+        "embeddings.word_embeddings.weight": "emb.word",
+        "embeddings.position_embeddings.weight": "emb.pos",
+        "embeddings.token_type_embeddings.weight": "emb.type",
+        "embeddings.LayerNorm.weight": "emb.ln.g",
+        "embeddings.LayerNorm.bias": "emb.ln.b",
+        "encoder.embedding_hidden_mapping_in.weight": "proj.w",
+        "encoder.embedding_hidden_mapping_in.bias": "proj.b",
+    }
+    pre = "encoder.albert_layer_groups.0.albert_layers.0."
+    sd.update({pre + "attention.query.weight": "q.w", pre + "attention.query.bias": "q.b",
+               pre + "attention.key.weight": "k.w", pre + "attention.key.bias": "k.b",
+               pre + "attention.value.weight": "v.w", pre + "attention.value.bias": "v.b",
+               pre + "attention.dense.weight": "o.w", pre + "attention.dense.bias": "o.b",
+               pre + "attention.LayerNorm.weight": "attn_ln.g",
+               pre + "attention.LayerNorm.bias": "attn_ln.b",
+               pre + "ffn.weight": "ffn1.w", pre + "ffn.bias": "ffn1.b",
+               pre + "ffn_output.weight": "ffn2.w", pre + "ffn_output.bias": "ffn2.b",
+               pre + "full_layer_layer_norm.weight": "ffn_ln.g",
+               pre + "full_layer_layer_norm.bias": "ffn_ln.b"})
+    params = dict(m.named_parameters())
+    assert set(params) == set(sd)
+    with torch.no_grad():
+        for hf, ours in sd.items():
+            params[hf].copy_(torch.from_numpy(np.ascontiguousarray(W[ours])))
+    return m
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_encoder_matches_hf_albert_shared_group(dtype):
+    """The Hugging Face ALBERT encoder with one layer group (fully shared)
+    and 12 hidden layers, followed by the 768->512 projection, is the same
+    function; padded slots are masked by its additive attention mask."""
+    W = _w64(dtype=dtype)
+    m = _hf_albert(W)
+    wl = synth.random_padded(11, B=3, T=24, lo=5, hi=24)
+    ids = torch.from_numpy(wl.ids.astype(np.int64))
+    am = (torch.arange(wl.T)[None, :] < torch.from_numpy(wl.lengths)[:, None]).long()
+    with torch.no_grad():
+        hid = m(input_ids=ids, attention_mask=am, token_type_ids=torch.zeros_like(ids)).last_hidden_state
+    ref = hid.numpy() @ W["out.w"].T + W["out.b"]
+    got = oracle.encode(wl.ids, wl.lengths, W, K)
+    for b in range(3):
+        L = int(wl.lengths[b])
+        assert np.max(np.abs(got[b, :L] - ref[b, :L])) < 1e-11
+        assert np.all(got[b, L:] == 0.0)
+
+
+def test_brute_force_agrees_on_tiny_shapes():
+    cfg = synth.TINY
+    W = _w64(cfg, seed=99)
+    rng = np.random.default_rng(12)
+    for L in (1, 2, 3, 4):
+        ids = rng.integers(0, cfg.vocab, L)
+        got = oracle.encode_sequence(ids, W, cfg)
+        ref = np.array(brute.encode_brute(ids, W, cfg))
+        assert np.max(np.abs(got - ref)) < 1e-12, L
+
+
+def test_shared_schedule_equals_repeated_layer_and_distinct_copies():
+    cfg = synth.TINY
+    W = _w64(cfg, seed=17)
+    ids = np.array([3, 1, 4, 1, 5])
+    rng_ids = ids[:cfg.max_pos]
+    out = oracle.encode_sequence(rng_ids, W, cfg)
+    # layer applied n_iter times by hand
+    h = oracle.dense(oracle.embed_ln(rng_ids, W, cfg), W["proj.w"], W["proj.b"])
+    for _ in range(cfg.n_iter):
+        h = oracle.shared_layer(h, W, cfg)
+    assert np.array_equal(out, oracle.dense(h, W["out.w"], W["out.b"]))
+    # a model with n_iter distinct layers given identical copies
+    layer = {k: W[k] for k in brute.LAYER_KEYS}
+    copies = np.array(brute.encode_brute(rng_ids, W, cfg, layers=[dict(layer)] * cfg.n_iter))
+    assert np.max(np.abs(out - copies)) < 1e-12
+    # ... and distinct layers are a different function
+    W2 = _w64(cfg, seed=18)
+    other = {k: W2[k] for k in brute.LAYER_KEYS}
+    mixed = np.array(brute.encode_brute(rng_ids, W, cfg, layers=[layer, other, layer]))
+    assert np.max(np.abs(out - mixed)) > 1e-3
+
+
+def test_one_iteration_is_one_layer():
+    W = _w64()
+    ids = np.array([0, 5, 9, 0])
+    h0 = oracle.dense(oracle.embed_ln(ids, W, K), W["proj.w"], W["proj.b"])
+    h1 = oracle.shared_layer(h0, W, K)
+    assert np.array_equal(oracle.encode_sequence(ids, W, K, n_iter=1),
+                          oracle.dense(h1, W["out.w"], W["out.b"]))
+
+
+def test_pad_invariance():
+    W = _w64(dtype="bf16")
+    wl = synth.random_padded(21, B=3, T=20, lo=4, hi=17)
+    base = oracle.encode(wl.ids, wl.lengths, W, K)
+    # change every pad-slot id (even to ids outside the vocabulary: never read)
+    ids2 = wl.ids.copy()
+    for b, L in enumerate(wl.lengths):
+        ids2[b, L:] = (np.arange(wl.T - L) * 37) % 1000 - 3
+    assert np.array_equal(oracle.encode(ids2, wl.lengths, W, K), base)
+    # more padding (larger T)
+    ids3 = np.concatenate([wl.ids, np.zeros((3, 9), np.int32)], axis=1)
+    assert np.array_equal(oracle.encode(ids3, wl.lengths, W, K)[:, :wl.T], base)
+    # a sequence alone == inside the padded batch == inside a packed batch
+    b = 1
+    L = int(wl.lengths[b])
+    alone = oracle.encode_sequence(wl.ids[b, :L], W, K)
+    assert np.array_equal(alone, base[b, :L])
+    packed = np.concatenate([wl.ids[i, :wl.lengths[i]] for i in range(3)])
+    cu = np.concatenate([[0], np.cumsum(wl.lengths)])
+    pv = oracle.encode_varlen(packed, cu, W, K)
+    assert np.array_equal(pv[cu[b]:cu[b + 1]], alone)
+    assert np.all(base[b, L:] == 0.0)
+
+
+def test_permutation_equivariance_without_positions():
+    W = _w64()
+    W["emb.pos"] = np.zeros_like(W["emb.pos"])
+    ids = np.array([7, 100, 3, 55, 9, 177])
+    perm = np.array([4, 0, 5, 2, 1, 3])
+    a = oracle.encode_sequence(ids, W, K, n_iter=2)
+    b = oracle.encode_sequence(ids[perm], W, K, n_iter=2)
+    assert np.max(np.abs(a[perm] - b)) < 1e-12
+    # with the position table the order matters
+    W2 = _w64()
+    a2 = oracle.encode_sequence(ids, W2, K, n_iter=2)
+    b2 = oracle.encode_sequence(ids[perm], W2, K, n_iter=2)
+    assert np.max(np.abs(a2[perm] - b2)) > 1e-3
+
+
+def test_validate_rejections():
+    ids = np.zeros((2, 8), np.int32)
+    oracle.validate(ids, np.array([8, 1]), 8, K)
+    with pytest.raises(oracle.OracleError) as e:
+        oracle.validate(ids, np.array([9, 1]), 8, K)
+    assert e.value.code == "E_LENGTH"
+    with pytest.raises(oracle.OracleError) as e:
+        oracle.validate(ids, np.array([0, 1]), 8, K)
+    assert e.value.code == "E_LENGTH"
+    bad = ids.copy()
+    bad[1, 0] = 178
+    with pytest.raises(oracle.OracleError) as e:
+        oracle.validate(bad, np.array([8, 1]), 8, K)
+    assert e.value.code == "E_ID"
+    bad[1, 0] = 0
+    bad[1, 5] = -4      # pad slot of sequence 1: never read
+    oracle.validate(bad, np.array([8, 1]), 8, K)
+    with pytest.raises(oracle.OracleError):
+        oracle.validate(np.zeros((1, 513), np.int32), np.array([513]), 513, K)
+
+
+# ------------------------------------------------------------ durations ----
+
+def test_duration_toy_from_page():
+    g = _golden("duration_toy.json")
+    x = np.array(g["tokens"], dtype=object)[:, None]
+    out, A = oracle.expand_durations(x, np.array(g["durations"]))
+    assert A == g["frames"]
+    assert [r[0] for r in out] == g["aligned"]
+
+
+def test_duration_rule_closed_forms():
+    # sigmoid(0) = 1/2: four zero channels sum to 2 frames; speed 2 gives 1
+    z = np.zeros((3, 4))
+    assert oracle.duration_from_logits(z).tolist() == [2, 2, 2]
+    assert oracle.duration_from_logits(z, speed=2.0).tolist() == [1, 1, 1]
+    # very negative logits would round to 0 frames: clamped to 1
+    assert oracle.duration_from_logits(np.full((2, 50), -40.0)).tolist() == [1, 1]
+    # very positive logits: every channel counts one frame
+    assert oracle.duration_from_logits(np.full((1, 50), 40.0)).tolist() == [50]
+    with pytest.raises(oracle.OracleError):
+        oracle.expand_durations(np.zeros((2, 3)), np.array([1, 0]))
