@@ -1,0 +1,214 @@
+"""ctypes binding of libalbert.so (the C ABI in include/albert.h).
+
+Argument marshalling only: every step of the encoder runs in the library's
+HIP kernels.  PyTorch supplies device memory and the current stream.  The
+binding refuses to work without the compiled library -- there is no CPU
+fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libalbert.so")
+
+OK, E_ARG, E_WORKSPACE, E_LENGTH, E_ID, E_ALIAS, E_HIP = range(7)
+STATUS_NAMES = {OK: "OK", E_ARG: "E_ARG", E_WORKSPACE: "E_WORKSPACE",
+                E_LENGTH: "E_LENGTH", E_ID: "E_ID", E_ALIAS: "E_ALIAS", E_HIP: "E_HIP"}
+F32, BF16 = 0, 1
+ASYNC = 1
+N_TENSORS = 25
+TAPS = {"status": 0, "cu": 1, "row_seq": 2, "row_pos": 3, "emb": 4, "x": 5,
+        "qkv": 6, "ctx": 7, "x1": 8, "g": 9}
+
+EXPORTS = ("albert_default_config", "albert_tensor_name", "albert_tensor_shape",
+           "albert_load_weights", "albert_workspace_bytes", "albert_encode",
+           "albert_encode_varlen", "albert_read_status", "albert_tap", "albert_free",
+           "albert_status_str")
+
+
+class Config(ctypes.Structure):
+    _fields_ = [("vocab", ctypes.c_int32), ("max_pos", ctypes.c_int32),
+                ("n_types", ctypes.c_int32), ("emb", ctypes.c_int32),
+                ("hidden", ctypes.c_int32), ("heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("ffn", ctypes.c_int32),
+                ("n_iter", ctypes.c_int32), ("out_dim", ctypes.c_int32),
+                ("ln_eps", ctypes.c_float)]
+
+
+_LIB = None
+
+
+def lib():
+    """Load libalbert.so once; raise if it has not been built."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m albert_transformer_amd.build` (no fallback exists)")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
+    L.albert_default_config.argtypes = [ctypes.POINTER(Config)]
+    L.albert_default_config.restype = i32
+    L.albert_tensor_name.argtypes = [i32]
+    L.albert_tensor_name.restype = ctypes.c_char_p
+    L.albert_tensor_shape.argtypes = [ctypes.POINTER(Config), i32,
+                                      ctypes.POINTER(i64), ctypes.POINTER(i64)]
+    L.albert_tensor_shape.restype = i32
+    L.albert_load_weights.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(Config),
+                                      ctypes.POINTER(vp), i32, vp]
+    L.albert_load_weights.restype = i32
+    L.albert_workspace_bytes.argtypes = [vp, i32, i64]
+    L.albert_workspace_bytes.restype = sz
+    L.albert_encode.argtypes = [vp, vp, vp, i32, i32, vp, vp, sz, vp, ctypes.c_uint]
+    L.albert_encode.restype = i32
+    L.albert_encode_varlen.argtypes = [vp, vp, vp, i32, i32, i32, vp, vp, sz, vp,
+                                       ctypes.c_uint]
+    L.albert_encode_varlen.restype = i32
+    L.albert_read_status.argtypes = [vp, vp]
+    L.albert_read_status.restype = i32
+    L.albert_tap.argtypes = [vp, i32, i64, i32, ctypes.POINTER(sz), ctypes.POINTER(sz),
+                             ctypes.POINTER(i64)]
+    L.albert_tap.restype = i32
+    L.albert_free.argtypes = [vp]
+    L.albert_free.restype = None
+    L.albert_status_str.argtypes = [i32]
+    L.albert_status_str.restype = ctypes.c_char_p
+    _LIB = L
+    return L
+
+
+def default_config(**overrides) -> Config:
+    c = Config()
+    lib().albert_default_config(ctypes.byref(c))
+    for k, v in overrides.items():
+        setattr(c, k, v)
+    return c
+
+
+def status_str(code: int) -> str:
+    return lib().albert_status_str(code).decode()
+
+
+class AlbertError(RuntimeError):
+    def __init__(self, code: int, what: str):
+        super().__init__(f"{what}: {STATUS_NAMES.get(code, code)} ({status_str(code)})")
+        self.code = code
+
+
+def _ptr(t) -> int:
+    return 0 if t is None else int(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(int(s.cuda_stream))
+
+
+class Encoder:
+    """One device-resident copy of the encoder weights (an albert_ctx).
+
+    weights: dict of canonical name -> float32 numpy array (see
+    ``synth.TENSOR_NAMES``); dtype "bf16" or "f32"; config overrides as
+    keyword arguments (e.g. n_iter=1).
+    """
+
+    def __init__(self, weights: dict, dtype: str = "bf16", stream=None, **cfg):
+        import torch  # noqa: F401  (HIP runtime shared with torch)
+        L = lib()
+        self.cfg = default_config(**cfg)
+        self.dtype = dtype
+        names = [L.albert_tensor_name(i).decode() for i in range(N_TENSORS)]
+        self._host = []
+        for i, n in enumerate(names):
+            a = np.ascontiguousarray(np.asarray(weights[n], dtype=np.float32))
+            r, c = ctypes.c_int64(), ctypes.c_int64()
+            rc = L.albert_tensor_shape(ctypes.byref(self.cfg), i, ctypes.byref(r), ctypes.byref(c))
+            if rc != OK:
+                raise AlbertError(rc, "albert_tensor_shape")
+            if a.size != r.value * c.value:
+                raise ValueError(f"{n}: expected {r.value}x{c.value}, got {a.shape}")
+            self._host.append(a)
+        ptrs = (ctypes.c_void_p * N_TENSORS)(*[a.ctypes.data for a in self._host])
+        h = ctypes.c_void_p()
+        rc = L.albert_load_weights(ctypes.byref(h), ctypes.byref(self.cfg), ptrs,
+                                   BF16 if dtype == "bf16" else F32, _stream(stream))
+        self._host = None
+        if rc != OK:
+            raise AlbertError(rc, "albert_load_weights")
+        self.handle = h
+
+    def close(self):
+        if getattr(self, "handle", None):
+            lib().albert_free(self.handle)
+            self.handle = None
+
+    __del__ = close
+
+    # -------------------------------------------------------------- sizes --
+    def workspace_bytes(self, n_seq: int, max_rows: int) -> int:
+        return int(lib().albert_workspace_bytes(self.handle, n_seq, max_rows))
+
+    def tap(self, n_seq: int, max_rows: int, name: str):
+        off, nb, st = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_int64()
+        rc = lib().albert_tap(self.handle, n_seq, max_rows, TAPS[name], ctypes.byref(off),
+                              ctypes.byref(nb), ctypes.byref(st))
+        if rc != OK:
+            raise AlbertError(rc, "albert_tap")
+        return off.value, nb.value, st.value
+
+    def new_workspace(self, n_seq: int, max_rows: int):
+        import torch
+        return torch.empty(self.workspace_bytes(n_seq, max_rows), dtype=torch.uint8,
+                           device="cuda")
+
+    # ------------------------------------------------------------- encode --
+    def encode_raw(self, ids, lengths, out, ws, stream=None, flags=0, ws_bytes=None) -> int:
+        """Padded call on caller tensors; returns the status code."""
+        B, T = ids.shape
+        nb = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
+        return lib().albert_encode(self.handle, _ptr(ids), _ptr(lengths), B, T, _ptr(out),
+                                   _ptr(ws), nb, _stream(stream), flags)
+
+    def encode_varlen_raw(self, ids, cu, max_len, out, ws, stream=None, flags=0,
+                          ws_bytes=None, n=None, total=None) -> int:
+        n = cu.numel() - 1 if n is None else n
+        total = ids.numel() if total is None else total
+        nb = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
+        return lib().albert_encode_varlen(self.handle, _ptr(ids), _ptr(cu), n, total, max_len,
+                                          _ptr(out), _ptr(ws), nb, _stream(stream), flags)
+
+    def encode(self, ids, lengths, out=None, ws=None, stream=None):
+        """ids int32 [B, T], lengths int32 [B] (CUDA tensors) -> fp32 [B, T, 512]."""
+        import torch
+        B, T = ids.shape
+        if out is None:
+            out = torch.empty(B, T, self.cfg.out_dim, dtype=torch.float32, device="cuda")
+        if ws is None:
+            ws = self.new_workspace(B, B * T)
+        rc = self.encode_raw(ids, lengths, out, ws, stream)
+        if rc != OK:
+            raise AlbertError(rc, "albert_encode")
+        return out
+
+    def encode_varlen(self, ids, cu, max_len, out=None, ws=None, stream=None):
+        """ids int32 [total], cu int32 [n+1] (CUDA tensors) -> fp32 [total, 512]."""
+        import torch
+        total = ids.numel()
+        if out is None:
+            out = torch.empty(total, self.cfg.out_dim, dtype=torch.float32, device="cuda")
+        if ws is None:
+            ws = self.new_workspace(cu.numel() - 1, total)
+        rc = self.encode_varlen_raw(ids, cu, max_len, out, ws, stream)
+        if rc != OK:
+            raise AlbertError(rc, "albert_encode_varlen")
+        return out
+
+
+def read_status(ws, stream=None) -> int:
+    return int(lib().albert_read_status(_ptr(ws), _stream(stream)))

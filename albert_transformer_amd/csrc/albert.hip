@@ -1,0 +1,462 @@
+// Host side of the encoder library: the C ABI declared in include/albert.h,
+// weight packing, workspace planning and the launch sequence.
+//
+// Launch sequence of one request (all on the caller's stream):
+//   derive (lengths -> offsets, status) -> rows/IDs check -> embedding + LN
+//   -> 128->768 projection -> n_iter x [QKV GEMM -> attention -> out-proj +
+//   residual + LN -> FFN1 + GELU -> FFN2 + residual + LN] -> 768->512
+//   projection into `out` (+ zeroing of padded rows).
+// The same weight pointers serve every execution of the shared layer (page
+// "ALBERT: How Kokoro's Phoneme Encoder Works", "Cross-layer parameter
+// sharing"); only the activations change.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "albert.h"
+#include "attention.hpp"
+#include "gemm.hpp"
+#include "prologue.hpp"
+
+using namespace albert;
+
+struct albert_ctx {
+  albert_config cfg;
+  int dtype;
+  int device;
+  void* mem;
+  // device pointers (tables/matrices in dtype, vectors fp32)
+  const void *word, *pos, *type, *proj_w, *qkv_w, *o_w, *ffn1_w, *ffn2_w, *out_w;
+  const float *emb_g, *emb_b, *proj_b, *qkv_b, *o_b, *ln1_g, *ln1_b, *ffn1_b, *ffn2_b,
+      *ln2_g, *ln2_b, *out_b;
+};
+
+namespace {
+
+constexpr size_t kAlign = 256;
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+const char* const kNames[ALBERT_N_TENSORS] = {
+    "emb.word", "emb.pos", "emb.type", "emb.ln.g", "emb.ln.b", "proj.w", "proj.b",
+    "q.w", "q.b", "k.w", "k.b", "v.w", "v.b", "o.w", "o.b", "attn_ln.g", "attn_ln.b",
+    "ffn1.w", "ffn1.b", "ffn2.w", "ffn2.b", "ffn_ln.g", "ffn_ln.b", "out.w", "out.b"};
+
+bool shape_of(const albert_config& c, int i, int64_t* r, int64_t* k) {
+  const int64_t E = c.emb, H = c.hidden, F = c.ffn, O = c.out_dim;
+  int64_t rows = 0, cols = 1;
+  switch (i) {
+    case 0: rows = c.vocab; cols = E; break;
+    case 1: rows = c.max_pos; cols = E; break;
+    case 2: rows = c.n_types; cols = E; break;
+    case 3: case 4: rows = E; break;
+    case 5: rows = H; cols = E; break;
+    case 6: rows = H; break;
+    case 7: case 9: case 11: case 13: rows = H; cols = H; break;
+    case 8: case 10: case 12: case 14: case 15: case 16: rows = H; break;
+    case 17: rows = F; cols = H; break;
+    case 18: rows = F; break;
+    case 19: rows = H; cols = F; break;
+    case 20: case 21: case 22: rows = H; break;
+    case 23: rows = O; cols = H; break;
+    case 24: rows = O; break;
+    default: return false;
+  }
+  *r = rows;
+  *k = cols;
+  return true;
+}
+
+// The kernels are specialised for Kokoro's geometry; sizes that only change
+// loop counts or table extents are free within tile multiples.
+bool config_ok(const albert_config& c) {
+  return c.emb == 128 && c.hidden == 768 && c.heads == 12 && c.head_dim == 64 &&
+         c.vocab >= 1 && c.max_pos >= 1 && c.max_pos <= 512 && c.n_types >= 1 &&
+         c.ffn >= 256 && c.ffn % 256 == 0 && c.out_dim >= 256 && c.out_dim % 256 == 0 &&
+         c.n_iter >= 0 && std::isfinite(c.ln_eps) && c.ln_eps > 0.f;
+}
+
+uint16_t f32_to_bf16_bits(float f) {
+  // round to nearest, ties to even (finite inputs)
+  uint32_t u;
+  std::memcpy(&u, &f, 4);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+struct Layout {
+  size_t status, cu, row_seq, row_pos, emb, x, x1, qkv, ctx, g, total;
+  int64_t rows_cap;
+};
+
+Layout plan(const albert_ctx* c, int n_seq, int64_t max_rows) {
+  Layout L{};
+  const size_t es = c->dtype == ALBERT_BF16 ? 2 : 4;
+  const int64_t rows = (int64_t)align_up((size_t)max_rows, 256);
+  size_t off = 0;
+  L.rows_cap = rows;
+  L.status = off; off += kAlign;
+  L.cu = off; off += align_up((size_t)(n_seq + 1) * 4, kAlign);
+  L.row_seq = off; off += align_up((size_t)rows * 4, kAlign);
+  L.row_pos = off; off += align_up((size_t)rows * 4, kAlign);
+  L.emb = off; off += align_up((size_t)rows * c->cfg.emb * es, kAlign);
+  L.x = off; off += align_up((size_t)rows * c->cfg.hidden * es, kAlign);
+  L.x1 = off; off += align_up((size_t)rows * c->cfg.hidden * es, kAlign);
+  L.qkv = off; off += align_up((size_t)rows * 3 * c->cfg.hidden * es, kAlign);
+  L.ctx = off; off += align_up((size_t)rows * c->cfg.hidden * es, kAlign);
+  L.g = off; off += align_up((size_t)rows * c->cfg.ffn * es, kAlign);
+  L.total = off;
+  return L;
+}
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  if (!a || !b || !na || !nb) return false;
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return x < y + nb && y < x + na;
+}
+
+template <typename T, int BM, int BN, int WGM, int WGN, int EPI>
+void launch_gemm(GemmArgs g, int64_t max_rows, hipStream_t s) {
+  g.n_tiles = g.N / BN;
+  const int64_t mt = (max_rows + BM - 1) / BM;
+  hipLaunchKernelGGL((gemm_kernel<T, BM, BN, WGM, WGN, EPI>), dim3((unsigned)(mt * g.n_tiles)),
+                     dim3(WGM * WGN * 64), 0, s, g);
+}
+
+// Large tiles for plain and GELU epilogues; full-row tiles for LayerNorm.
+template <typename T, int EPI>
+void gemm_big(GemmArgs g, int64_t max_rows, hipStream_t s) {
+  launch_gemm<T, 256, 256, 2, 2, EPI>(g, max_rows, s);
+}
+template <typename T>
+void gemm_ln(GemmArgs g, int64_t max_rows, hipStream_t s) {
+  launch_gemm<T, 128, 768, 2, 4, EPI_LN>(g, max_rows, s);
+}
+
+template <typename T>
+int run(albert_ctx* c, const int32_t* ids, const int32_t* lens_or_cu, int n_seq, int pad_T,
+        int64_t max_rows, int max_len, float* out, void* ws, hipStream_t s) {
+  const albert_config& cf = c->cfg;
+  const Layout L = plan(c, n_seq, max_rows);
+  char* w = static_cast<char*>(ws);
+  int* status = reinterpret_cast<int*>(w + L.status);
+  int* cu = reinterpret_cast<int*>(w + L.cu);
+  int* row_seq = reinterpret_cast<int*>(w + L.row_seq);
+  int* row_pos = reinterpret_cast<int*>(w + L.row_pos);
+  T* emb = reinterpret_cast<T*>(w + L.emb);
+  T* X = reinterpret_cast<T*>(w + L.x);
+  T* X1 = reinterpret_cast<T*>(w + L.x1);
+  T* QKV = reinterpret_cast<T*>(w + L.qkv);
+  T* CTX = reinterpret_cast<T*>(w + L.ctx);
+  T* G = reinterpret_cast<T*>(w + L.g);
+  const int H = cf.hidden, F = cf.ffn;
+  const int* m_ptr = cu + n_seq;
+
+  if (pad_T)
+    hipLaunchKernelGGL(derive_padded_kernel, dim3(1), dim3(1024), 0, s, lens_or_cu, n_seq, pad_T,
+                       cu, status);
+  else
+    hipLaunchKernelGGL(derive_packed_kernel, dim3(1), dim3(1024), 0, s, lens_or_cu, n_seq,
+                       (int)max_rows, max_len, cu, status);
+  hipLaunchKernelGGL(rows_ids_kernel, dim3(n_seq), dim3(256), 0, s, ids, cu, pad_T, cf.vocab,
+                     row_seq, row_pos, status);
+  hipLaunchKernelGGL(embed_ln_kernel<T>, dim3((unsigned)((max_rows + 15) / 16)), dim3(256), 0, s,
+                     ids, pad_T, row_seq, row_pos, m_ptr, (const T*)c->word, (const T*)c->pos,
+                     (const T*)c->type, c->emb_g, c->emb_b, cf.ln_eps, emb, status);
+
+  GemmArgs base{};
+  base.status = status;
+  base.m_ptr = m_ptr;
+  base.eps = cf.ln_eps;
+
+  GemmArgs g = base;  // input projection E -> H
+  g.X = emb; g.ldx = cf.emb; g.W = c->proj_w; g.bias = c->proj_b; g.Y = X; g.ldy = H;
+  g.N = H; g.K = cf.emb;
+  gemm_big<T, EPI_BIAS>(g, max_rows, s);
+
+  const int qtiles = (max_len + 127) / 128;
+  for (int it = 0; it < cf.n_iter; ++it) {
+    g = base;  // fused Q|K|V projection
+    g.X = X; g.ldx = H; g.W = c->qkv_w; g.bias = c->qkv_b; g.Y = QKV; g.ldy = 3 * H;
+    g.N = 3 * H; g.K = H;
+    gemm_big<T, EPI_BIAS>(g, max_rows, s);
+
+    AttnArgs a{QKV, CTX, cu, status};
+    hipLaunchKernelGGL(attention_kernel<T>, dim3(n_seq, cf.heads, qtiles), dim3(256), 0, s, a);
+
+    g = base;  // output projection + residual + LayerNorm
+    g.X = CTX; g.ldx = H; g.W = c->o_w; g.bias = c->o_b; g.R = X; g.ldr = H;
+    g.ln_g = c->ln1_g; g.ln_b = c->ln1_b; g.Y = X1; g.ldy = H; g.N = H; g.K = H;
+    gemm_ln<T>(g, max_rows, s);
+
+    g = base;  // FFN 768 -> 2048 + GELU
+    g.X = X1; g.ldx = H; g.W = c->ffn1_w; g.bias = c->ffn1_b; g.Y = G; g.ldy = F;
+    g.N = F; g.K = H;
+    gemm_big<T, EPI_GELU>(g, max_rows, s);
+
+    g = base;  // FFN 2048 -> 768 + residual + LayerNorm
+    g.X = G; g.ldx = F; g.W = c->ffn2_w; g.bias = c->ffn2_b; g.R = X1; g.ldr = H;
+    g.ln_g = c->ln2_g; g.ln_b = c->ln2_b; g.Y = X; g.ldy = H; g.N = H; g.K = F;
+    gemm_ln<T>(g, max_rows, s);
+  }
+
+  g = base;  // output projection H -> 512, fp32, into the caller's rows
+  g.X = X; g.ldx = H; g.W = c->out_w; g.bias = c->out_b; g.out = out;
+  g.row_seq = row_seq; g.row_pos = row_pos; g.out_T = pad_T; g.N = cf.out_dim; g.K = H;
+  gemm_big<T, EPI_OUT>(g, max_rows, s);
+  if (pad_T)
+    hipLaunchKernelGGL(zero_pad_rows_kernel, dim3(n_seq), dim3(256), 0, s, out, cu, pad_T,
+                       cf.out_dim, status);
+  return hipGetLastError() == hipSuccess ? ALBERT_OK : ALBERT_E_HIP;
+}
+
+int finish(int rc, const void* ws, hipStream_t s, unsigned flags) {
+  if (rc != ALBERT_OK || (flags & ALBERT_ASYNC)) return rc;
+  return albert_read_status(ws, s);
+}
+
+bool device_matches(const albert_ctx* c) {
+  int d = -1;
+  return hipGetDevice(&d) == hipSuccess && d == c->device;
+}
+
+}  // namespace
+
+extern "C" {
+
+int albert_default_config(albert_config* cfg) {
+  if (!cfg) return ALBERT_E_ARG;
+  *cfg = albert_config{178, 512, 2, 128, 768, 12, 64, 2048, 12, 512, 1e-12f};
+  return ALBERT_OK;
+}
+
+const char* albert_tensor_name(int index) {
+  return (index >= 0 && index < ALBERT_N_TENSORS) ? kNames[index] : nullptr;
+}
+
+int albert_tensor_shape(const albert_config* cfg, int index, int64_t* rows, int64_t* cols) {
+  if (!cfg || !rows || !cols || !config_ok(*cfg)) return ALBERT_E_ARG;
+  return shape_of(*cfg, index, rows, cols) ? ALBERT_OK : ALBERT_E_ARG;
+}
+
+int albert_load_weights(albert_ctx** out_ctx, const albert_config* cfg,
+                        const float* const* host, int dtype, void* stream) {
+  if (!out_ctx) return ALBERT_E_ARG;
+  *out_ctx = nullptr;
+  if (!cfg || !host || !config_ok(*cfg) || (dtype != ALBERT_F32 && dtype != ALBERT_BF16))
+    return ALBERT_E_ARG;
+  const albert_config c = *cfg;
+  const size_t es = dtype == ALBERT_BF16 ? 2 : 4;
+  int64_t rows[ALBERT_N_TENSORS], cols[ALBERT_N_TENSORS];
+  for (int i = 0; i < ALBERT_N_TENSORS; ++i) {
+    if (!host[i]) return ALBERT_E_ARG;
+    shape_of(c, i, &rows[i], &cols[i]);
+    for (int64_t e = 0; e < rows[i] * cols[i]; ++e)
+      if (!std::isfinite(host[i][e])) return ALBERT_E_ARG;
+  }
+  const int64_t H = c.hidden;
+
+  // Device image: segments in the order below, each 256-byte aligned.
+  struct Seg { size_t off, bytes; };
+  std::vector<Seg> seg;
+  size_t off = 0;
+  auto add = [&](size_t bytes) { seg.push_back({off, bytes}); off += align_up(bytes, kAlign); };
+  add((size_t)c.vocab * c.emb * es);       // 0 word
+  add((size_t)c.max_pos * c.emb * es);     // 1 pos
+  add((size_t)c.n_types * c.emb * es);     // 2 type
+  add((size_t)c.emb * 4);                  // 3 emb g
+  add((size_t)c.emb * 4);                  // 4 emb b
+  add((size_t)H * c.emb * es);             // 5 proj w
+  add((size_t)H * 4);                      // 6 proj b
+  add((size_t)3 * H * H * es);             // 7 qkv w
+  add((size_t)3 * H * 4);                  // 8 qkv b
+  add((size_t)H * H * es);                 // 9 o w
+  add((size_t)H * 4);                      // 10 o b
+  add((size_t)H * 4);                      // 11 ln1 g
+  add((size_t)H * 4);                      // 12 ln1 b
+  add((size_t)c.ffn * H * es);             // 13 ffn1 w
+  add((size_t)c.ffn * 4);                  // 14 ffn1 b
+  add((size_t)H * c.ffn * es);             // 15 ffn2 w
+  add((size_t)H * 4);                      // 16 ffn2 b
+  add((size_t)H * 4);                      // 17 ln2 g
+  add((size_t)H * 4);                      // 18 ln2 b
+  add((size_t)c.out_dim * H * es);         // 19 out w
+  add((size_t)c.out_dim * 4);              // 20 out b
+  std::vector<unsigned char> img(off, 0);
+
+  auto put_mat = [&](int s, const float* src, int64_t n, float scale, size_t elem_off) {
+    unsigned char* d = img.data() + seg[s].off + elem_off * es;
+    for (int64_t e = 0; e < n; ++e) {
+      const float v = src[e] * scale;  // scale is 1 or a power of two: exact
+      if (es == 2) {
+        const uint16_t bits = f32_to_bf16_bits(v);
+        std::memcpy(d + e * 2, &bits, 2);
+      } else {
+        std::memcpy(d + e * 4, &v, 4);
+      }
+    }
+  };
+  auto put_vec = [&](int s, const float* src, int64_t n, float scale, size_t elem_off) {
+    float* d = reinterpret_cast<float*>(img.data() + seg[s].off) + elem_off;
+    for (int64_t e = 0; e < n; ++e) d[e] = src[e] * scale;
+  };
+  const float qscale = 1.0f / std::sqrt((float)c.head_dim);  // 1/8 for head_dim 64
+  put_mat(0, host[0], rows[0] * cols[0], 1.f, 0);
+  put_mat(1, host[1], rows[1] * cols[1], 1.f, 0);
+  put_mat(2, host[2], rows[2] * cols[2], 1.f, 0);
+  put_vec(3, host[3], c.emb, 1.f, 0);
+  put_vec(4, host[4], c.emb, 1.f, 0);
+  put_mat(5, host[5], H * c.emb, 1.f, 0);
+  put_vec(6, host[6], H, 1.f, 0);
+  put_mat(7, host[7], H * H, qscale, 0);
+  put_mat(7, host[9], H * H, 1.f, (size_t)(H * H));
+  put_mat(7, host[11], H * H, 1.f, (size_t)(2 * H * H));
+  put_vec(8, host[8], H, qscale, 0);
+  put_vec(8, host[10], H, 1.f, (size_t)H);
+  put_vec(8, host[12], H, 1.f, (size_t)(2 * H));
+  put_mat(9, host[13], H * H, 1.f, 0);
+  put_vec(10, host[14], H, 1.f, 0);
+  put_vec(11, host[15], H, 1.f, 0);
+  put_vec(12, host[16], H, 1.f, 0);
+  put_mat(13, host[17], (int64_t)c.ffn * H, 1.f, 0);
+  put_vec(14, host[18], c.ffn, 1.f, 0);
+  put_mat(15, host[19], H * c.ffn, 1.f, 0);
+  put_vec(16, host[20], H, 1.f, 0);
+  put_vec(17, host[21], H, 1.f, 0);
+  put_vec(18, host[22], H, 1.f, 0);
+  put_mat(19, host[23], (int64_t)c.out_dim * H, 1.f, 0);
+  put_vec(20, host[24], c.out_dim, 1.f, 0);
+
+  albert_ctx* ctx = new (std::nothrow) albert_ctx();
+  if (!ctx) return ALBERT_E_ARG;
+  ctx->cfg = c;
+  ctx->dtype = dtype;
+  if (hipGetDevice(&ctx->device) != hipSuccess || hipMalloc(&ctx->mem, off) != hipSuccess) {
+    delete ctx;
+    return ALBERT_E_HIP;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (hipMemcpyAsync(ctx->mem, img.data(), off, hipMemcpyHostToDevice, s) != hipSuccess ||
+      hipStreamSynchronize(s) != hipSuccess) {
+    (void)hipFree(ctx->mem);
+    delete ctx;
+    return ALBERT_E_HIP;
+  }
+  char* m = static_cast<char*>(ctx->mem);
+  auto P = [&](int sidx) { return (const void*)(m + seg[sidx].off); };
+  auto Pf = [&](int sidx) { return (const float*)(m + seg[sidx].off); };
+  ctx->word = P(0); ctx->pos = P(1); ctx->type = P(2);
+  ctx->emb_g = Pf(3); ctx->emb_b = Pf(4);
+  ctx->proj_w = P(5); ctx->proj_b = Pf(6);
+  ctx->qkv_w = P(7); ctx->qkv_b = Pf(8);
+  ctx->o_w = P(9); ctx->o_b = Pf(10); ctx->ln1_g = Pf(11); ctx->ln1_b = Pf(12);
+  ctx->ffn1_w = P(13); ctx->ffn1_b = Pf(14); ctx->ffn2_w = P(15); ctx->ffn2_b = Pf(16);
+  ctx->ln2_g = Pf(17); ctx->ln2_b = Pf(18);
+  ctx->out_w = P(19); ctx->out_b = Pf(20);
+  *out_ctx = ctx;
+  return ALBERT_OK;
+}
+
+size_t albert_workspace_bytes(const albert_ctx* ctx, int n_seq, int64_t max_rows) {
+  if (!ctx || n_seq < 1 || max_rows < 1) return 0;
+  return plan(ctx, n_seq, max_rows).total;
+}
+
+int albert_encode(albert_ctx* ctx, const int32_t* ids, const int32_t* lengths, int B, int T,
+                  float* out, void* ws, size_t ws_bytes, void* stream, unsigned flags) {
+  if (ctx && B == 0) return ALBERT_OK;  // empty batch: nothing to do
+  if (!ctx || !ids || !lengths || !out || !ws || B < 1 || T < 1 || T > ctx->cfg.max_pos ||
+      ((uintptr_t)ws % kAlign) != 0 || (int64_t)B * T > INT32_MAX || !device_matches(ctx))
+    return ALBERT_E_ARG;
+  const int64_t rows = (int64_t)B * T;
+  const size_t need = plan(ctx, B, rows).total;
+  if (ws_bytes < need) return ALBERT_E_WORKSPACE;
+  const size_t out_bytes = (size_t)rows * ctx->cfg.out_dim * 4;
+  if (overlaps(out, out_bytes, ids, (size_t)rows * 4) ||
+      overlaps(out, out_bytes, lengths, (size_t)B * 4) || overlaps(out, out_bytes, ws, need))
+    return ALBERT_E_ALIAS;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int rc = ctx->dtype == ALBERT_BF16
+                     ? run<bf16>(ctx, ids, lengths, B, T, rows, T, out, ws, s)
+                     : run<float>(ctx, ids, lengths, B, T, rows, T, out, ws, s);
+  return finish(rc, ws, s, flags);
+}
+
+int albert_encode_varlen(albert_ctx* ctx, const int32_t* ids, const int32_t* cu_seqlens, int n,
+                         int total, int max_len, float* out, void* ws, size_t ws_bytes,
+                         void* stream, unsigned flags) {
+  if (ctx && n == 0 && total == 0) return ALBERT_OK;  // empty batch
+  if (!ctx || !ids || !cu_seqlens || !out || !ws || n < 1 || total < 1 || max_len < 1 ||
+      max_len > ctx->cfg.max_pos || ((uintptr_t)ws % kAlign) != 0 || !device_matches(ctx))
+    return ALBERT_E_ARG;
+  const size_t need = plan(ctx, n, total).total;
+  if (ws_bytes < need) return ALBERT_E_WORKSPACE;
+  const size_t out_bytes = (size_t)total * ctx->cfg.out_dim * 4;
+  if (overlaps(out, out_bytes, ids, (size_t)total * 4) ||
+      overlaps(out, out_bytes, cu_seqlens, (size_t)(n + 1) * 4) ||
+      overlaps(out, out_bytes, ws, need))
+    return ALBERT_E_ALIAS;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int rc = ctx->dtype == ALBERT_BF16
+                     ? run<bf16>(ctx, ids, cu_seqlens, n, 0, total, max_len, out, ws, s)
+                     : run<float>(ctx, ids, cu_seqlens, n, 0, total, max_len, out, ws, s);
+  return finish(rc, ws, s, flags);
+}
+
+int albert_read_status(const void* ws, void* stream) {
+  if (!ws) return ALBERT_E_ARG;
+  int st = -1;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (hipMemcpyAsync(&st, ws, sizeof(int), hipMemcpyDeviceToHost, s) != hipSuccess ||
+      hipStreamSynchronize(s) != hipSuccess)
+    return ALBERT_E_HIP;
+  return st;
+}
+
+int albert_tap(const albert_ctx* ctx, int n_seq, int64_t max_rows, int tap, size_t* offset,
+               size_t* bytes, int64_t* row_stride) {
+  if (!ctx || !offset || !bytes || !row_stride || n_seq < 1 || max_rows < 1) return ALBERT_E_ARG;
+  const Layout L = plan(ctx, n_seq, max_rows);
+  const size_t es = ctx->dtype == ALBERT_BF16 ? 2 : 4;
+  const albert_config& c = ctx->cfg;
+  const size_t R = (size_t)max_rows;
+  switch (tap) {
+    case ALBERT_TAP_STATUS: *offset = L.status; *bytes = 4; *row_stride = 0; break;
+    case ALBERT_TAP_CU: *offset = L.cu; *bytes = (size_t)(n_seq + 1) * 4; *row_stride = 0; break;
+    case ALBERT_TAP_ROW_SEQ: *offset = L.row_seq; *bytes = R * 4; *row_stride = 0; break;
+    case ALBERT_TAP_ROW_POS: *offset = L.row_pos; *bytes = R * 4; *row_stride = 0; break;
+    case ALBERT_TAP_EMB: *offset = L.emb; *bytes = R * c.emb * es; *row_stride = c.emb; break;
+    case ALBERT_TAP_X: *offset = L.x; *bytes = R * c.hidden * es; *row_stride = c.hidden; break;
+    case ALBERT_TAP_QKV:
+      *offset = L.qkv; *bytes = R * 3 * c.hidden * es; *row_stride = 3 * c.hidden; break;
+    case ALBERT_TAP_CTX: *offset = L.ctx; *bytes = R * c.hidden * es; *row_stride = c.hidden; break;
+    case ALBERT_TAP_X1: *offset = L.x1; *bytes = R * c.hidden * es; *row_stride = c.hidden; break;
+    case ALBERT_TAP_G: *offset = L.g; *bytes = R * c.ffn * es; *row_stride = c.ffn; break;
+    default: return ALBERT_E_ARG;
+  }
+  return ALBERT_OK;
+}
+
+void albert_free(albert_ctx* ctx) {
+  if (!ctx) return;
+  if (ctx->mem) (void)hipFree(ctx->mem);
+  delete ctx;
+}
+
+const char* albert_status_str(int status) {
+  switch (status) {
+    case ALBERT_OK: return "ok";
+    case ALBERT_E_ARG: return "invalid argument";
+    case ALBERT_E_WORKSPACE: return "workspace too small";
+    case ALBERT_E_LENGTH: return "sequence length out of range or bad offsets";
+    case ALBERT_E_ID: return "phoneme id outside the vocabulary";
+    case ALBERT_E_ALIAS: return "output overlaps an input or the workspace";
+    case ALBERT_E_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

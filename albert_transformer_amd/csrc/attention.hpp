@@ -1,0 +1,151 @@
+// Fused masked-softmax bidirectional attention over packed sequences.
+//
+// Per sequence s and head h: C = softmax(Q K^T / sqrt(64)) V over the
+// sequence's own keys only ("Inside One Real ALBERT Layer", step 4; the
+// shorthand softmax(QK^T/sqrt(d) + mask) V of "How Kokoro TTS Works and Where
+// CKE Stands", section "What ALBERT does here": keys beyond the length get no
+// weight).  The 1/8 scale is already folded into the stored query weights.
+//
+// Grid: (sequences, 12 heads, query tiles of 128).  Each wave owns 32
+// queries.  Keys and values of the (sequence, head) are staged in LDS in
+// chunks of 128 keys (K row-major, V transposed), zero-filled past the
+// length, so one workgroup walks the whole sequence (<= 512 keys).
+// Scores are computed transposed, S^T = K Q^T, so each lane owns one query
+// and 16 keys of every 32-key block: the running max and sum of the online
+// softmax need only the partner half-wave, and the probabilities feed the
+// second MFMA (O^T = V^T P^T) directly from registers, with V^T read from
+// LDS in the matching key order.
+#pragma once
+
+#include "common.hpp"
+
+namespace albert {
+
+struct AttnArgs {
+  const void* qkv;    // [M, 3H]: q*(1/8) | k | v, head h at h*64
+  void* ctx;          // [M, H]
+  const int* cu;      // [n_seq + 1]
+  const int* status;
+};
+
+template <typename T>
+__global__ void __launch_bounds__(256)
+attention_kernel(AttnArgs a) {
+  typedef Tr<T> TR;
+  constexpr int H = 768, D = 64, LDQKV = 3 * H;
+  constexpr int KC = 128;                 // keys per staged chunk
+  constexpr int VEC = 16 / sizeof(T);
+  constexpr int LDKS = D + VEC;           // K rows, padded
+  constexpr int LDVT = KC + VEC;          // V^T rows, padded
+  __shared__ __attribute__((aligned(16))) T Ks[KC * LDKS];
+  __shared__ __attribute__((aligned(16))) T Vt[D * LDVT];
+
+  if (*a.status != 0) return;
+  const int b = blockIdx.x, h = blockIdx.y;
+  const int start = a.cu[b], L = a.cu[b + 1] - start;
+  const int q0 = blockIdx.z * 128;
+  if (q0 >= L) return;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, hh = lane >> 5;
+  const int qi = q0 + wave * 32 + l32;  // this lane's query (column of S^T)
+
+  const T* __restrict__ qkv = static_cast<const T*>(a.qkv);
+  const T* __restrict__ base = qkv + (int64_t)start * LDQKV;
+
+  typename TR::frag fq[4];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk)
+    fq[kk] = (qi < L) ? TR::load(base + (int64_t)qi * LDQKV + h * D + kk * 16 + hh * 8)
+                      : TR::zero();
+
+  f32x16 o[2];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) { o[0][r] = 0.f; o[1][r] = 0.f; }
+  float mrun = kNegInf, lrun = 0.f;
+
+  for (int c0 = 0; c0 < L; c0 += KC) {
+    const int nk = min(KC, L - c0);
+    __syncthreads();  // the previous chunk is fully consumed
+    // K chunk, row-major [key][dim]
+    for (int idx = tid; idx < KC * (D / VEC); idx += 256) {
+      const int j = idx / (D / VEC), cc = idx % (D / VEC);
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (j < nk) v = *reinterpret_cast<const uint4*>(base + (int64_t)(c0 + j) * LDQKV + H + h * D + cc * VEC);
+      *reinterpret_cast<uint4*>(Ks + j * LDKS + cc * VEC) = v;
+    }
+    // V chunk, transposed [dim][key]
+    for (int idx = tid; idx < KC * (D / VEC); idx += 256) {
+      const int j = idx % KC, cc = idx / KC;
+      T tmp[VEC];
+      if (j < nk) {
+        *reinterpret_cast<uint4*>(tmp) =
+            *reinterpret_cast<const uint4*>(base + (int64_t)(c0 + j) * LDQKV + 2 * H + h * D + cc * VEC);
+      } else {
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) tmp[e] = (T)0.0f;
+      }
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) Vt[(cc * VEC + e) * LDVT + j] = tmp[e];
+    }
+    __syncthreads();
+
+    const int nkb = (nk + 31) / 32;
+    for (int kb = 0; kb < nkb; ++kb) {
+      f32x16 s;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[r] = 0.f;
+      const T* kp = Ks + (kb * 32 + l32) * LDKS + hh * 8;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) TR::mma(s, TR::load(kp + kk * 16), fq[kk]);
+      // s[r] = score of key c0 + kb*32 + 8(r/4) + 4hh + r%4 for query qi
+      const int kbase = c0 + kb * 32 + 4 * hh;
+      float mx = kNegInf;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = kbase + 8 * (r >> 2) + (r & 3);
+        if (key >= L) s[r] = kNegInf;
+        mx = fmaxf(mx, s[r]);
+      }
+      mx = fmaxf(mx, wave_xor(mx, 32));
+      const float mnew = fmaxf(mrun, mx);
+      const float alpha = fast_exp2((mrun - mnew) * kLog2e);
+      const float mb = mnew * kLog2e;
+      float p[16];
+      float psum = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        p[r] = fast_exp2(s[r] * kLog2e - mb);
+        psum += p[r];
+      }
+      lrun = lrun * alpha + psum;
+      mrun = mnew;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) { o[0][r] *= alpha; o[1][r] *= alpha; }
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        // element e of this lane <-> key 16c + 4hh + e (e < 4), 16c + 8 + 4hh + e - 4
+        const typename TR::frag fp = TR::from_f32(p + 8 * c);
+#pragma unroll
+        for (int dt = 0; dt < 2; ++dt) {
+          const T* vp = Vt + (dt * 32 + l32) * LDVT + kb * 32 + 16 * c + 4 * hh;
+          TR::mma(o[dt], TR::load2x4(vp, vp + 8), fp);
+        }
+      }
+    }
+  }
+  lrun += wave_xor(lrun, 32);
+  if (qi >= L) return;
+  const float inv = 1.0f / lrun;
+  T* __restrict__ out = static_cast<T*>(a.ctx) + ((int64_t)start + qi) * H + h * D;
+#pragma unroll
+  for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int d = dt * 32 + 8 * q + 4 * hh;
+      TR::store4(out + d, o[dt][4 * q + 0] * inv, o[dt][4 * q + 1] * inv,
+                 o[dt][4 * q + 2] * inv, o[dt][4 * q + 3] * inv);
+    }
+}
+
+}  // namespace albert

@@ -1,0 +1,134 @@
+// Device-side building blocks shared by the encoder's HIP kernels (gfx950).
+//
+// Storage types: __bf16 (the production path) or float (the fp32 debug
+// path).  All arithmetic outside the matrix cores is fp32.
+//
+// Matrix-core conventions used by every kernel here (CDNA 32x32 MFMA):
+//   D[32x32] += A[32xK] * B[Kx32], wave64.
+//   Lane l supplies row (l % 32) of A and column (l % 32) of B, each as 8
+//   consecutive elements of a 16-wide K step; half-wave h = l / 32 supplies
+//   elements h*8 .. h*8+7 of that step.  Because A and B use the same
+//   (lane, element) -> k assignment, any permutation of k inside a step is
+//   harmless; the kernels exploit this to feed softmax probabilities straight
+//   from accumulator registers.
+//   Lane l holds D column (l % 32); register r holds D row
+//   8*(r/4) + 4*h + (r%4).
+//   bf16: one v_mfma_f32_32x32x16_bf16 per K step of 16.
+//   fp32: eight v_mfma_f32_32x32x2_f32, element s of each lane in the s-th.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace albert {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kNegInf = -__builtin_inff();
+
+template <typename T> struct Tr;
+
+template <> struct Tr<bf16> {
+  typedef bf16x8 frag;
+  static constexpr int BK = 32;  // GEMM K tile: 64 bytes per row
+  static __device__ __forceinline__ frag load(const bf16* p) {
+    return *reinterpret_cast<const bf16x8*>(p);
+  }
+  // two groups of 4 consecutive elements
+  static __device__ __forceinline__ frag load2x4(const bf16* p0, const bf16* p1) {
+    bf16x4 a = *reinterpret_cast<const bf16x4*>(p0);
+    bf16x4 b = *reinterpret_cast<const bf16x4*>(p1);
+    frag f;
+    f[0] = a[0]; f[1] = a[1]; f[2] = a[2]; f[3] = a[3];
+    f[4] = b[0]; f[5] = b[1]; f[6] = b[2]; f[7] = b[3];
+    return f;
+  }
+  static __device__ __forceinline__ frag from_f32(const float* v) {
+    frag f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f[e] = (bf16)v[e];
+    return f;
+  }
+  static __device__ __forceinline__ frag zero() {
+    frag f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f[e] = (bf16)0.0f;
+    return f;
+  }
+  static __device__ __forceinline__ void mma(f32x16& c, const frag& a, const frag& b) {
+    c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ void store4(bf16* p, float a, float b, float c, float d) {
+    bf16x4 v;
+    v[0] = (bf16)a; v[1] = (bf16)b; v[2] = (bf16)c; v[3] = (bf16)d;
+    *reinterpret_cast<bf16x4*>(p) = v;
+  }
+  static __device__ __forceinline__ f32x4 load4f(const bf16* p) {
+    bf16x4 v = *reinterpret_cast<const bf16x4*>(p);
+    f32x4 r;
+    r[0] = (float)v[0]; r[1] = (float)v[1]; r[2] = (float)v[2]; r[3] = (float)v[3];
+    return r;
+  }
+};
+
+template <> struct Tr<float> {
+  struct frag { f32x4 lo, hi; };
+  static constexpr int BK = 16;  // 64 bytes per row
+  static __device__ __forceinline__ frag load(const float* p) {
+    frag f;
+    f.lo = *reinterpret_cast<const f32x4*>(p);
+    f.hi = *reinterpret_cast<const f32x4*>(p + 4);
+    return f;
+  }
+  static __device__ __forceinline__ frag load2x4(const float* p0, const float* p1) {
+    frag f;
+    f.lo = *reinterpret_cast<const f32x4*>(p0);
+    f.hi = *reinterpret_cast<const f32x4*>(p1);
+    return f;
+  }
+  static __device__ __forceinline__ frag from_f32(const float* v) {
+    frag f;
+    f.lo[0] = v[0]; f.lo[1] = v[1]; f.lo[2] = v[2]; f.lo[3] = v[3];
+    f.hi[0] = v[4]; f.hi[1] = v[5]; f.hi[2] = v[6]; f.hi[3] = v[7];
+    return f;
+  }
+  static __device__ __forceinline__ frag zero() {
+    frag f;
+    f.lo = f32x4{0.f, 0.f, 0.f, 0.f};
+    f.hi = f.lo;
+    return f;
+  }
+  static __device__ __forceinline__ void mma(f32x16& c, const frag& a, const frag& b) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) c = __builtin_amdgcn_mfma_f32_32x32x2f32(a.lo[s], b.lo[s], c, 0, 0, 0);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) c = __builtin_amdgcn_mfma_f32_32x32x2f32(a.hi[s], b.hi[s], c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ void store4(float* p, float a, float b, float c, float d) {
+    *reinterpret_cast<f32x4*>(p) = f32x4{a, b, c, d};
+  }
+  static __device__ __forceinline__ f32x4 load4f(const float* p) {
+    return *reinterpret_cast<const f32x4*>(p);
+  }
+};
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// GELU, tanh approximation: x/2 (1 + tanh(a)), a = sqrt(2/pi) (x + 0.044715 x^3).
+// Uses 1/2 (1 + tanh(a)) = 1 / (1 + e^(-2a)); for large |a| the exponential
+// saturates to +inf or 0 and the result to 0 or x without special cases.
+__device__ __forceinline__ float gelu_tanh(float x) {
+  const float c = 0.7978845608028654f;  // sqrt(2/pi)
+  const float a = c * (x + 0.044715f * (x * x * x));
+  const float e = fast_exp2(-2.0f * kLog2e * a);
+  return x * __builtin_amdgcn_rcpf(1.0f + e);
+}
+
+__device__ __forceinline__ float wave_xor(float v, int m) { return __shfl_xor(v, m, 64); }
+
+}  // namespace albert

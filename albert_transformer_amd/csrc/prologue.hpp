@@ -1,0 +1,167 @@
+// Request validation, packed-row bookkeeping, the three-table embedding with
+// its LayerNorm, and the zeroing of padded output rows.
+//
+// Every kernel reads the device status word first and does nothing when a
+// previous step has rejected the request, so that a rejected request never
+// writes the caller's output (the validate-before-write contract of the page
+// "ALBERT: How Kokoro's Phoneme Encoder Works", section "How CKE Represents
+// It"; the header ID check of "How Kokoro TTS Works and Where CKE Stands",
+// section "How I want CKE to stitch it").
+#pragma once
+
+#include "common.hpp"
+
+namespace albert {
+
+enum DevStatus { ST_OK = 0, ST_LENGTH = 3, ST_ID = 4 };
+
+// Inclusive prefix sum over one 1024-thread block (Hillis-Steele in LDS).
+__device__ __forceinline__ int block_incl_scan_1024(int v, int* sh) {
+  const int t = threadIdx.x;
+  sh[t] = v;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    int add = (t >= off) ? sh[t - off] : 0;
+    __syncthreads();
+    sh[t] += add;
+    __syncthreads();
+  }
+  int r = sh[t];
+  __syncthreads();
+  return r;
+}
+
+// Padded batch: check every length in [1, T], write cu[0..B] (prefix sums)
+// and the status word.  One block of 1024 threads.
+__global__ void __launch_bounds__(1024)
+derive_padded_kernel(const int* __restrict__ lengths, int B, int T, int* __restrict__ cu,
+                     int* __restrict__ status) {
+  __shared__ int sh[1024];
+  __shared__ int bad;
+  if (threadIdx.x == 0) bad = 0;
+  __syncthreads();
+  int carry = 0;
+  for (int base = 0; base < B; base += 1024) {
+    const int i = base + threadIdx.x;
+    int len = 0;
+    if (i < B) {
+      len = lengths[i];
+      if (len < 1 || len > T) { bad = 1; len = 0; }
+    }
+    const int incl = block_incl_scan_1024(len, sh);
+    if (i < B) cu[i + 1] = carry + incl;
+    // the last thread's inclusive sum is this chunk's total
+    if (threadIdx.x == 1023) sh[0] = incl;
+    __syncthreads();
+    carry += sh[0];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    cu[0] = 0;
+    *status = bad ? ST_LENGTH : ST_OK;
+  }
+}
+
+// Packed batch: cu_in[0] = 0, cu_in[n] = total, every length in
+// [1, max_len]; copy the offsets into the workspace.  One block.
+__global__ void __launch_bounds__(1024)
+derive_packed_kernel(const int* __restrict__ cu_in, int n, int total, int max_len,
+                     int* __restrict__ cu, int* __restrict__ status) {
+  __shared__ int bad;
+  if (threadIdx.x == 0) bad = (cu_in[0] != 0 || cu_in[n] != total) ? 1 : 0;
+  __syncthreads();
+  for (int i = threadIdx.x; i < n; i += 1024) {
+    const int d = cu_in[i + 1] - cu_in[i];
+    if (d < 1 || d > max_len) bad = 1;
+  }
+  for (int i = threadIdx.x; i <= n; i += 1024) cu[i] = cu_in[i];
+  __syncthreads();
+  if (threadIdx.x == 0) *status = bad ? ST_LENGTH : ST_OK;
+}
+
+// One block per sequence: write each valid row's sequence index and
+// position, and check the ID at that slot.  Pad slots are never read.
+// pad_T > 0: ids is [B, pad_T]; pad_T == 0: ids is packed [total].
+__global__ void __launch_bounds__(256)
+rows_ids_kernel(const int* __restrict__ ids, const int* __restrict__ cu, int pad_T, int vocab,
+                int* __restrict__ row_seq, int* __restrict__ row_pos, int* __restrict__ status) {
+  if (*status != ST_OK) return;
+  const int b = blockIdx.x;
+  const int start = cu[b], L = cu[b + 1] - start;
+  int bad = 0;
+  for (int t = threadIdx.x; t < L; t += blockDim.x) {
+    const int r = start + t;
+    row_seq[r] = b;
+    row_pos[r] = t;
+    const int id = pad_T ? ids[(int64_t)b * pad_T + t] : ids[r];
+    bad |= (id < 0 || id >= vocab);
+  }
+  if (bad) atomicOr(status, (int)ST_ID);
+}
+
+// Three-table embedding + LayerNorm over E = 128 ("Inside One Real ALBERT
+// Layer", step 1): e = word[id] + pos[t] + type[0]; LN with the given eps.
+// 16 lanes per row, 8 channels per lane; fp32 arithmetic, output in T.
+template <typename T>
+__global__ void __launch_bounds__(256)
+embed_ln_kernel(const int* __restrict__ ids, int pad_T, const int* __restrict__ row_seq,
+                const int* __restrict__ row_pos, const int* __restrict__ m_ptr,
+                const T* __restrict__ word, const T* __restrict__ pos, const T* __restrict__ type,
+                const float* __restrict__ g, const float* __restrict__ bta, float eps,
+                T* __restrict__ out, const int* __restrict__ status) {
+  constexpr int E = 128;
+  if (*status != ST_OK) return;
+  const int M = *m_ptr;
+  const int r = blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int sub = threadIdx.x & 15;
+  if (r >= M) return;  // whole 16-lane groups leave together
+  const int p = row_pos[r];
+  const int id = pad_T ? ids[(int64_t)row_seq[r] * pad_T + p] : ids[r];
+  float v[8];
+  const int c0 = sub * 8;
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    f32x4 a = Tr<T>::load4f(word + (int64_t)id * E + c0 + 4 * q);
+    f32x4 b = Tr<T>::load4f(pos + (int64_t)p * E + c0 + 4 * q);
+    f32x4 c = Tr<T>::load4f(type + c0 + 4 * q);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[4 * q + e] = a[e] + b[e] + c[e];
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) s += v[e];
+#pragma unroll
+  for (int m = 8; m >= 1; m >>= 1) s += __shfl_xor(s, m, 16);
+  const float mean = s * (1.0f / E);
+  float s2 = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) { v[e] -= mean; s2 += v[e] * v[e]; }
+#pragma unroll
+  for (int m = 8; m >= 1; m >>= 1) s2 += __shfl_xor(s2, m, 16);
+  const float rstd = 1.0f / sqrtf(s2 * (1.0f / E) + eps);
+  T* o = out + (int64_t)r * E + c0;
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int c = c0 + 4 * q;
+    Tr<T>::store4(o + 4 * q,
+                  v[4 * q + 0] * rstd * g[c + 0] + bta[c + 0],
+                  v[4 * q + 1] * rstd * g[c + 1] + bta[c + 1],
+                  v[4 * q + 2] * rstd * g[c + 2] + bta[c + 2],
+                  v[4 * q + 3] * rstd * g[c + 3] + bta[c + 3]);
+  }
+}
+
+// Padded output: rows t >= lengths[b] of out[B, T, n_out] are set to 0.
+__global__ void __launch_bounds__(256)
+zero_pad_rows_kernel(float* __restrict__ out, const int* __restrict__ cu, int T, int n_out,
+                     const int* __restrict__ status) {
+  if (*status != ST_OK) return;
+  const int b = blockIdx.x;
+  const int L = cu[b + 1] - cu[b];
+  const int per_row = n_out / 4;
+  const int64_t n4 = (int64_t)(T - L) * per_row;
+  f32x4* o = reinterpret_cast<f32x4*>(out + ((int64_t)b * T + L) * n_out);
+  for (int64_t i = threadIdx.x; i < n4; i += blockDim.x) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+}
+
+}  // namespace albert

@@ -1,0 +1,188 @@
+/*
+ * albert.h -- C ABI of the MI355X (gfx950) Kokoro ALBERT phoneme encoder.
+ *
+ * The encoder is the front end of Kokoro TTS, as described on the page
+ * "ALBERT: How Kokoro's Phoneme Encoder Works, and Where CKE Has Reached It"
+ * (sections "What ALBERT Changed: Two Kinds of Sharing" and "Inside One Real
+ * ALBERT Layer"):
+ *   phoneme IDs -> word + position + type tables (width 128), summed and
+ *   LayerNormed -> 128->768 projection -> n_iter executions of ONE shared
+ *   post-LayerNorm transformer layer (12 heads of 64, bidirectional masked
+ *   attention, 768->2048->768 tanh-GELU FFN) -> 768->512 projection.
+ *
+ * Every call takes plain pointers and sizes.  Unless stated otherwise:
+ *   - "dev" pointers are device memory on the current HIP device,
+ *   - hip_stream is a hipStream_t (NULL = the null stream); all device work
+ *     of a call is enqueued on it, in stream order,
+ *   - the return value is an albert_status (0 = ALBERT_OK).
+ * The library never allocates device memory per request: the caller owns the
+ * inputs, the output and a workspace of albert_workspace_bytes() bytes.
+ */
+#ifndef ALBERT_H
+#define ALBERT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes.  A request that fails validation writes nothing to `out`
+ * (the checked, validate-before-write contract of the page "ALBERT: How
+ * Kokoro's Phoneme Encoder Works", section "How CKE Represents It"), and the
+ * context stays usable for the next request. */
+enum albert_status {
+  ALBERT_OK = 0,
+  ALBERT_E_ARG = 1,       /* null pointer, bad size, bad dtype or config     */
+  ALBERT_E_WORKSPACE = 2, /* ws_bytes smaller than albert_workspace_bytes()  */
+  ALBERT_E_LENGTH = 3,    /* a length outside [1, T] / bad cu_seqlens        */
+  ALBERT_E_ID = 4,        /* an ID at a valid slot outside [0, vocab-1]      */
+  ALBERT_E_ALIAS = 5,     /* `out` overlaps an input or the workspace        */
+  ALBERT_E_HIP = 6        /* a HIP runtime call failed                       */
+};
+
+/* Compute/storage type of tables, weight matrices and activations.
+ * Accumulation, biases, LayerNorm, softmax and GELU are always fp32. */
+enum albert_dtype { ALBERT_F32 = 0, ALBERT_BF16 = 1 };
+
+/* flags for albert_encode / albert_encode_varlen */
+#define ALBERT_ASYNC 1u /* return after enqueueing; read the status later
+                           with albert_read_status()                        */
+
+typedef struct albert_config {
+  int32_t vocab;    /* word-table rows (Kokoro: 178)                       */
+  int32_t max_pos;  /* position-table rows, also the longest sequence (512)*/
+  int32_t n_types;  /* type-table rows (2); type id is always 0            */
+  int32_t emb;      /* embedding width E (must be 128)                     */
+  int32_t hidden;   /* hidden width H (must be 768)                        */
+  int32_t heads;    /* attention heads (must be 12)                        */
+  int32_t head_dim; /* per-head width (must be 64)                         */
+  int32_t ffn;      /* FFN width (Kokoro: 2048; multiple of 256)           */
+  int32_t n_iter;   /* executions of the shared layer (Kokoro: 12; >= 0)   */
+  int32_t out_dim;  /* output width (Kokoro: 512; multiple of 256)         */
+  float ln_eps;     /* LayerNorm epsilon (Kokoro: 1e-12)                   */
+} albert_config;
+
+/* Number of weight tensors and their canonical order (index: name [shape]).
+ * Linear weights are [out, in] row-major, y_j = b_j + sum_i x_i W[j][i]
+ * (contract A of "Qwen3-TTS and Kokoro: Two Routes from Text to Speech").
+ *   0 emb.word [vocab,E]    1 emb.pos [max_pos,E]   2 emb.type [n_types,E]
+ *   3 emb.ln.g [E]          4 emb.ln.b [E]
+ *   5 proj.w [H,E]          6 proj.b [H]
+ *   7 q.w [H,H]  8 q.b [H]  9 k.w [H,H] 10 k.b [H] 11 v.w [H,H] 12 v.b [H]
+ *  13 o.w [H,H] 14 o.b [H] 15 attn_ln.g [H] 16 attn_ln.b [H]
+ *  17 ffn1.w [F,H] 18 ffn1.b [F] 19 ffn2.w [H,F] 20 ffn2.b [H]
+ *  21 ffn_ln.g [H] 22 ffn_ln.b [H]
+ *  23 out.w [O,H] 24 out.b [O]                                            */
+#define ALBERT_N_TENSORS 25
+
+typedef struct albert_ctx albert_ctx; /* opaque; owns the device weights */
+
+/* Fill *cfg with the Kokoro configuration. */
+int albert_default_config(albert_config* cfg);
+
+/* Canonical name of tensor `index` (NULL if out of range). */
+const char* albert_tensor_name(int index);
+
+/* Shape of tensor `index` under cfg: writes rows/cols (cols = 1 for
+ * vectors).  Returns ALBERT_E_ARG for a bad index or config. */
+int albert_tensor_shape(const albert_config* cfg, int index, int64_t* rows, int64_t* cols);
+
+/* Create a context holding ONE copy of the encoder weights on the current
+ * device -- one weight set serves all n_iter executions of the shared layer
+ * (page "ALBERT: How Kokoro's Phoneme Encoder Works", "Cross-layer parameter
+ * sharing", and the canonical-name weight binding of "How CKE Represents It").
+ *
+ * host_tensors: ALBERT_N_TENSORS host pointers to fp32 arrays in canonical
+ *   order and shape.  They are read during the call and may be freed after.
+ * dtype: ALBERT_BF16 stores tables and weight matrices as bfloat16 (round to
+ *   nearest even); ALBERT_F32 stores them as given.  Biases and LayerNorm
+ *   vectors are fp32 in both.  The query weights and bias are stored scaled
+ *   by 1/sqrt(head_dim) = 1/8, a power of two, so the attention scores need
+ *   no further scaling and the stored values are exact.
+ * This is the only call that allocates device memory (and it synchronises
+ * hip_stream before returning).  On failure *ctx is NULL. */
+int albert_load_weights(albert_ctx** ctx, const albert_config* cfg,
+                        const float* const* host_tensors, int dtype, void* hip_stream);
+
+/* Bytes of workspace for a request of n_seq sequences and max_rows token
+ * rows: padded calls use (B, B*T); packed calls use (n, total).
+ * Returns 0 for invalid arguments.  Size is linear in max_rows. */
+size_t albert_workspace_bytes(const albert_ctx* ctx, int n_seq, int64_t max_rows);
+
+/* Padded batch.
+ * ids     dev int32 [B, T], row-major; slots t >= lengths[b] are padding
+ *         and are never read.
+ * lengths dev int32 [B]; each in [1, T].
+ * B >= 1, 1 <= T <= max_pos.  B == 0 is an empty request: ALBERT_OK, nothing
+ * is read, written or enqueued.
+ * out     dev fp32 [B, T, out_dim]; rows t >= lengths[b] are written as 0.
+ * ws      dev workspace of ws_bytes >= albert_workspace_bytes(ctx, B, B*T),
+ *         256-byte aligned; its contents on entry are ignored.
+ * Attention of sequence b reads keys 0..lengths[b]-1 only (the pad mask of
+ * "How Kokoro TTS Works and Where CKE Stands", "What ALBERT does here");
+ * positions are 0..lengths[b]-1 and the token type is 0.
+ * IDs and lengths are validated on the device before anything is written to
+ * `out`; on ALBERT_E_LENGTH / ALBERT_E_ID `out` is left byte-for-byte
+ * unchanged.  Argument errors (E_ARG, E_WORKSPACE, E_ALIAS) are detected on
+ * the host before any work is enqueued.  Without ALBERT_ASYNC the call waits
+ * for the stream and returns the device status; with it, the call returns
+ * ALBERT_OK after enqueueing and the device status is read with
+ * albert_read_status(ws, stream).  Calls that share a workspace must be
+ * ordered on one stream. */
+int albert_encode(albert_ctx* ctx, const int32_t* ids, const int32_t* lengths,
+                  int B, int T, float* out, void* ws, size_t ws_bytes,
+                  void* hip_stream, unsigned flags);
+
+/* Packed (varlen) batch of n sequences with no padding.
+ * ids        dev int32 [total]; sequence s occupies rows cu[s] .. cu[s+1]-1.
+ * cu_seqlens dev int32 [n + 1]; cu[0] = 0, cu[n] = total, and every length
+ *            cu[s+1]-cu[s] in [1, max_len]; positions restart at 0 per
+ *            sequence.
+ * max_len    host-side bound on every length, 1 <= max_len <= max_pos.
+ * out        dev fp32 [total, out_dim].
+ * ws         workspace of albert_workspace_bytes(ctx, n, total) bytes.
+ * n == 0 with total == 0 is an empty request (ALBERT_OK, nothing enqueued).
+ * Validation, errors and flags as albert_encode. */
+int albert_encode_varlen(albert_ctx* ctx, const int32_t* ids, const int32_t* cu_seqlens,
+                         int n, int total, int max_len, float* out, void* ws,
+                         size_t ws_bytes, void* hip_stream, unsigned flags);
+
+/* Wait for hip_stream and return the device status word that the last
+ * request enqueued with this workspace left there (ALBERT_E_HIP if the read
+ * fails). */
+int albert_read_status(const void* ws, void* hip_stream);
+
+/* Debug taps: where a request's intermediate tensors sit in the workspace
+ * after it completes (checkpoints at fixed boundaries of the graph, in graph
+ * order).  Rows are packed tokens (sequence s at rows cu[s]..cu[s+1]-1);
+ * elements are the context's dtype (fp32 or bf16) unless noted.
+ *   0 STATUS  int32 [1]          1 CU     int32 [n_seq + 1]
+ *   2 ROW_SEQ int32 [rows]       3 ROW_POS int32 [rows]
+ *   4 EMB  [rows, E]   embedding sum after LayerNorm
+ *   5 X    [rows, H]   input projection (n_iter = 0) or last layer output
+ *   6 QKV  [rows, 3H]  last execution's q/8 | k | v, head h at h*64
+ *   7 CTX  [rows, H]   last execution's attention context (token-major)
+ *   8 X1   [rows, H]   last execution's post-attention LayerNorm output
+ *   9 G    [rows, F]   last execution's GELU output
+ * Writes the byte offset from ws, the byte size, and the row stride in
+ * elements (0 for the int32 taps).  Host-only; enqueues nothing. */
+enum albert_tap {
+  ALBERT_TAP_STATUS = 0, ALBERT_TAP_CU = 1, ALBERT_TAP_ROW_SEQ = 2,
+  ALBERT_TAP_ROW_POS = 3, ALBERT_TAP_EMB = 4, ALBERT_TAP_X = 5,
+  ALBERT_TAP_QKV = 6, ALBERT_TAP_CTX = 7, ALBERT_TAP_X1 = 8, ALBERT_TAP_G = 9
+};
+int albert_tap(const albert_ctx* ctx, int n_seq, int64_t max_rows, int tap,
+               size_t* offset, size_t* bytes, int64_t* row_stride);
+
+/* Release the context's device memory.  NULL is accepted. */
+void albert_free(albert_ctx* ctx);
+
+/* Static description of a status code. */
+const char* albert_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* ALBERT_H */

@@ -1,0 +1,90 @@
+"""Host-side checks of the C-ABI library (no GPU work is launched).
+
+The library must load, export every entry point include/albert.h declares,
+and answer the host-only queries (configuration, tensor names and shapes,
+status strings, argument rejection) without touching a device.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "albert.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    import torch  # noqa: F401  (shares its HIP runtime with the library)
+    import albert_transformer_amd as A
+    return A.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(albert_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_exports():
+    import albert_transformer_amd as A
+    assert declared_functions() == sorted(A.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(L):
+    for name in declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_default_config_and_tensor_table(L):
+    import albert_transformer_amd as A
+    c = A.default_config()
+    k = synth.KOKORO
+    for f in ("vocab", "max_pos", "n_types", "emb", "hidden", "heads", "head_dim",
+              "ffn", "n_iter", "out_dim"):
+        assert getattr(c, f) == getattr(k, f), f
+    assert abs(c.ln_eps - 1e-12) < 1e-18
+    shapes = k.shapes()
+    for i, name in enumerate(synth.TENSOR_NAMES):
+        assert L.albert_tensor_name(i).decode() == name
+        r, cc = ctypes.c_int64(), ctypes.c_int64()
+        assert L.albert_tensor_shape(ctypes.byref(c), i, ctypes.byref(r), ctypes.byref(cc)) == 0
+        shp = shapes[name]
+        assert (r.value, cc.value) == (shp[0], shp[1] if len(shp) == 2 else 1)
+    assert L.albert_tensor_name(25) is None
+    assert L.albert_tensor_name(-1) is None
+
+
+def test_config_rejections(L):
+    import albert_transformer_amd as A
+    r, cc = ctypes.c_int64(), ctypes.c_int64()
+    for bad in (dict(hidden=1024), dict(heads=8), dict(ffn=1000), dict(out_dim=100),
+                dict(max_pos=513), dict(n_iter=-1), dict(emb=64)):
+        c = A.default_config(**bad)
+        assert L.albert_tensor_shape(ctypes.byref(c), 0, ctypes.byref(r), ctypes.byref(cc)) == A.E_ARG
+    h = ctypes.c_void_p()
+    ptrs = (ctypes.c_void_p * 25)()
+    c = A.default_config(hidden=1024)
+    assert L.albert_load_weights(ctypes.byref(h), ctypes.byref(c), ptrs, 1, None) == A.E_ARG
+    assert h.value is None
+
+
+def test_null_context_is_rejected_without_device_work(L):
+    import albert_transformer_amd as A
+    assert L.albert_workspace_bytes(None, 4, 512) == 0
+    assert L.albert_encode(None, None, None, 1, 8, None, None, 0, None, 0) == A.E_ARG
+    assert L.albert_encode_varlen(None, None, None, 1, 8, 8, None, None, 0, None, 0) == A.E_ARG
+    assert L.albert_read_status(None, None) == A.E_ARG
+    off, nb, st = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_int64()
+    assert L.albert_tap(None, 1, 1, 0, ctypes.byref(off), ctypes.byref(nb), ctypes.byref(st)) == A.E_ARG
+    L.albert_free(None)
+
+
+def test_status_strings(L):
+    import albert_transformer_amd as A
+    for code in A.STATUS_NAMES:
+        assert A.status_str(code)
+    assert A.status_str(99) == "unknown status"

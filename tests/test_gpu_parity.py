@@ -1,0 +1,294 @@
+"""GPU parity: the HIP library (through its C ABI) against the float64 oracle.
+
+Tolerances: bf16 path max |error| <= 3e-2 and per-token cosine >= 0.999;
+fp32 debug path max |error| <= 1e-4; integer bookkeeping bit-exact.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+from _gpu import check, dev, encoder, oracle_weights, read_tap
+
+pytestmark = pytest.mark.gpu
+K = synth.KOKORO
+
+
+def _expected_rows(lengths):
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    row_seq = np.repeat(np.arange(len(lengths)), lengths).astype(np.int32)
+    row_pos = np.concatenate([np.arange(L) for L in lengths]).astype(np.int32)
+    return cu, row_seq, row_pos
+
+
+def _run_padded(enc, wl):
+    import torch
+    ids, lens = dev(wl.ids), dev(wl.lengths)
+    B, T = wl.ids.shape
+    ws = enc.new_workspace(B, B * T)
+    out = torch.full((B, T, K.out_dim), float("nan"), device="cuda")
+    rc = enc.encode_raw(ids, lens, out, ws)
+    assert rc == 0, rc
+    return out.cpu().numpy().astype(np.float64), ws
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_stage_checkpoints_one_execution(dtype):
+    """Checkpoints in graph order with one execution of the layer: integer
+    bookkeeping, embedding LN, Q|K|V, attention context, both LayerNorms,
+    GELU, output."""
+    enc = encoder(dtype, n_iter=1)
+    W = oracle_weights(dtype)
+    wl = synth.random_padded(31, B=3, T=70, lo=1, hi=70)
+    wl.lengths[:] = [70, 33, 1]
+    out, ws = _run_padded(enc, wl)
+    B, T = wl.ids.shape
+    rows = int(wl.lengths.sum())
+    cu, row_seq, row_pos = _expected_rows(wl.lengths)
+    assert np.array_equal(read_tap(enc, ws, B, B * T, "cu", 0)[:B + 1], cu)
+    assert np.array_equal(read_tap(enc, ws, B, B * T, "row_seq", 0)[:rows], row_seq)
+    assert np.array_equal(read_tap(enc, ws, B, B * T, "row_pos", 0)[:rows], row_pos)
+    assert read_tap(enc, ws, B, B * T, "status", 0)[0] == 0
+    taps = {n: read_tap(enc, ws, B, B * T, n, rows) for n in ("emb", "qkv", "ctx", "x1", "g", "x")}
+    for b in range(B):
+        L = int(wl.lengths[b])
+        sl = slice(int(cu[b]), int(cu[b + 1]))
+        t = {}
+        ref = oracle.encode_sequence(wl.ids[b, :L], W, K, n_iter=1, taps=t)
+        it = t["iter0"]
+        check(taps["emb"][sl], t["emb"], dtype, f"seq{b} emb")
+        qkv = np.concatenate([it["q"] / 8.0, it["k"], it["v"]], axis=1)
+        check(taps["qkv"][sl], qkv, dtype, f"seq{b} qkv")
+        check(taps["ctx"][sl], it["ctx"], dtype, f"seq{b} ctx")
+        check(taps["x1"][sl], it["h1"], dtype, f"seq{b} x1")
+        check(taps["g"][sl], it["g"], dtype, f"seq{b} gelu")
+        check(taps["x"][sl], it["out"], dtype, f"seq{b} layer out")
+        check(out[b, :L], ref, dtype, f"seq{b} out")
+        assert np.all(out[b, L:] == 0.0)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_zero_executions_is_projection_chain(dtype):
+    enc = encoder(dtype, n_iter=0)
+    W = oracle_weights(dtype)
+    wl = synth.random_padded(32, B=2, T=40, lo=1, hi=40)
+    out, _ = _run_padded(enc, wl)
+    for b in range(2):
+        L = int(wl.lengths[b])
+        check(out[b, :L], oracle.encode_sequence(wl.ids[b, :L], W, K, n_iter=0), dtype,
+              f"n_iter=0 seq{b}")
+
+
+def test_config1_single_utterance_fp32():
+    wl = synth.make_workload(1)
+    enc = encoder("f32")
+    out, _ = _run_padded(enc, wl)
+    ref = oracle.encode(wl.ids, wl.lengths, oracle_weights("f32"), K)
+    check(out, ref, "f32", "config1 B=1 T=36")
+
+
+def test_fp32_ragged_batch():
+    enc = encoder("f32")
+    wl = synth.random_padded(33, B=4, T=150, lo=1, hi=150)
+    wl.lengths[:] = [150, 37, 129, 1]
+    out, _ = _run_padded(enc, wl)
+    ref = oracle.encode(wl.ids, wl.lengths, oracle_weights("f32"), K)
+    check(out, ref, "f32", "fp32 ragged")
+
+
+def test_bf16_ragged_tails_packed():
+    """Lengths around the 32-key block, the 128-query tile and the 256-row
+    GEMM tile boundaries, the longest sequence, and a single token."""
+    import torch
+    lengths = [1, 31, 32, 33, 127, 128, 129, 257, 512]
+    wl = synth.random_packed(34, lengths)
+    enc = encoder("bf16")
+    out = torch.full((wl.tokens, K.out_dim), float("nan"), device="cuda")
+    ws = enc.new_workspace(len(lengths), wl.tokens)
+    rc = enc.encode_varlen_raw(dev(wl.ids), dev(wl.cu_seqlens), 512, out, ws)
+    assert rc == 0
+    ref = oracle.encode_varlen(wl.ids, wl.cu_seqlens, oracle_weights("bf16"), K)
+    check(out.cpu().numpy(), ref, "bf16", "packed ragged tails")
+
+
+def _sample(lengths, k, rng):
+    order = np.argsort(lengths)
+    pick = {int(order[0]), int(order[-1])}
+    while len(pick) < min(k, len(lengths)):
+        pick.add(int(rng.integers(0, len(lengths))))
+    return sorted(pick)
+
+
+@pytest.mark.parametrize("k,nsample", [(2, 4), (3, 3), (4, 2), (5, 5)])
+def test_full_size_configs_sampled(k, nsample):
+    """The bench's launch at full size; the oracle checks sampled sequences
+    (the longest, the shortest and random others)."""
+    import torch
+    wl = synth.make_workload(k)
+    enc = encoder("bf16")
+    W = oracle_weights("bf16")
+    rng = np.random.default_rng(500 + k)
+    seqs = _sample(wl.lengths, nsample, rng)
+    if wl.packed:
+        out = torch.full((wl.tokens, K.out_dim), float("nan"), device="cuda")
+        ws = enc.new_workspace(wl.n_seq, wl.tokens)
+        rc = enc.encode_varlen_raw(dev(wl.ids), dev(wl.cu_seqlens), wl.T, out, ws)
+        assert rc == 0
+        got = out.cpu().numpy()
+        assert np.all(np.isfinite(got))
+        ref = oracle.encode_varlen(wl.ids, wl.cu_seqlens, W, K, seqs=seqs)
+        cu = wl.cu_seqlens
+        for s in seqs:
+            check(got[cu[s]:cu[s + 1]], ref[cu[s]:cu[s + 1]], "bf16", f"config{k} seq{s}")
+    else:
+        got, _ = _run_padded(enc, wl)
+        assert np.all(np.isfinite(got))
+        ref = oracle.encode(wl.ids, wl.lengths, W, K, seqs=seqs)
+        for s in seqs:
+            L = int(wl.lengths[s])
+            check(got[s, :L], ref[s, :L], "bf16", f"config{k} seq{s}")
+        pad = np.arange(wl.T)[None, :] >= wl.lengths[:, None]
+        assert np.all(got[pad] == 0.0)
+
+
+def test_packed_equals_padded_bitwise():
+    """Every row is computed independently of the others apart from its own
+    sequence's keys, so the same sequences give identical bits whether they
+    arrive padded or packed."""
+    import torch
+    enc = encoder("bf16")
+    wl = synth.random_padded(35, B=6, T=200, lo=1, hi=200)
+    out_pad, _ = _run_padded(enc, wl)
+    packed = np.concatenate([wl.ids[b, :L] for b, L in enumerate(wl.lengths)]).astype(np.int32)
+    cu = np.concatenate([[0], np.cumsum(wl.lengths)]).astype(np.int32)
+    out = torch.empty((int(cu[-1]), K.out_dim), device="cuda")
+    ws = enc.new_workspace(6, int(cu[-1]))
+    assert enc.encode_varlen_raw(dev(packed), dev(cu), 200, out, ws) == 0
+    got = out.cpu().numpy()
+    for b, L in enumerate(wl.lengths):
+        assert np.array_equal(got[cu[b]:cu[b + 1]], out_pad[b, :L].astype(np.float32))
+
+
+def test_pad_slots_and_more_padding_do_not_change_real_tokens():
+    enc = encoder("bf16")
+    wl = synth.random_padded(36, B=3, T=64, lo=5, hi=60)
+    a, _ = _run_padded(enc, wl)
+    wl2 = synth.Workload(wl.name, wl.dtype, wl.ids.copy(), wl.lengths, wl.T)
+    for b, L in enumerate(wl.lengths):
+        wl2.ids[b, L:] = 999  # pad slots are never read, even out of range
+    b_, _ = _run_padded(enc, wl2)
+    ids3 = np.concatenate([wl.ids, np.zeros((3, 100), np.int32)], axis=1)
+    c, _ = _run_padded(enc, synth.Workload(wl.name, wl.dtype, ids3, wl.lengths, 164))
+    for b, L in enumerate(wl.lengths):
+        assert np.array_equal(a[b, :L], b_[b, :L])
+        assert np.array_equal(a[b, :L], c[b, :L])
+
+
+def test_determinism_and_no_carry_over():
+    """Bitwise-identical repeats, and a different request in between leaves
+    no state behind (second request with a different length)."""
+    enc = encoder("bf16")
+    wa = synth.random_padded(37, B=5, T=90)
+    wb = synth.random_padded(38, B=9, T=300)
+    a1, _ = _run_padded(enc, wa)
+    _run_padded(enc, wb)
+    a2, _ = _run_padded(enc, wa)
+    assert np.array_equal(a1, a2)
+
+
+def test_repeated_ids():
+    enc = encoder("bf16")
+    ids = np.full((2, 50), 7, np.int32)
+    lengths = np.array([50, 20], np.int32)
+    wl = synth.Workload("repeated ids", "bf16", ids, lengths, 50)
+    out, _ = _run_padded(enc, wl)
+    ref = oracle.encode(ids, lengths, oracle_weights("bf16"), K)
+    check(out[0, :50], ref[0, :50], "bf16", "repeated ids 50")
+    check(out[1, :20], ref[1, :20], "bf16", "repeated ids 20")
+
+
+def test_rejections_leave_output_untouched():
+    import torch
+    import albert_transformer_amd as A
+    enc = encoder("bf16")
+    B, T = 3, 32
+    ids = np.ones((B, T), np.int32)
+    lengths = np.array([32, 10, 5], np.int32)
+    ws = enc.new_workspace(B, B * T)
+    canary = torch.full((B, T, K.out_dim), 12345.0, device="cuda")
+
+    def call(i, l, **kw):
+        out = canary.clone()
+        rc = enc.encode_raw(dev(i), dev(l), out, ws, **kw)
+        assert torch.equal(out, canary), "output changed on a rejected request"
+        return rc
+
+    bad_id = ids.copy()
+    bad_id[1, 9] = 178
+    assert call(bad_id, lengths) == A.E_ID
+    bad_id[1, 9] = -1
+    assert call(bad_id, lengths) == A.E_ID
+    assert call(ids, np.array([32, 0, 5], np.int32)) == A.E_LENGTH
+    assert call(ids, np.array([33, 1, 5], np.int32)) == A.E_LENGTH
+    need = enc.workspace_bytes(B, B * T)
+    assert call(ids, lengths, ws_bytes=need - 1) == A.E_WORKSPACE
+    # an id beyond the length is a pad slot: accepted
+    ok_ids = ids.copy()
+    ok_ids[2, 7] = 5000
+    out = canary.clone()
+    assert enc.encode_raw(dev(ok_ids), dev(lengths), out, ws) == 0
+    # aliasing: output inside the workspace
+    wsv = ws[: B * T * K.out_dim * 4].view(torch.float32)
+    assert lib_encode_alias(enc, ids, lengths, wsv, ws) == A.E_ALIAS
+    # T beyond the position table
+    big = np.ones((1, 513), np.int32)
+    out2 = torch.empty((1, 513, K.out_dim), device="cuda")
+    ws2 = enc.new_workspace(1, 513)
+    assert enc.encode_raw(dev(big), dev(np.array([513], np.int32)), out2, ws2) == A.E_ARG
+    # the context is still usable
+    assert enc.encode_raw(dev(ids), dev(lengths), out, ws) == 0
+
+
+def lib_encode_alias(enc, ids, lengths, out_view, ws):
+    return enc.encode_raw(dev(ids), dev(lengths), out_view, ws)
+
+
+def test_packed_rejections():
+    import torch
+    import albert_transformer_amd as A
+    enc = encoder("bf16")
+    ids = np.ones(40, np.int32)
+    ws = enc.new_workspace(3, 40)
+    canary = torch.full((40, K.out_dim), -7.0, device="cuda")
+    for cu, max_len, code in (([0, 10, 10, 40], 40, A.E_LENGTH),   # empty sequence
+                              ([0, 10, 25, 39], 40, A.E_LENGTH),   # cu[n] != total
+                              ([1, 10, 25, 40], 40, A.E_LENGTH),   # cu[0] != 0
+                              ([0, 10, 25, 40], 12, A.E_LENGTH)):  # longer than max_len
+        out = canary.clone()
+        rc = enc.encode_varlen_raw(dev(ids), dev(np.array(cu, np.int32)), max_len, out, ws)
+        assert rc == code, (cu, rc)
+        assert torch.equal(out, canary)
+    bad = ids.copy()
+    bad[39] = 178
+    out = canary.clone()
+    assert enc.encode_varlen_raw(dev(bad), dev(np.array([0, 10, 25, 40], np.int32)), 40,
+                                 out, ws) == A.E_ID
+    assert torch.equal(out, canary)
+
+
+def test_async_flag_and_empty_batch():
+    import torch
+    import albert_transformer_amd as A
+    enc = encoder("bf16")
+    wl = synth.random_padded(39, B=2, T=16)
+    ws = enc.new_workspace(2, 32)
+    out = torch.empty((2, 16, K.out_dim), device="cuda")
+    assert enc.encode_raw(dev(wl.ids), dev(wl.lengths), out, ws, flags=A.ASYNC) == 0
+    assert A.read_status(ws) == 0
+    bad = wl.ids.copy()
+    bad[0, 0] = 400
+    assert enc.encode_raw(dev(bad), dev(wl.lengths), out, ws, flags=A.ASYNC) == 0
+    assert A.read_status(ws) == A.E_ID
+    empty = torch.empty((0, 16), dtype=torch.int32, device="cuda")
+    assert enc.encode_raw(empty, torch.empty(0, dtype=torch.int32, device="cuda"), out, ws) == 0
