@@ -27,7 +27,8 @@ TAPS = {"status": 0, "cu": 1, "row_seq": 2, "row_pos": 3, "emb": 4, "x": 5,
 EXPORTS = ("albert_default_config", "albert_tensor_name", "albert_tensor_shape",
            "albert_load_weights", "albert_workspace_bytes", "albert_encode",
            "albert_encode_varlen", "albert_read_status", "albert_tap", "albert_free",
-           "albert_status_str")
+           "albert_status_str", "albert_time_kernel", "albert_kernel_time")
+KERNEL_KINDS = ("embed", "proj", "qkv", "attn", "attn_out_ln", "ffn1_gelu", "ffn2_ln", "out")
 
 
 class Config(ctypes.Structure):
@@ -78,6 +79,10 @@ def lib():
     L.albert_free.restype = None
     L.albert_status_str.argtypes = [i32]
     L.albert_status_str.restype = ctypes.c_char_p
+    L.albert_time_kernel.argtypes = [vp, i32, i32]
+    L.albert_time_kernel.restype = i32
+    L.albert_kernel_time.argtypes = [vp, ctypes.POINTER(i32), ctypes.POINTER(ctypes.c_double)]
+    L.albert_kernel_time.restype = i32
     _LIB = L
     return L
 
@@ -161,6 +166,21 @@ class Encoder:
         if rc != OK:
             raise AlbertError(rc, "albert_tap")
         return off.value, nb.value, st.value
+
+    def time_kernel(self, kind: str | None, max_launches: int = 1024) -> None:
+        """Bracket later launches of one kernel kind with HIP events."""
+        k = -1 if kind is None else KERNEL_KINDS.index(kind)
+        rc = lib().albert_time_kernel(self.handle, k, max_launches)
+        if rc != OK:
+            raise AlbertError(rc, "albert_time_kernel")
+
+    def kernel_time(self) -> tuple[int, float]:
+        """(launches timed, summed milliseconds) since time_kernel()."""
+        n, ms = ctypes.c_int(), ctypes.c_double()
+        rc = lib().albert_kernel_time(self.handle, ctypes.byref(n), ctypes.byref(ms))
+        if rc != OK:
+            raise AlbertError(rc, "albert_kernel_time")
+        return n.value, ms.value
 
     def new_workspace(self, n_seq: int, max_rows: int):
         import torch

@@ -33,6 +33,10 @@ struct albert_ctx {
   const void *word, *pos, *type, *proj_w, *qkv_w, *o_w, *ffn1_w, *ffn2_w, *out_w;
   const float *emb_g, *emb_b, *proj_b, *qkv_b, *o_b, *ln1_g, *ln1_b, *ffn1_b, *ffn2_b,
       *ln2_g, *ln2_b, *out_b;
+  // optional kernel timing (albert_time_kernel)
+  int time_kind = -1;
+  int n_timed = 0;
+  std::vector<hipEvent_t> ev;  // start/stop pairs
 };
 
 namespace {
@@ -136,6 +140,19 @@ void gemm_ln(GemmArgs g, int64_t max_rows, hipStream_t s) {
   launch_gemm<T, 128, 768, 2, 4, EPI_LN>(g, max_rows, s);
 }
 
+// Launch `fn` on stream s, bracketed by timing events when `kind` is the
+// kernel kind selected with albert_time_kernel().
+template <typename Fn>
+void timed(albert_ctx* c, int kind, hipStream_t s, Fn&& fn) {
+  const bool on = c->time_kind == kind && 2 * (c->n_timed + 1) <= (int)c->ev.size();
+  if (on) (void)hipEventRecord(c->ev[2 * c->n_timed], s);
+  fn();
+  if (on) {
+    (void)hipEventRecord(c->ev[2 * c->n_timed + 1], s);
+    ++c->n_timed;
+  }
+}
+
 template <typename T>
 int run(albert_ctx* c, const int32_t* ids, const int32_t* lens_or_cu, int n_seq, int pad_T,
         int64_t max_rows, int max_len, float* out, void* ws, hipStream_t s) {
@@ -163,9 +180,12 @@ int run(albert_ctx* c, const int32_t* ids, const int32_t* lens_or_cu, int n_seq,
                        (int)max_rows, max_len, cu, status);
   hipLaunchKernelGGL(rows_ids_kernel, dim3(n_seq), dim3(256), 0, s, ids, cu, pad_T, cf.vocab,
                      row_seq, row_pos, status);
-  hipLaunchKernelGGL(embed_ln_kernel<T>, dim3((unsigned)((max_rows + 15) / 16)), dim3(256), 0, s,
-                     ids, pad_T, row_seq, row_pos, m_ptr, (const T*)c->word, (const T*)c->pos,
-                     (const T*)c->type, c->emb_g, c->emb_b, cf.ln_eps, emb, status);
+  timed(c, ALBERT_K_EMBED, s, [&] {
+    hipLaunchKernelGGL(embed_ln_kernel<T>, dim3((unsigned)((max_rows + 15) / 16)), dim3(256), 0,
+                       s, ids, pad_T, row_seq, row_pos, m_ptr, (const T*)c->word,
+                       (const T*)c->pos, (const T*)c->type, c->emb_g, c->emb_b, cf.ln_eps, emb,
+                       status);
+  });
 
   GemmArgs base{};
   base.status = status;
@@ -175,38 +195,40 @@ int run(albert_ctx* c, const int32_t* ids, const int32_t* lens_or_cu, int n_seq,
   GemmArgs g = base;  // input projection E -> H
   g.X = emb; g.ldx = cf.emb; g.W = c->proj_w; g.bias = c->proj_b; g.Y = X; g.ldy = H;
   g.N = H; g.K = cf.emb;
-  gemm_big<T, EPI_BIAS>(g, max_rows, s);
+  timed(c, ALBERT_K_PROJ, s, [&] { gemm_big<T, EPI_BIAS>(g, max_rows, s); });
 
   const int qtiles = (max_len + 127) / 128;
   for (int it = 0; it < cf.n_iter; ++it) {
     g = base;  // fused Q|K|V projection
     g.X = X; g.ldx = H; g.W = c->qkv_w; g.bias = c->qkv_b; g.Y = QKV; g.ldy = 3 * H;
     g.N = 3 * H; g.K = H;
-    gemm_big<T, EPI_BIAS>(g, max_rows, s);
+    timed(c, ALBERT_K_QKV, s, [&] { gemm_big<T, EPI_BIAS>(g, max_rows, s); });
 
     AttnArgs a{QKV, CTX, cu, status};
-    hipLaunchKernelGGL(attention_kernel<T>, dim3(n_seq, cf.heads, qtiles), dim3(256), 0, s, a);
+    timed(c, ALBERT_K_ATTN, s, [&] {
+      hipLaunchKernelGGL(attention_kernel<T>, dim3(n_seq, cf.heads, qtiles), dim3(256), 0, s, a);
+    });
 
     g = base;  // output projection + residual + LayerNorm
     g.X = CTX; g.ldx = H; g.W = c->o_w; g.bias = c->o_b; g.R = X; g.ldr = H;
     g.ln_g = c->ln1_g; g.ln_b = c->ln1_b; g.Y = X1; g.ldy = H; g.N = H; g.K = H;
-    gemm_ln<T>(g, max_rows, s);
+    timed(c, ALBERT_K_ATTN_OUT_LN, s, [&] { gemm_ln<T>(g, max_rows, s); });
 
     g = base;  // FFN 768 -> 2048 + GELU
     g.X = X1; g.ldx = H; g.W = c->ffn1_w; g.bias = c->ffn1_b; g.Y = G; g.ldy = F;
     g.N = F; g.K = H;
-    gemm_big<T, EPI_GELU>(g, max_rows, s);
+    timed(c, ALBERT_K_FFN1_GELU, s, [&] { gemm_big<T, EPI_GELU>(g, max_rows, s); });
 
     g = base;  // FFN 2048 -> 768 + residual + LayerNorm
     g.X = G; g.ldx = F; g.W = c->ffn2_w; g.bias = c->ffn2_b; g.R = X1; g.ldr = H;
     g.ln_g = c->ln2_g; g.ln_b = c->ln2_b; g.Y = X; g.ldy = H; g.N = H; g.K = F;
-    gemm_ln<T>(g, max_rows, s);
+    timed(c, ALBERT_K_FFN2_LN, s, [&] { gemm_ln<T>(g, max_rows, s); });
   }
 
   g = base;  // output projection H -> 512, fp32, into the caller's rows
   g.X = X; g.ldx = H; g.W = c->out_w; g.bias = c->out_b; g.out = out;
   g.row_seq = row_seq; g.row_pos = row_pos; g.out_T = pad_T; g.N = cf.out_dim; g.K = H;
-  gemm_big<T, EPI_OUT>(g, max_rows, s);
+  timed(c, ALBERT_K_OUT, s, [&] { gemm_big<T, EPI_OUT>(g, max_rows, s); });
   if (pad_T)
     hipLaunchKernelGGL(zero_pad_rows_kernel, dim3(n_seq), dim3(256), 0, s, out, cu, pad_T,
                        cf.out_dim, status);
@@ -440,8 +462,48 @@ int albert_tap(const albert_ctx* ctx, int n_seq, int64_t max_rows, int tap, size
   return ALBERT_OK;
 }
 
+static void drop_events(albert_ctx* ctx) {
+  for (hipEvent_t e : ctx->ev) (void)hipEventDestroy(e);
+  ctx->ev.clear();
+  ctx->time_kind = -1;
+  ctx->n_timed = 0;
+}
+
+int albert_time_kernel(albert_ctx* ctx, int kind, int max_launches) {
+  if (!ctx || kind < -1 || kind >= ALBERT_K_COUNT || (kind >= 0 && max_launches < 1))
+    return ALBERT_E_ARG;
+  drop_events(ctx);
+  if (kind < 0) return ALBERT_OK;
+  ctx->ev.resize((size_t)2 * max_launches);
+  for (auto& e : ctx->ev) {
+    if (hipEventCreate(&e) != hipSuccess) {
+      e = nullptr;
+      drop_events(ctx);
+      return ALBERT_E_HIP;
+    }
+  }
+  ctx->time_kind = kind;
+  return ALBERT_OK;
+}
+
+int albert_kernel_time(albert_ctx* ctx, int* launches, double* total_ms) {
+  if (!ctx || !launches || !total_ms) return ALBERT_E_ARG;
+  double sum = 0.0;
+  for (int i = 0; i < ctx->n_timed; ++i) {
+    float ms = 0.f;
+    if (hipEventSynchronize(ctx->ev[2 * i + 1]) != hipSuccess ||
+        hipEventElapsedTime(&ms, ctx->ev[2 * i], ctx->ev[2 * i + 1]) != hipSuccess)
+      return ALBERT_E_HIP;
+    sum += ms;
+  }
+  *launches = ctx->n_timed;
+  *total_ms = sum;
+  return ALBERT_OK;
+}
+
 void albert_free(albert_ctx* ctx) {
   if (!ctx) return;
+  drop_events(ctx);
   if (ctx->mem) (void)hipFree(ctx->mem);
   delete ctx;
 }

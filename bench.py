@@ -1,0 +1,261 @@
+"""Throughput of the MI355X ALBERT phoneme encoder (one GPU).
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 3]
+
+A step is one albert_encode call: the whole encoder forward pass (embedding,
+projection, 12 shared-layer executions, output projection) over one batch
+of synthetic phoneme IDs already resident in HBM.  Prints one JSON line.
+
+Besides the headline tokens/s the line carries
+  roofline      the dominant kernel's algorithmic FLOP per launch divided by
+                its average launch time, measured with HIP events on the
+                library's stream during the timed steps, against MI355X's
+                dense bf16 MFMA peak;
+  cpu_baseline  the float64 oracle timed on this host's cores over a
+                bounded sample of the same sequences (also a parity check of
+                those sequences).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+
+METRIC = "encoded phoneme tokens/sec at B=256,T=128 bf16; % of MFMA roofline"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA (vendor figure)
+PEAK_F32_TFLOPS = 157.3     # MI355X dense fp32 MFMA
+H, E, F, O, NITER = 768, 128, 2048, 512, 12
+
+
+def seq_flops(L: np.ndarray) -> float:
+    """Algorithmic FLOP of one encoder pass over sequences of lengths L."""
+    L = np.asarray(L, np.float64)
+    return float(np.sum(133_103_616.0 * L + 36_864.0 * L * L))
+
+
+def kernel_flops(kind: str, lengths: np.ndarray) -> float:
+    """Algorithmic FLOP of ONE launch of a kernel kind (valid tokens only)."""
+    M = float(np.sum(lengths))
+    L = np.asarray(lengths, np.float64)
+    return {
+        "embed": 0.0,
+        "proj": 2 * M * E * H,
+        "qkv": 2 * M * H * 3 * H,
+        "attn": float(np.sum(4.0 * H * L * L)),
+        "attn_out_ln": 2 * M * H * H,
+        "ffn1_gelu": 2 * M * H * F,
+        "ffn2_ln": 2 * M * F * H,
+        "out": 2 * M * H * O,
+    }[kind]
+
+
+def source_hash() -> str:
+    d = os.path.join(ROOT, "albert_transformer_amd", "csrc")
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(d)):
+        with open(os.path.join(d, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(kind: str, config: int):
+    """HBM bytes per launch from the committed counter summary, or None when
+    the kernels changed since the counters were taken."""
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        t = json.load(f)
+    rec = t.get("kernels", {}).get(kind)
+    if not rec or t.get("source_sha") != source_hash() or t.get("config") != config:
+        return None
+    return rec["fetch_bytes"] + rec["write_bytes"]
+
+
+def cpu_baseline(wl, got, budget_s: float):
+    """Time the float64 oracle on this host over whole sequences of the same
+    workload until `budget_s` seconds have passed; compare the GPU rows."""
+    import oracle
+    from threadpoolctl import threadpool_info
+    W = oracle.prepare_weights(synth.make_weights(), wl.dtype)
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()
+                   if i.get("user_api") == "blas"] or [1])
+    order = np.random.default_rng(7).permutation(wl.n_seq)
+    tokens, done, max_abs, min_cos = 0, 0, 0.0, 1.0
+    t0 = time.perf_counter()
+    for s in order:
+        L = int(wl.lengths[s])
+        if wl.packed:
+            a = int(wl.cu_seqlens[s])
+            ids, rows = wl.ids[a:a + L], got[a:a + L]
+        else:
+            ids, rows = wl.ids[s, :L], got[s, :L]
+        ref = oracle.encode_sequence(ids, W, synth.KOKORO)
+        tokens += L
+        done += 1
+        d = rows.astype(np.float64) - ref
+        max_abs = max(max_abs, float(np.abs(d).max()))
+        cos = (rows * ref).sum(-1) / (np.linalg.norm(rows, axis=-1) * np.linalg.norm(ref, axis=-1))
+        min_cos = min(min_cos, float(cos.min()))
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    base = {"value": tokens / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} of {wl.n_seq} sequences ({tokens} tokens), float64 NumPy/BLAS, "
+                      f"{dt:.1f} s"}
+    parity = {"sequences": done, "max_abs": max_abs, "min_token_cosine": min_cos}
+    return base, parity
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=3, help="workload 1..5 (3 = headline)")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="wall budget of the oracle CPU baseline (0 = skip)")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="run one plain device copy of this size first (counter scaling)")
+    args = ap.parse_args(argv)
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
+              "(the encoder shards as independent data-parallel copies; nothing here "
+              "uses a second GPU).", file=sys.stderr)
+        return 2
+
+    import torch
+    import albert_transformer_amd as A
+
+    torch.cuda.set_device(0)
+    wl = synth.make_workload(args.config)
+    dtype = wl.dtype
+    enc = A.Encoder(synth.make_weights(), dtype)
+    ids = torch.from_numpy(wl.ids).cuda()
+    if wl.packed:
+        cu = torch.from_numpy(wl.cu_seqlens).cuda()
+        out = torch.empty((wl.tokens, O), dtype=torch.float32, device="cuda")
+        ws = enc.new_workspace(wl.n_seq, wl.tokens)
+
+        def step():
+            return enc.encode_varlen_raw(ids, cu, wl.T, out, ws, flags=A.ASYNC)
+    else:
+        lens = torch.from_numpy(wl.lengths).cuda()
+        out = torch.empty((wl.n_seq, wl.T, O), dtype=torch.float32, device="cuda")
+        ws = enc.new_workspace(wl.n_seq, wl.n_seq * wl.T)
+
+        def step():
+            return enc.encode_raw(ids, lens, out, ws, flags=A.ASYNC)
+
+    if args.copy_probe_mib > 0:
+        a = torch.empty(args.copy_probe_mib << 20, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    for _ in range(args.warmup):
+        assert step() == A.OK
+    torch.cuda.synchronize()
+    st = A.read_status(ws)
+    if st != A.OK:
+        raise SystemExit(f"encoder rejected the workload: {A.STATUS_NAMES.get(st, st)}")
+
+    # per-kind breakdown (3 steps each) to find the dominant kernel
+    per_kind = {}
+    for kind in A.KERNEL_KINDS:
+        enc.time_kernel(kind)
+        for _ in range(3):
+            step()
+        n, ms = enc.kernel_time()
+        per_kind[kind] = {"launches_per_step": n // 3, "ms_per_step": ms / 3,
+                          "ms_per_launch": ms / max(n, 1)}
+    enc.time_kernel(None)
+    dominant = max(per_kind, key=lambda k: per_kind[k]["ms_per_step"])
+
+    # timed region: K steps, the dominant kernel bracketed by events
+    launches = per_kind[dominant]["launches_per_step"] * args.steps
+    enc.time_kernel(dominant, max_launches=max(launches, 1))
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    n_dom, ms_dom = enc.kernel_time()
+    enc.time_kernel(None)
+    st = A.read_status(ws)
+    if st != A.OK:
+        raise SystemExit(f"encoder failed during timing: {A.STATUS_NAMES.get(st, st)}")
+
+    elapsed = t1 - t0
+    ms_step = 1e3 * elapsed / args.steps
+    tokens = wl.tokens
+    value = tokens * args.steps / elapsed
+    flops_step = seq_flops(wl.lengths)
+    peak = PEAK_BF16_TFLOPS if dtype == "bf16" else PEAK_F32_TFLOPS
+    launch_ms = ms_dom / max(n_dom, 1)
+    achieved = kernel_flops(dominant, wl.lengths) / (launch_ms * 1e-3) / 1e12
+
+    got = out.cpu().numpy()
+    base, parity = (cpu_baseline(wl, got, args.cpu_seconds) if args.cpu_seconds > 0
+                    else (None, None))
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dtype,
+        "data": "synthetic (seeded N(0,0.02) weights, uniform phoneme ids)",
+        "config": {
+            "workload": wl.name,
+            "sequences": wl.n_seq,
+            "T": wl.T,
+            "packed": wl.packed,
+            "tokens_per_step": tokens,
+            "padded_slots_per_step": wl.rows,
+            "shared_layer_executions": NITER,
+        },
+        "tflops_end_to_end": round(flops_step / (ms_step * 1e-3) / 1e12, 2),
+        "mfma_frac_end_to_end": round(flops_step / (ms_step * 1e-3) / 1e12 / peak, 4),
+        "roofline": {
+            "kernel": dominant,
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / peak, 4),
+            "traffic": traffic_for(dominant, args.config),
+            "ms_per_launch": round(launch_ms, 5),
+            "launches_timed": n_dom,
+        },
+        "kernels_ms_per_step": {k: round(v["ms_per_step"], 4) for k, v in per_kind.items()},
+        "cpu_baseline": base,
+        "parity_sample": parity,
+        "source_sha": source_hash(),
+    }
+    print(json.dumps(line), flush=True)
+    enc.close()
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

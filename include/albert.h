@@ -176,6 +176,31 @@ enum albert_tap {
 int albert_tap(const albert_ctx* ctx, int n_seq, int64_t max_rows, int tap,
                size_t* offset, size_t* bytes, int64_t* row_stride);
 
+/* Kernel kinds of the launch sequence, for albert_time_kernel(). */
+enum albert_kernel_kind {
+  ALBERT_K_EMBED = 0,       /* embedding sum + LayerNorm                    */
+  ALBERT_K_PROJ = 1,        /* 128 -> 768 input projection                  */
+  ALBERT_K_QKV = 2,         /* fused Q|K|V projection, once per execution   */
+  ALBERT_K_ATTN = 3,        /* masked-softmax attention, once per execution */
+  ALBERT_K_ATTN_OUT_LN = 4, /* output projection + residual + LayerNorm     */
+  ALBERT_K_FFN1_GELU = 5,   /* 768 -> 2048 + GELU                           */
+  ALBERT_K_FFN2_LN = 6,     /* 2048 -> 768 + residual + LayerNorm           */
+  ALBERT_K_OUT = 7,         /* 768 -> 512 output projection                 */
+  ALBERT_K_COUNT = 8
+};
+
+/* Measurement hook for benchmarks and profilers.  After this call every
+ * launch of kernel `kind` in later requests on `ctx` (up to max_launches of
+ * them) is bracketed by two HIP events recorded on the request's stream;
+ * kind = -1 switches timing off.  Creates 2*max_launches events (host
+ * call, no device allocation per request).  Not thread-safe: one host thread
+ * per context while timing. */
+int albert_time_kernel(albert_ctx* ctx, int kind, int max_launches);
+
+/* Wait for the recorded events and report how many launches were timed
+ * since albert_time_kernel() and their summed duration in milliseconds. */
+int albert_kernel_time(albert_ctx* ctx, int* launches, double* total_ms);
+
 /* Release the context's device memory.  NULL is accepted. */
 void albert_free(albert_ctx* ctx);
 
