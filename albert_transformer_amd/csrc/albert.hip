@@ -76,6 +76,8 @@ bool shape_of(const albert_config& c, int i, int64_t* r, int64_t* k) {
 
 // The kernels are specialised for Kokoro's geometry; sizes that only change
 // loop counts or table extents are free within tile multiples.
+// (The GEMM K loop runs an even number of 128-byte slices: every K here --
+// 128, 768 and ffn -- is a multiple of 128 elements.)
 bool config_ok(const albert_config& c) {
   return c.emb == 128 && c.hidden == 768 && c.heads == 12 && c.head_dim == 64 &&
          c.vocab >= 1 && c.max_pos >= 1 && c.max_pos <= 512 && c.n_types >= 1 &&
@@ -122,22 +124,22 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
   return x < y + nb && y < x + na;
 }
 
-template <typename T, int BM, int BN, int WGM, int WGN, int EPI>
+template <typename T, int BM, int BN, int WGM, int WGN, int RB, int EPI>
 void launch_gemm(GemmArgs g, int64_t max_rows, hipStream_t s) {
   g.n_tiles = g.N / BN;
   const int64_t mt = (max_rows + BM - 1) / BM;
-  hipLaunchKernelGGL((gemm_kernel<T, BM, BN, WGM, WGN, EPI>), dim3((unsigned)(mt * g.n_tiles)),
-                     dim3(WGM * WGN * 64), 0, s, g);
+  hipLaunchKernelGGL((gemm_kernel<T, BM, BN, WGM, WGN, RB, EPI>),
+                     dim3((unsigned)(mt * g.n_tiles)), dim3(WGM * WGN * 64), 0, s, g);
 }
 
 // Large tiles for plain and GELU epilogues; full-row tiles for LayerNorm.
 template <typename T, int EPI>
 void gemm_big(GemmArgs g, int64_t max_rows, hipStream_t s) {
-  launch_gemm<T, 256, 256, 2, 2, EPI>(g, max_rows, s);
+  launch_gemm<T, 256, 256, 2, 2, 128, EPI>(g, max_rows, s);
 }
 template <typename T>
 void gemm_ln(GemmArgs g, int64_t max_rows, hipStream_t s) {
-  launch_gemm<T, 128, 768, 2, 4, EPI_LN>(g, max_rows, s);
+  launch_gemm<T, 128, 768, 2, 4, 64, EPI_LN>(g, max_rows, s);
 }
 
 // Launch `fn` on stream s, bracketed by timing events when `kind` is the

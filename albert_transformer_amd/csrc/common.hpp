@@ -39,6 +39,9 @@ template <> struct Tr<bf16> {
   static __device__ __forceinline__ frag load(const bf16* p) {
     return *reinterpret_cast<const bf16x8*>(p);
   }
+  // one fragment stored as 16-byte chunks at p0 (and p1 when a fragment
+  // spans two chunks; bf16 fragments are a single chunk)
+  static __device__ __forceinline__ frag load2(const bf16* p0, const bf16*) { return load(p0); }
   // two groups of 4 consecutive elements
   static __device__ __forceinline__ frag load2x4(const bf16* p0, const bf16* p1) {
     bf16x4 a = *reinterpret_cast<const bf16x4*>(p0);
@@ -83,6 +86,12 @@ template <> struct Tr<float> {
     frag f;
     f.lo = *reinterpret_cast<const f32x4*>(p);
     f.hi = *reinterpret_cast<const f32x4*>(p + 4);
+    return f;
+  }
+  static __device__ __forceinline__ frag load2(const float* p0, const float* p1) {
+    frag f;
+    f.lo = *reinterpret_cast<const f32x4*>(p0);
+    f.hi = *reinterpret_cast<const f32x4*>(p1);
     return f;
   }
   static __device__ __forceinline__ frag load2x4(const float* p0, const float* p1) {
