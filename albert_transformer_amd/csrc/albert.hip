@@ -124,22 +124,22 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
   return x < y + nb && y < x + na;
 }
 
-template <typename T, int BM, int BN, int WGM, int WGN, int RB, int EPI>
+template <typename T, int BM, int BN, int WGM, int WGN, int RB, int STAGES, int EPI>
 void launch_gemm(GemmArgs g, int64_t max_rows, hipStream_t s) {
   g.n_tiles = g.N / BN;
   const int64_t mt = (max_rows + BM - 1) / BM;
-  hipLaunchKernelGGL((gemm_kernel<T, BM, BN, WGM, WGN, RB, EPI>),
+  hipLaunchKernelGGL((gemm_kernel<T, BM, BN, WGM, WGN, RB, STAGES, EPI>),
                      dim3((unsigned)(mt * g.n_tiles)), dim3(WGM * WGN * 64), 0, s, g);
 }
 
 // Large tiles for plain and GELU epilogues; full-row tiles for LayerNorm.
 template <typename T, int EPI>
 void gemm_big(GemmArgs g, int64_t max_rows, hipStream_t s) {
-  launch_gemm<T, 256, 256, 2, 2, 128, EPI>(g, max_rows, s);
+  launch_gemm<T, 256, 256, 2, 2, 128, 2, EPI>(g, max_rows, s);
 }
 template <typename T>
 void gemm_ln(GemmArgs g, int64_t max_rows, hipStream_t s) {
-  launch_gemm<T, 128, 768, 2, 4, 64, EPI_LN>(g, max_rows, s);
+  launch_gemm<T, 128, 768, 2, 4, 64, 2, EPI_LN>(g, max_rows, s);
 }
 
 // Launch `fn` on stream s, bracketed by timing events when `kind` is the

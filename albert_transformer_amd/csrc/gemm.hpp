@@ -73,7 +73,7 @@ __device__ __forceinline__ int swz_key(int row) {
   return (row / (256 / RB)) % (RB / 16);
 }
 
-template <typename T, int BM, int BN, int WGM, int WGN, int RB, int EPI>
+template <typename T, int BM, int BN, int WGM, int WGN, int RB, int STAGES, int EPI>
 __global__ void __launch_bounds__(WGM * WGN * 64)
 gemm_kernel(GemmArgs g) {
   typedef Tr<T> TR;
@@ -93,16 +93,42 @@ gemm_kernel(GemmArgs g) {
   static_assert((BM / RPI) % NW == 0, "each DMA slot must be all-X or all-W");
   static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be 32-aligned");
   static_assert(RB == 64 || RB == 128, "row bytes");
+  static_assert(STAGES >= 2 && STAGES <= 4, "stages");
+  static_assert(IPW * (STAGES - 2) <= 63, "vmcnt range");
 
+  // One LDS array per stage, so that alias analysis sees that the DMA into
+  // one stage never touches the stage being read.
   __shared__ __attribute__((aligned(1024))) char lds0[STAGE];
   __shared__ __attribute__((aligned(1024))) char lds1[STAGE];
+  __shared__ __attribute__((aligned(1024))) char lds2[STAGES > 2 ? STAGE : 16];
+  __shared__ __attribute__((aligned(1024))) char lds3[STAGES > 3 ? STAGE : 16];
 
   if (*g.status != 0) return;
   const int M = *g.m_ptr;
-  const int tile = blockIdx.x;
+  // XCD-aware tile order: consecutive workgroups are dealt round-robin to the
+  // 8 XCDs, so renumber them so that each XCD works on a contiguous range of
+  // tiles (row-major, features fastest): the blocks running together on one
+  // XCD then share their X rows and weight columns in that XCD's L2.
+  const int nb = gridDim.x, bid = blockIdx.x;
+  const int xq = nb / 8, xrem = nb % 8, xcd = bid % 8, xl = bid / 8;
+  const int tile = xcd < xrem ? xcd * (xq + 1) + xl : xrem * (xq + 1) + (xcd - xrem) * xq + xl;
   const int tn = tile % g.n_tiles, tm = tile / g.n_tiles;
   const int m0 = tm * BM, n0 = tn * BN;
   if (m0 >= M) return;
+
+  // Per-feature epilogue vectors (bias; LayerNorm gain and shift) are staged
+  // in LDS up front: their load latency hides behind the K loop, and the
+  // epilogue then reads them without waiting on global memory (on gfx9 a
+  // wait for a load also waits for every earlier store).
+  constexpr int NVEC = EPI == EPI_LN ? 3 : 1;
+  __shared__ float vecs[NVEC][BN];
+  for (int c = threadIdx.x; c < BN; c += WGM * WGN * 64) {
+    vecs[0][c] = g.bias[n0 + c];
+    if constexpr (EPI == EPI_LN) {
+      vecs[1 % NVEC][c] = g.ln_g[n0 + c];
+      vecs[2 % NVEC][c] = g.ln_b[n0 + c];
+    }
+  }
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -169,44 +195,86 @@ gemm_kernel(GemmArgs g) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
+  // One slice: fragments of k-step j+1 are read while the matrix cores
+  // work on k-step j, and the scheduler is asked to alternate MFMAs with
+  // LDS reads so the reads hide behind the 32-cycle MFMAs.
   auto compute = [&](const char* buf) __attribute__((always_inline)) {
-#pragma unroll
-    for (int j = 0; j < KSTEPS; ++j) {
-      typename TR::frag fx[TM], fw[TN];
+    typename TR::frag fx[2][TM], fw[2][TN];
+    auto ld = [&](int j, int b) __attribute__((always_inline)) {
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
         const char* p = buf + xrow + i * 32 * RB;
-        fx[i] = TR::load2(reinterpret_cast<const T*>(p + coff[j][0]),
-                          reinterpret_cast<const T*>(p + coff[j][FCH - 1]));
+        fx[b][i] = TR::load2(reinterpret_cast<const T*>(p + coff[j][0]),
+                             reinterpret_cast<const T*>(p + coff[j][FCH - 1]));
       }
 #pragma unroll
       for (int jj = 0; jj < TN; ++jj) {
         const char* p = buf + wrow + jj * 32 * RB;
-        fw[jj] = TR::load2(reinterpret_cast<const T*>(p + coff[j][0]),
-                           reinterpret_cast<const T*>(p + coff[j][FCH - 1]));
+        fw[b][jj] = TR::load2(reinterpret_cast<const T*>(p + coff[j][0]),
+                              reinterpret_cast<const T*>(p + coff[j][FCH - 1]));
       }
+    };
+    ld(0, 0);
+#pragma unroll
+    for (int j = 0; j < KSTEPS; ++j) {
+      if (j + 1 < KSTEPS) ld(j + 1, (j + 1) & 1);
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int jj = 0; jj < TN; ++jj) TR::mma(acc[i][jj], fw[jj], fx[i]);
+        for (int jj = 0; jj < TN; ++jj) {
+          TR::mma(acc[i][jj], fw[j & 1][jj], fx[j & 1][i]);
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // then one LDS read
+        }
     }
   };
 
-  const int KT = g.K / BK;  // even: the host checks K % (2*BK) == 0
-  issue(lds0, 0);
-  for (int kt = 0; kt < KT; kt += 2) {
-    __syncthreads();  // slice kt is in lds0 everywhere; lds1 is free
-    issue(lds1, (kt + 1) * BK);
-    compute(lds0);
-    __syncthreads();  // slice kt+1 is in lds1 everywhere; lds0 is free
-    if (kt + 2 < KT) issue(lds0, (kt + 2) * BK);
-    compute(lds1);
+  // STAGES-deep pipeline: slices t+1 .. t+STAGES-2 stay in flight while
+  // slice t is consumed.  Before the barrier of slice t each wave waits only
+  // for its own DMA of slice t (later slices may still be in flight); the
+  // barrier then makes every wave's part visible and frees the buffer
+  // consumed at t-1, which receives slice t+STAGES-1.  The slice count is a
+  // multiple of STAGES (checked by the host), so the main loop is
+  // branch-free and the last STAGES slices are peeled with static waits.
+  const int KT = g.K / BK;
+#define ALBERT_BUF(i) ((i) == 0 ? lds0 : (i) == 1 ? lds1 : (i) == 2 ? lds2 : lds3)
+#pragma unroll
+  for (int s = 0; s < STAGES - 1; ++s) issue(ALBERT_BUF(s), s * BK);
+  for (int kt = 0; kt < KT - STAGES; kt += STAGES) {
+#pragma unroll
+    for (int s = 0; s < STAGES; ++s) {
+      asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(IPW * (STAGES - 2)) : "memory");
+      issue(ALBERT_BUF((s + STAGES - 1) % STAGES), (kt + s + STAGES - 1) * BK);
+      compute(ALBERT_BUF(s));
+    }
   }
+  {
+    const int kt = KT - STAGES;
+#pragma unroll
+    for (int s = 0; s < STAGES; ++s) {
+      // slices issued after slice kt+s: min(STAGES-2, STAGES-1-s)
+      if constexpr (true) {
+        if (s + 1 < STAGES - 1 || s == 0)
+          asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(IPW * (STAGES - 2)) : "memory");
+        else if (s == STAGES - 2)
+          asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(IPW * (STAGES > 2 ? 1 : 0)) : "memory");
+        else
+          asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+      }
+      if (s == 0) issue(ALBERT_BUF(STAGES - 1), (kt + STAGES - 1) * BK);
+      compute(ALBERT_BUF(s));
+    }
+  }
+#undef ALBERT_BUF
 
   // ---------------------------------------------------------------- epilogue
   // acc[i][j][4q+e] holds token m0 + wm*WTM + i*32 + l32 and feature
-  // n0 + wn*WTN + j*32 + 8q + 4hh + e.
+  // n0 + wn*WTN + j*32 + 8q + 4hh + e.  (The K loop's barriers ordered the
+  // LDS vectors written above.)
+  const float* __restrict__ bias_s = vecs[0];
   if constexpr (EPI == EPI_LN) {
+    const float* __restrict__ g_s = vecs[1 % NVEC];
+    const float* __restrict__ b_s = vecs[2 % NVEC];
     __syncthreads();  // every wave is done with the staging buffers
     float* red = reinterpret_cast<float*>(lds0);  // [WGN][BM]
     const int N = g.N;
@@ -215,21 +283,24 @@ gemm_kernel(GemmArgs g) {
     for (int i = 0; i < TM; ++i) {
       const int m = m0 + wm * WTM + i * 32 + l32;
       const int mr = m < M ? m : M - 1;  // rows past M compute on a valid row, never stored
+      const T* __restrict__ rrow = R + (int64_t)mr * g.ldr + n0 + wn * WTN + 4 * hh;
       float s = 0.f;
 #pragma unroll
-      for (int j = 0; j < TN; ++j)
+      for (int j = 0; j < TN; ++j) {
+        f32x4 rv[4];  // this column group's residual loads first, then one wait
+#pragma unroll
+        for (int q = 0; q < 4; ++q) rv[q] = TR::load4f(rrow + j * 32 + 8 * q);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int n = n0 + wn * WTN + j * 32 + 8 * q + 4 * hh;
-          const f32x4 rv = TR::load4f(R + (int64_t)mr * g.ldr + n);
-          const f32x4 bv = *reinterpret_cast<const f32x4*>(g.bias + n);
+          const int nl = wn * WTN + j * 32 + 8 * q + 4 * hh;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const float v = acc[i][j][4 * q + e] + bv[e] + rv[e];
+            const float v = acc[i][j][4 * q + e] + bias_s[nl + e] + rv[q][e];
             acc[i][j][4 * q + e] = v;
             s += v;
           }
         }
+      }
       s += wave_xor(s, 32);
       if (hh == 0) red[wn * BM + wm * WTM + i * 32 + l32] = s;
     }
@@ -270,13 +341,12 @@ gemm_kernel(GemmArgs g) {
       for (int j = 0; j < TN; ++j)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int n = n0 + wn * WTN + j * 32 + 8 * q + 4 * hh;
-          const f32x4 gv = *reinterpret_cast<const f32x4*>(g.ln_g + n);
-          const f32x4 bv = *reinterpret_cast<const f32x4*>(g.ln_b + n);
+          const int nl = wn * WTN + j * 32 + 8 * q + 4 * hh;
           float o[4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) o[e] = (acc[i][j][4 * q + e] - mean[i]) * rstd * gv[e] + bv[e];
-          TR::store4(Y + (int64_t)m * g.ldy + n, o[0], o[1], o[2], o[3]);
+          for (int e = 0; e < 4; ++e)
+            o[e] = (acc[i][j][4 * q + e] - mean[i]) * rstd * g_s[nl + e] + b_s[nl + e];
+          TR::store4(Y + (int64_t)m * g.ldy + n0 + nl, o[0], o[1], o[2], o[3]);
         }
     }
   } else {
@@ -292,18 +362,17 @@ gemm_kernel(GemmArgs g) {
       for (int j = 0; j < TN; ++j)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int n = n0 + wn * WTN + j * 32 + 8 * q + 4 * hh;
-          const f32x4 bv = *reinterpret_cast<const f32x4*>(g.bias + n);
+          const int nl = wn * WTN + j * 32 + 8 * q + 4 * hh;
           float o[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            o[e] = acc[i][j][4 * q + e] + bv[e];
+            o[e] = acc[i][j][4 * q + e] + bias_s[nl + e];
             if constexpr (EPI == EPI_GELU) o[e] = gelu_tanh(o[e]);
           }
           if constexpr (EPI == EPI_OUT) {
-            *reinterpret_cast<f32x4*>(g.out + orow * g.N + n) = f32x4{o[0], o[1], o[2], o[3]};
+            *reinterpret_cast<f32x4*>(g.out + orow * g.N + n0 + nl) = f32x4{o[0], o[1], o[2], o[3]};
           } else {
-            TR::store4(static_cast<T*>(g.Y) + orow * g.ldy + n, o[0], o[1], o[2], o[3]);
+            TR::store4(static_cast<T*>(g.Y) + orow * g.ldy + n0 + nl, o[0], o[1], o[2], o[3]);
           }
         }
     }
