@@ -13,8 +13,10 @@
 
 #include <cmath>
 #include <cstdint>
+#include <algorithm>
 #include <cstring>
 #include <new>
+#include <type_traits>
 #include <vector>
 
 #include "albert.h"
@@ -28,6 +30,7 @@ struct albert_ctx {
   albert_config cfg;
   int dtype;
   int device;
+  int grid_cap;  // persistent GEMM grid: CUs rounded down to a multiple of 8
   void* mem;
   // device pointers (tables/matrices in dtype, vectors fp32)
   const void *word, *pos, *type, *proj_w, *qkv_w, *o_w, *ffn1_w, *ffn2_w, *out_w;
@@ -124,22 +127,32 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
   return x < y + nb && y < x + na;
 }
 
-template <typename T, int BM, int BN, int WGM, int WGN, int RB, int STAGES, int EPI>
-void launch_gemm(GemmArgs g, int64_t max_rows, hipStream_t s) {
+// Persistent launch: one block per CU at most (a multiple of 8, so that the
+// kernel's XCD-aware tile numbering is a bijection), each walking its tiles.
+template <typename T, int BM, int BN, int WGM, int WGN, int RB, int STAGES, int EPI, bool DEFER>
+void launch_gemm(GemmArgs g, int64_t max_rows, int grid_cap, hipStream_t s) {
   g.n_tiles = g.N / BN;
-  const int64_t mt = (max_rows + BM - 1) / BM;
-  hipLaunchKernelGGL((gemm_kernel<T, BM, BN, WGM, WGN, RB, STAGES, EPI>),
-                     dim3((unsigned)(mt * g.n_tiles)), dim3(WGM * WGN * 64), 0, s, g);
+  const int64_t tiles = (max_rows + BM - 1) / BM * g.n_tiles;
+  const int64_t grid = std::min<int64_t>((tiles + 7) / 8 * 8, grid_cap);
+  hipLaunchKernelGGL((gemm_kernel<T, BM, BN, WGM, WGN, RB, STAGES, EPI, DEFER>),
+                     dim3((unsigned)grid), dim3(WGM * WGN * 64), 0, s, g);
 }
 
 // Large tiles for plain and GELU epilogues; full-row tiles for LayerNorm.
+// bf16 bias/GELU GEMMs with at least 12 (an even number of) K slices keep
+// each tile's outputs in registers and write them during the next tile.
 template <typename T, int EPI>
-void gemm_big(GemmArgs g, int64_t max_rows, hipStream_t s) {
-  launch_gemm<T, 256, 256, 2, 2, 128, 2, EPI>(g, max_rows, s);
+void gemm_big(GemmArgs g, int64_t max_rows, int grid_cap, hipStream_t s) {
+  constexpr bool can_defer = std::is_same<T, bf16>::value && (EPI == EPI_BIAS || EPI == EPI_GELU);
+  const int slices = g.K / (128 / (int)sizeof(T));
+  if (can_defer && slices >= 12 && slices % 2 == 0)
+    launch_gemm<T, 256, 256, 2, 2, 128, 2, EPI, can_defer>(g, max_rows, grid_cap, s);
+  else
+    launch_gemm<T, 256, 256, 2, 2, 128, 2, EPI, false>(g, max_rows, grid_cap, s);
 }
 template <typename T>
-void gemm_ln(GemmArgs g, int64_t max_rows, hipStream_t s) {
-  launch_gemm<T, 128, 768, 2, 4, 64, 2, EPI_LN>(g, max_rows, s);
+void gemm_ln(GemmArgs g, int64_t max_rows, int grid_cap, hipStream_t s) {
+  launch_gemm<T, 128, 768, 2, 4, 64, 2, EPI_LN, false>(g, max_rows, grid_cap, s);
 }
 
 // Launch `fn` on stream s, bracketed by timing events when `kind` is the
@@ -197,14 +210,14 @@ int run(albert_ctx* c, const int32_t* ids, const int32_t* lens_or_cu, int n_seq,
   GemmArgs g = base;  // input projection E -> H
   g.X = emb; g.ldx = cf.emb; g.W = c->proj_w; g.bias = c->proj_b; g.Y = X; g.ldy = H;
   g.N = H; g.K = cf.emb;
-  timed(c, ALBERT_K_PROJ, s, [&] { gemm_big<T, EPI_BIAS>(g, max_rows, s); });
+  timed(c, ALBERT_K_PROJ, s, [&] { gemm_big<T, EPI_BIAS>(g, max_rows, c->grid_cap, s); });
 
   const int qtiles = (max_len + 127) / 128;
   for (int it = 0; it < cf.n_iter; ++it) {
     g = base;  // fused Q|K|V projection
     g.X = X; g.ldx = H; g.W = c->qkv_w; g.bias = c->qkv_b; g.Y = QKV; g.ldy = 3 * H;
     g.N = 3 * H; g.K = H;
-    timed(c, ALBERT_K_QKV, s, [&] { gemm_big<T, EPI_BIAS>(g, max_rows, s); });
+    timed(c, ALBERT_K_QKV, s, [&] { gemm_big<T, EPI_BIAS>(g, max_rows, c->grid_cap, s); });
 
     AttnArgs a{QKV, CTX, cu, status};
     timed(c, ALBERT_K_ATTN, s, [&] {
@@ -214,23 +227,23 @@ int run(albert_ctx* c, const int32_t* ids, const int32_t* lens_or_cu, int n_seq,
     g = base;  // output projection + residual + LayerNorm
     g.X = CTX; g.ldx = H; g.W = c->o_w; g.bias = c->o_b; g.R = X; g.ldr = H;
     g.ln_g = c->ln1_g; g.ln_b = c->ln1_b; g.Y = X1; g.ldy = H; g.N = H; g.K = H;
-    timed(c, ALBERT_K_ATTN_OUT_LN, s, [&] { gemm_ln<T>(g, max_rows, s); });
+    timed(c, ALBERT_K_ATTN_OUT_LN, s, [&] { gemm_ln<T>(g, max_rows, c->grid_cap, s); });
 
     g = base;  // FFN 768 -> 2048 + GELU
     g.X = X1; g.ldx = H; g.W = c->ffn1_w; g.bias = c->ffn1_b; g.Y = G; g.ldy = F;
     g.N = F; g.K = H;
-    timed(c, ALBERT_K_FFN1_GELU, s, [&] { gemm_big<T, EPI_GELU>(g, max_rows, s); });
+    timed(c, ALBERT_K_FFN1_GELU, s, [&] { gemm_big<T, EPI_GELU>(g, max_rows, c->grid_cap, s); });
 
     g = base;  // FFN 2048 -> 768 + residual + LayerNorm
     g.X = G; g.ldx = F; g.W = c->ffn2_w; g.bias = c->ffn2_b; g.R = X1; g.ldr = H;
     g.ln_g = c->ln2_g; g.ln_b = c->ln2_b; g.Y = X; g.ldy = H; g.N = H; g.K = F;
-    timed(c, ALBERT_K_FFN2_LN, s, [&] { gemm_ln<T>(g, max_rows, s); });
+    timed(c, ALBERT_K_FFN2_LN, s, [&] { gemm_ln<T>(g, max_rows, c->grid_cap, s); });
   }
 
   g = base;  // output projection H -> 512, fp32, into the caller's rows
   g.X = X; g.ldx = H; g.W = c->out_w; g.bias = c->out_b; g.out = out;
   g.row_seq = row_seq; g.row_pos = row_pos; g.out_T = pad_T; g.N = cf.out_dim; g.K = H;
-  timed(c, ALBERT_K_OUT, s, [&] { gemm_big<T, EPI_OUT>(g, max_rows, s); });
+  timed(c, ALBERT_K_OUT, s, [&] { gemm_big<T, EPI_OUT>(g, max_rows, c->grid_cap, s); });
   if (pad_T)
     hipLaunchKernelGGL(zero_pad_rows_kernel, dim3(n_seq), dim3(256), 0, s, out, cu, pad_T,
                        cf.out_dim, status);
@@ -358,10 +371,15 @@ int albert_load_weights(albert_ctx** out_ctx, const albert_config* cfg,
   if (!ctx) return ALBERT_E_ARG;
   ctx->cfg = c;
   ctx->dtype = dtype;
-  if (hipGetDevice(&ctx->device) != hipSuccess || hipMalloc(&ctx->mem, off) != hipSuccess) {
+  int n_cu = 0;
+  if (hipGetDevice(&ctx->device) != hipSuccess ||
+      hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, ctx->device) !=
+          hipSuccess ||
+      hipMalloc(&ctx->mem, off) != hipSuccess) {
     delete ctx;
     return ALBERT_E_HIP;
   }
+  ctx->grid_cap = std::max(8, n_cu / 8 * 8);
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (hipMemcpyAsync(ctx->mem, img.data(), off, hipMemcpyHostToDevice, s) != hipSuccess ||
       hipStreamSynchronize(s) != hipSuccess) {

@@ -23,16 +23,28 @@
 // half-waves, then across the WGN waves through LDS.
 //
 // Staging.  Each K slice of RB bytes per row (X rows then W rows) goes from
-// global memory straight into LDS with gfx950's global_load_lds_dwordx4: one
+// global memory straight into LDS with gfx950's buffer_load ... lds DMA: one
 // wave instruction fills 1 KB of LDS, 16 bytes per lane in lane order, with
 // no register round trip.  Because the DMA fixes where each lane's 16 bytes
 // land, bank conflicts of the fragment reads are avoided by choosing which
 // 16-byte chunk each lane fetches: physical chunk p of row r holds logical
 // chunk p ^ key(r), key(r) = (r / (256/RB)) % (RB/16), so the 8 rows read
-// by 8 consecutive lanes fall on distinct banks.  Two LDS buffers alternate
-// (the loop is unrolled by two so each half names its buffers statically):
-// while the matrix cores consume one slice, the DMA fills the other.
+// by 8 consecutive lanes fall on distinct banks.  Each stage has its own LDS
+// array (the loop is unrolled so each step names its buffers statically):
+// while the matrix cores consume one slice, the DMA fills the others.
+//
+// Persistence.  The grid holds at most one block per CU (a multiple of 8);
+// each block walks tiles slot, slot + G, slot + 2G, ...  Once the last slice
+// of a tile has been read out of LDS, the block issues the DMA of the next
+// tile's first slices and loads the next tile's epilogue vectors, and only
+// then runs the current tile's epilogue: the next tile's fill latency hides
+// behind the epilogue's arithmetic and stores.  Tiles of one round are
+// numbered so that each XCD (workgroups are dealt to the 8 XCDs
+// round-robin) gets a contiguous range, features fastest, so blocks running
+// together on one XCD share X rows and weight columns in that XCD's L2.
 #pragma once
+
+#include <type_traits>
 
 #include "common.hpp"
 
@@ -73,11 +85,16 @@ __device__ __forceinline__ int swz_key(int row) {
   return (row / (256 / RB)) % (RB / 16);
 }
 
-template <typename T, int BM, int BN, int WGM, int WGN, int RB, int STAGES, int EPI>
+// Wait until this wave has at most N vector-memory operations outstanding,
+// then meet the other waves of the block.
+#define ALBERT_WAIT_BARRIER(N) asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory")
+
+template <typename T, int BM, int BN, int WGM, int WGN, int RB, int STAGES, int EPI, bool DEFER>
 __global__ void __launch_bounds__(WGM * WGN * 64)
 gemm_kernel(GemmArgs g) {
   typedef Tr<T> TR;
   constexpr int NW = WGM * WGN;
+  constexpr int NT = NW * 64;
   constexpr int CH = 16 / sizeof(T);          // elements per 16-byte chunk
   constexpr int CPR = RB / 16;                // chunks per staged row
   constexpr int BK = RB / sizeof(T);          // K elements per slice
@@ -89,12 +106,23 @@ gemm_kernel(GemmArgs g) {
   constexpr int TM = WTM / 32, TN = WTN / 32;
   constexpr int KSTEPS = BK / 16;             // MFMA k-steps per slice
   constexpr int FCH = 8 / CH;                 // chunks per fragment (1 bf16, 2 fp32)
+  constexpr int NVEC = EPI == EPI_LN ? 3 : 1; // bias (+ LayerNorm gain, shift)
+  constexpr int VPT = (BN + NT - 1) / NT;     // vector elements per thread
   static_assert(NINST % NW == 0, "DMA split");
   static_assert((BM / RPI) % NW == 0, "each DMA slot must be all-X or all-W");
   static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be 32-aligned");
   static_assert(RB == 64 || RB == 128, "row bytes");
   static_assert(STAGES >= 2 && STAGES <= 4, "stages");
   static_assert(IPW * (STAGES - 2) <= 63, "vmcnt range");
+  static_assert(CPR == 8 ? (NW % 2 == 0) : true, "swizzle key must not depend on i");
+  // Deferred stores: bf16 outputs of tile i are kept in registers and written
+  // in NB batches of SB stores during the first NB K-slices of tile i+1.
+  constexpr int NST = TM * TN * 4;            // 8-byte stores per lane per tile
+  constexpr int NB = 8, SB = NST / NB;
+  static_assert(!DEFER || (std::is_same<T, bf16>::value && STAGES == 2 &&
+                           (EPI == EPI_BIAS || EPI == EPI_GELU) && NST % NB == 0 &&
+                           SB <= 63 && TN % (NB / TM) == 0),
+                "deferred stores: bf16, two stages, bias/GELU epilogues");
 
   // One LDS array per stage, so that alias analysis sees that the DMA into
   // one stage never touches the stage being read.
@@ -102,33 +130,17 @@ gemm_kernel(GemmArgs g) {
   __shared__ __attribute__((aligned(1024))) char lds1[STAGE];
   __shared__ __attribute__((aligned(1024))) char lds2[STAGES > 2 ? STAGE : 16];
   __shared__ __attribute__((aligned(1024))) char lds3[STAGES > 3 ? STAGE : 16];
+  // Epilogue vectors, double-buffered across consecutive tiles, and the
+  // LayerNorm cross-wave row reduction.
+  __shared__ float vecs[2][NVEC][BN];
+  __shared__ float red[EPI == EPI_LN ? WGN * BM : 1];
 
   if (*g.status != 0) return;
   const int M = *g.m_ptr;
-  // XCD-aware tile order: consecutive workgroups are dealt round-robin to the
-  // 8 XCDs, so renumber them so that each XCD works on a contiguous range of
-  // tiles (row-major, features fastest): the blocks running together on one
-  // XCD then share their X rows and weight columns in that XCD's L2.
-  const int nb = gridDim.x, bid = blockIdx.x;
-  const int xq = nb / 8, xrem = nb % 8, xcd = bid % 8, xl = bid / 8;
-  const int tile = xcd < xrem ? xcd * (xq + 1) + xl : xrem * (xq + 1) + (xcd - xrem) * xq + xl;
-  const int tn = tile % g.n_tiles, tm = tile / g.n_tiles;
-  const int m0 = tm * BM, n0 = tn * BN;
-  if (m0 >= M) return;
-
-  // Per-feature epilogue vectors (bias; LayerNorm gain and shift) are staged
-  // in LDS up front: their load latency hides behind the K loop, and the
-  // epilogue then reads them without waiting on global memory (on gfx9 a
-  // wait for a load also waits for every earlier store).
-  constexpr int NVEC = EPI == EPI_LN ? 3 : 1;
-  __shared__ float vecs[NVEC][BN];
-  for (int c = threadIdx.x; c < BN; c += WGM * WGN * 64) {
-    vecs[0][c] = g.bias[n0 + c];
-    if constexpr (EPI == EPI_LN) {
-      vecs[1 % NVEC][c] = g.ln_g[n0 + c];
-      vecs[2 % NVEC][c] = g.ln_b[n0 + c];
-    }
-  }
+  const int ntiles = ((M + BM - 1) / BM) * g.n_tiles;
+  const int G = gridDim.x;  // the host launches a multiple of 8 blocks
+  int tile = (blockIdx.x % 8) * (G / 8) + blockIdx.x / 8;
+  if (tile >= ntiles) return;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -136,18 +148,23 @@ gemm_kernel(GemmArgs g) {
   const int wm = wave / WGN, wn = wave % WGN;
   const int l32 = lane & 31, hh = lane >> 5;
 
-  const char* Xt = static_cast<const char*>(g.X) + (int64_t)m0 * g.ldx * (int64_t)sizeof(T);
-  const char* Wt = static_cast<const char*>(g.W) + (int64_t)n0 * g.K * (int64_t)sizeof(T);
+  // ------------------------------------------------------- per-tile state
+  int m0 = 0, n0 = 0;
+  __amdgpu_buffer_rsrc_t xr, wr;
   // Buffer resources over the tile's rows: the hardware range check turns
   // reads of X rows at or past M into zeros (their results are never stored).
-  const int64_t xbytes = (int64_t)(M - m0) * g.ldx * (int64_t)sizeof(T);
-  const int64_t wbytes = (int64_t)(g.N - n0) * g.K * (int64_t)sizeof(T);
-  const int xrec = __builtin_amdgcn_readfirstlane((int)(xbytes > 0x7fffffff ? 0x7fffffff : xbytes));
-  const int wrec = __builtin_amdgcn_readfirstlane((int)(wbytes > 0x7fffffff ? 0x7fffffff : wbytes));
-  const __amdgpu_buffer_rsrc_t xr =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(Xt), (short)0, xrec, kRsrcWord3);
-  const __amdgpu_buffer_rsrc_t wr =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(Wt), (short)0, wrec, kRsrcWord3);
+  auto setup = [&](int t) __attribute__((always_inline)) {
+    m0 = (t / g.n_tiles) * BM;
+    n0 = (t % g.n_tiles) * BN;
+    const char* Xt = static_cast<const char*>(g.X) + (int64_t)m0 * g.ldx * (int64_t)sizeof(T);
+    const char* Wt = static_cast<const char*>(g.W) + (int64_t)n0 * g.K * (int64_t)sizeof(T);
+    const int64_t xbytes = (int64_t)(M - m0) * g.ldx * (int64_t)sizeof(T);
+    const int64_t wbytes = (int64_t)(g.N - n0) * g.K * (int64_t)sizeof(T);
+    const int xrec = __builtin_amdgcn_readfirstlane((int)(xbytes > 0x7fffffff ? 0x7fffffff : xbytes));
+    const int wrec = __builtin_amdgcn_readfirstlane((int)(wbytes > 0x7fffffff ? 0x7fffffff : wbytes));
+    xr = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(Xt), (short)0, xrec, kRsrcWord3);
+    wr = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(Wt), (short)0, wrec, kRsrcWord3);
+  };
 
   // DMA sources.  Instruction i of this wave fills rows q*RPI .. q*RPI+RPI-1
   // of the slice, q = wave + i*NW (X rows first, then W rows); lane t takes
@@ -155,7 +172,6 @@ gemm_kernel(GemmArgs g) {
   // shapes used here the key does not depend on i, so one 32-bit per-lane
   // byte offset (VGPR) plus a uniform per-instruction offset (SGPR) address
   // every load.
-  static_assert(CPR == 8 ? (NW % 2 == 0) : true, "swizzle key must not depend on i");
   const int lrow = lane / CPR;
   const int lchunk = (lane % CPR) ^ swz_key<RB>(wave * RPI + lrow);
   const int xoff = lrow * (int)g.ldx * (int)sizeof(T) + lchunk * 16;
@@ -163,7 +179,10 @@ gemm_kernel(GemmArgs g) {
   const int xrow_b = (int)g.ldx * (int)sizeof(T);  // bytes per X row
   const int wrow_b = g.K * (int)sizeof(T);
   auto issue = [&](char* buf, int k0) __attribute__((always_inline)) {
-    const int kb = k0 * (int)sizeof(T);
+    int kb = k0 * (int)sizeof(T);
+    // keep the per-slice offset opaque so the compiler does not precompute
+    // (and keep live) every slice's per-instruction offsets
+    asm volatile("" : "+s"(kb));
 #pragma unroll
     for (int i = 0; i < IPW; ++i) {
       const int q = wave + i * NW;
@@ -174,6 +193,40 @@ gemm_kernel(GemmArgs g) {
       else
         __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (lds_ptr_t*)dst, 16, woff,
                                                  kb + (q * RPI - BM) * wrow_b, 0, 0);
+    }
+  };
+#define ALBERT_BUF(i) ((i) == 0 ? lds0 : (i) == 1 ? lds1 : (i) == 2 ? lds2 : lds3)
+  auto prologue = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int s = 0; s < STAGES - 1; ++s) issue(ALBERT_BUF(s), s * BK);
+  };
+
+  // Epilogue vectors go through registers into LDS; loading them for the
+  // next tile before the current epilogue hides their latency, and the
+  // epilogue then reads LDS only (on gfx9 a wait for a global load also
+  // waits for every earlier store).
+  float vreg[NVEC][VPT];
+  auto vload = [&](int nb0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) {
+      const int c = tid + k * NT;
+      if (c < BN) {
+        vreg[0][k] = g.bias[nb0 + c];
+        if constexpr (EPI == EPI_LN) {
+          vreg[1 % NVEC][k] = g.ln_g[nb0 + c];
+          vreg[2 % NVEC][k] = g.ln_b[nb0 + c];
+        }
+      }
+    }
+  };
+  auto vstore = [&](int b) __attribute__((always_inline)) {
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) {
+      const int c = tid + k * NT;
+      if (c < BN) {
+#pragma unroll
+        for (int v = 0; v < NVEC; ++v) vecs[b][v][c] = vreg[v][k];
+      }
     }
   };
 
@@ -188,18 +241,48 @@ gemm_kernel(GemmArgs g) {
     for (int f = 0; f < FCH; ++f) coff[j][f] = (((j * 16 + hh * 8) / CH + f) ^ key) * 16;
 
   f32x16 acc[TM][TN];
+
+  // Deferred-store state: packed bf16 pairs, the output resource of the tile
+  // they belong to (rows at or past M fall outside it and are dropped by the
+  // hardware range check, so every batch issues the same number of stores),
+  // and per-row byte offsets.  Before the first tile the resource is empty.
+  uint32_t held[DEFER ? TM : 1][DEFER ? TN : 1][4][2];
+  __amdgpu_buffer_rsrc_t yr = __builtin_amdgcn_make_buffer_rsrc(g.Y, (short)0, 0, kRsrcWord3);
+  int hoff[TM];
 #pragma unroll
-  for (int i = 0; i < TM; ++i)
+  for (int i = 0; i < TM; ++i) hoff[i] = 0;
+  if constexpr (DEFER) {
 #pragma unroll
-    for (int j = 0; j < TN; ++j)
+    for (int i = 0; i < TM; ++i)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) held[i][j][q][0] = held[i][j][q][1] = 0u;
+  }
+  // batch b: token tile i = b / (NB/TM), column tiles j in [jb, jb + TN/(NB/TM))
+  auto store_batch = [&](int b) __attribute__((always_inline)) {
+    if constexpr (DEFER) {
+      constexpr int JPB = TN / (NB / TM);
+      const int i = b / (NB / TM), jb = (b % (NB / TM)) * JPB;
+#pragma unroll
+      for (int jj = 0; jj < JPB; ++jj)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+          u32x2 v = {held[i][jb + jj][q][0], held[i][jb + jj][q][1]};
+          __builtin_amdgcn_raw_buffer_store_b64(v, yr, hoff[i] + ((jb + jj) * 32 + 8 * q) * 2, 0, 0);
+        }
+    }
+  };
 
   // One slice: fragments of k-step j+1 are read while the matrix cores
   // work on k-step j, and the scheduler is asked to alternate MFMAs with
-  // LDS reads so the reads hide behind the 32-cycle MFMAs.
+  // LDS reads so the reads hide behind the 32-cycle MFMAs.  Blocks with two
+  // waves per SIMD (8 waves) have half the registers per wave, so they read
+  // each k-step's fragments right before use instead.
+  constexpr int PF = (NW <= 4 && !DEFER) ? 2 : 1;
   auto compute = [&](const char* buf) __attribute__((always_inline)) {
-    typename TR::frag fx[2][TM], fw[2][TN];
+    typename TR::frag fx[PF][TM], fw[PF][TN];
     auto ld = [&](int j, int b) __attribute__((always_inline)) {
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
@@ -214,169 +297,268 @@ gemm_kernel(GemmArgs g) {
                               reinterpret_cast<const T*>(p + coff[j][FCH - 1]));
       }
     };
-    ld(0, 0);
+    if constexpr (PF == 2) ld(0, 0);
 #pragma unroll
     for (int j = 0; j < KSTEPS; ++j) {
-      if (j + 1 < KSTEPS) ld(j + 1, (j + 1) & 1);
+      if constexpr (PF == 2) {
+        if (j + 1 < KSTEPS) ld(j + 1, (j + 1) & 1);
+      } else {
+        ld(j, 0);
+      }
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int jj = 0; jj < TN; ++jj) {
-          TR::mma(acc[i][jj], fw[j & 1][jj], fx[j & 1][i]);
+          TR::mma(acc[i][jj], fw[j % PF][jj], fx[j % PF][i]);
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
           __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // then one LDS read
         }
     }
   };
 
-  // STAGES-deep pipeline: slices t+1 .. t+STAGES-2 stay in flight while
-  // slice t is consumed.  Before the barrier of slice t each wave waits only
-  // for its own DMA of slice t (later slices may still be in flight); the
-  // barrier then makes every wave's part visible and frees the buffer
-  // consumed at t-1, which receives slice t+STAGES-1.  The slice count is a
-  // multiple of STAGES (checked by the host), so the main loop is
-  // branch-free and the last STAGES slices are peeled with static waits.
-  const int KT = g.K / BK;
-#define ALBERT_BUF(i) ((i) == 0 ? lds0 : (i) == 1 ? lds1 : (i) == 2 ? lds2 : lds3)
+  // ------------------------------------------------------------ epilogue
+  // acc[i][j][4q+e] holds token m0 + wm*WTM + i*32 + l32 and feature
+  // n0 + wn*WTN + j*32 + 8q + 4hh + e.
+  auto epilogue = [&](int em0, int en0, int vb) __attribute__((always_inline)) {
+    const float* __restrict__ bias_s = vecs[vb][0];
+    if constexpr (EPI == EPI_LN) {
+      const float* __restrict__ g_s = vecs[vb][1 % NVEC];
+      const float* __restrict__ b_s = vecs[vb][2 % NVEC];
+      const int N = g.N;
+      const T* __restrict__ R = static_cast<const T*>(g.R);
 #pragma unroll
-  for (int s = 0; s < STAGES - 1; ++s) issue(ALBERT_BUF(s), s * BK);
-  for (int kt = 0; kt < KT - STAGES; kt += STAGES) {
+      for (int i = 0; i < TM; ++i) {
+        const int m = em0 + wm * WTM + i * 32 + l32;
+        const int mr = m < M ? m : M - 1;  // rows past M compute on a valid row, never stored
+        const T* __restrict__ rrow = R + (int64_t)mr * g.ldr + en0 + wn * WTN + 4 * hh;
+        float s = 0.f;
 #pragma unroll
-    for (int s = 0; s < STAGES; ++s) {
-      asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(IPW * (STAGES - 2)) : "memory");
-      issue(ALBERT_BUF((s + STAGES - 1) % STAGES), (kt + s + STAGES - 1) * BK);
-      compute(ALBERT_BUF(s));
-    }
-  }
-  {
-    const int kt = KT - STAGES;
+        for (int j = 0; j < TN; ++j) {
+          f32x4 rv[4];  // this column group's residual loads first, then one wait
 #pragma unroll
-    for (int s = 0; s < STAGES; ++s) {
-      // slices issued after slice kt+s: min(STAGES-2, STAGES-1-s)
-      if constexpr (true) {
-        if (s + 1 < STAGES - 1 || s == 0)
-          asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(IPW * (STAGES - 2)) : "memory");
-        else if (s == STAGES - 2)
-          asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(IPW * (STAGES > 2 ? 1 : 0)) : "memory");
-        else
-          asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+          for (int q = 0; q < 4; ++q) rv[q] = TR::load4f(rrow + j * 32 + 8 * q);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int nl = wn * WTN + j * 32 + 8 * q + 4 * hh;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float v = acc[i][j][4 * q + e] + bias_s[nl + e] + rv[q][e];
+              acc[i][j][4 * q + e] = v;
+              s += v;
+            }
+          }
+        }
+        s += wave_xor(s, 32);
+        if (hh == 0) red[wn * BM + wm * WTM + i * 32 + l32] = s;
       }
-      if (s == 0) issue(ALBERT_BUF(STAGES - 1), (kt + STAGES - 1) * BK);
-      compute(ALBERT_BUF(s));
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      float mean[TM];
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        float s = 0.f;
+#pragma unroll
+        for (int w = 0; w < WGN; ++w) s += red[w * BM + wm * WTM + i * 32 + l32];
+        mean[i] = s * (1.0f / N);
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        float s = 0.f;
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float d = acc[i][j][r] - mean[i];
+            s += d * d;
+          }
+        s += wave_xor(s, 32);
+        if (hh == 0) red[wn * BM + wm * WTM + i * 32 + l32] = s;
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      T* __restrict__ Y = static_cast<T*>(g.Y);
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        float s = 0.f;
+#pragma unroll
+        for (int w = 0; w < WGN; ++w) s += red[w * BM + wm * WTM + i * 32 + l32];
+        const float rstd = 1.0f / sqrtf(s * (1.0f / N) + g.eps);
+        const int m = em0 + wm * WTM + i * 32 + l32;
+        if (m >= M) continue;
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int nl = wn * WTN + j * 32 + 8 * q + 4 * hh;
+            float o[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              o[e] = (acc[i][j][4 * q + e] - mean[i]) * rstd * g_s[nl + e] + b_s[nl + e];
+            TR::store4(Y + (int64_t)m * g.ldy + en0 + nl, o[0], o[1], o[2], o[3]);
+          }
+      }
+      // the next tile's epilogue reuses `red`: everyone has read it
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    } else if constexpr (DEFER) {
+      // pack into registers; stored during the next tile's K loop
+      char* ybase = static_cast<char*>(g.Y) + ((int64_t)em0 * g.ldy + en0) * (int64_t)sizeof(T);
+      const int64_t ybytes = (int64_t)(M - em0) * g.ldy * (int64_t)sizeof(T);
+      yr = __builtin_amdgcn_make_buffer_rsrc(
+          ybase, (short)0,
+          __builtin_amdgcn_readfirstlane((int)(ybytes > 0x7fffffff ? 0x7fffffff : ybytes)), kRsrcWord3);
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        hoff[i] = ((wm * WTM + i * 32 + l32) * (int)g.ldy + wn * WTN + 4 * hh) * (int)sizeof(T);
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int nl = wn * WTN + j * 32 + 8 * q + 4 * hh;
+            float o[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              o[e] = acc[i][j][4 * q + e] + bias_s[nl + e];
+              if constexpr (EPI == EPI_GELU) o[e] = gelu_tanh(o[e]);
+            }
+            typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+            bf16x2 p0 = {(bf16)o[0], (bf16)o[1]}, p1 = {(bf16)o[2], (bf16)o[3]};
+            held[i][j][q][0] = __builtin_bit_cast(uint32_t, p0);
+            held[i][j][q][1] = __builtin_bit_cast(uint32_t, p1);
+          }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const int m = em0 + wm * WTM + i * 32 + l32;
+        if (m >= M) continue;
+        int64_t orow = m;
+        if constexpr (EPI == EPI_OUT) {
+          if (g.out_T) orow = (int64_t)g.row_seq[m] * g.out_T + g.row_pos[m];
+        }
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int nl = wn * WTN + j * 32 + 8 * q + 4 * hh;
+            float o[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              o[e] = acc[i][j][4 * q + e] + bias_s[nl + e];
+              if constexpr (EPI == EPI_GELU) o[e] = gelu_tanh(o[e]);
+            }
+            if constexpr (EPI == EPI_OUT) {
+              *reinterpret_cast<f32x4*>(g.out + orow * g.N + en0 + nl) = f32x4{o[0], o[1], o[2], o[3]};
+            } else {
+              TR::store4(static_cast<T*>(g.Y) + orow * g.ldy + en0 + nl, o[0], o[1], o[2], o[3]);
+            }
+          }
+      }
     }
+  };
+
+  // --------------------------------------------------------- tile loop
+  setup(tile);
+  vload(n0);
+  vstore(0);
+  prologue();
+  int vb = 0;
+  const int KT = g.K / BK;  // a multiple of STAGES (checked by the host)
+  for (;;) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+    if constexpr (DEFER) {
+      // Two stages; step t waits for slice t, issues slice t+1, then (t < NB)
+      // the previous tile's store batch t, then computes slice t.  The only
+      // vector-memory operations younger than slice t's DMA at step t are the
+      // SB stores of batch t-1, so the wait lets them stay in flight.
+      // Steps 0..NB+1 are unrolled, then pairs, then the last two peeled
+      // (the host guarantees KT >= NB + 4 and KT even).
+#pragma unroll
+      for (int t = 0; t < NB + 2; ++t) {
+        if (t >= 1 && t <= NB) ALBERT_WAIT_BARRIER(SB);
+        else ALBERT_WAIT_BARRIER(0);
+        issue(ALBERT_BUF((t + 1) % 2), (t + 1) * BK);
+        // all of slice t+1's DMA must be issued before the stores: the next
+        // step's wait counts only the stores as younger operations
+        __builtin_amdgcn_sched_barrier(0);
+        asm volatile("" ::: "memory");
+        if (t < NB) store_batch(t);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(ALBERT_BUF(t % 2));
+      }
+      for (int kt = NB + 2; kt < KT - 2; kt += 2) {
+        ALBERT_WAIT_BARRIER(0);
+        issue(lds1, (kt + 1) * BK);
+        compute(lds0);
+        ALBERT_WAIT_BARRIER(0);
+        issue(lds0, (kt + 2) * BK);
+        compute(lds1);
+      }
+      ALBERT_WAIT_BARRIER(0);
+      issue(lds1, (KT - 1) * BK);
+      compute(lds0);
+      ALBERT_WAIT_BARRIER(0);
+      compute(lds1);
+    } else {
+      // STAGES-deep pipeline: slices t+1 .. t+STAGES-2 stay in flight while
+      // slice t is consumed.  Before the barrier of slice t each wave waits
+      // only for its own DMA of slice t (later slices may still be in flight);
+      // the barrier then makes every wave's part visible and frees the buffer
+      // consumed at t-1, which receives slice t+STAGES-1.  The main loop is
+      // branch-free and the last STAGES slices are peeled with static waits.
+      for (int kt = 0; kt < KT - STAGES; kt += STAGES) {
+  #pragma unroll
+        for (int s = 0; s < STAGES; ++s) {
+          ALBERT_WAIT_BARRIER(IPW * (STAGES - 2));
+          issue(ALBERT_BUF((s + STAGES - 1) % STAGES), (kt + s + STAGES - 1) * BK);
+          compute(ALBERT_BUF(s));
+        }
+      }
+      {
+        const int kt = KT - STAGES;
+  #pragma unroll
+        for (int s = 0; s < STAGES; ++s) {
+          // slices issued after slice kt+s: min(STAGES-2, STAGES-1-s)
+          if (s + 1 < STAGES - 1 || s == 0)
+            ALBERT_WAIT_BARRIER(IPW * (STAGES - 2));
+          else if (s == STAGES - 2)
+            ALBERT_WAIT_BARRIER(IPW * (STAGES > 2 ? 1 : 0));
+          else
+            ALBERT_WAIT_BARRIER(0);
+          if (s == 0) issue(ALBERT_BUF(STAGES - 1), (kt + STAGES - 1) * BK);
+          compute(ALBERT_BUF(s));
+        }
+      }
+    }
+
+    const int next = tile + G;
+    const bool more = next < ntiles;
+    const int em0 = m0, en0 = n0;
+    if (more) {
+      setup(next);
+      vload(n0);
+    }
+    // every wave has finished reading the staging buffers (their reads fed
+    // the MFMAs above), so the next tile's first slices may land there
+    asm volatile("s_barrier" ::: "memory");
+    if (more) prologue();
+    epilogue(em0, en0, vb);
+    if (!more) {
+#pragma unroll
+      for (int bt = 0; bt < NB; ++bt) store_batch(bt);  // last tile: write everything now
+      break;
+    }
+    vstore(vb ^ 1);  // read only after the next tile's K-loop barriers
+    vb ^= 1;
+    tile = next;
   }
 #undef ALBERT_BUF
-
-  // ---------------------------------------------------------------- epilogue
-  // acc[i][j][4q+e] holds token m0 + wm*WTM + i*32 + l32 and feature
-  // n0 + wn*WTN + j*32 + 8q + 4hh + e.  (The K loop's barriers ordered the
-  // LDS vectors written above.)
-  const float* __restrict__ bias_s = vecs[0];
-  if constexpr (EPI == EPI_LN) {
-    const float* __restrict__ g_s = vecs[1 % NVEC];
-    const float* __restrict__ b_s = vecs[2 % NVEC];
-    __syncthreads();  // every wave is done with the staging buffers
-    float* red = reinterpret_cast<float*>(lds0);  // [WGN][BM]
-    const int N = g.N;
-    const T* __restrict__ R = static_cast<const T*>(g.R);
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      const int m = m0 + wm * WTM + i * 32 + l32;
-      const int mr = m < M ? m : M - 1;  // rows past M compute on a valid row, never stored
-      const T* __restrict__ rrow = R + (int64_t)mr * g.ldr + n0 + wn * WTN + 4 * hh;
-      float s = 0.f;
-#pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        f32x4 rv[4];  // this column group's residual loads first, then one wait
-#pragma unroll
-        for (int q = 0; q < 4; ++q) rv[q] = TR::load4f(rrow + j * 32 + 8 * q);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int nl = wn * WTN + j * 32 + 8 * q + 4 * hh;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float v = acc[i][j][4 * q + e] + bias_s[nl + e] + rv[q][e];
-            acc[i][j][4 * q + e] = v;
-            s += v;
-          }
-        }
-      }
-      s += wave_xor(s, 32);
-      if (hh == 0) red[wn * BM + wm * WTM + i * 32 + l32] = s;
-    }
-    __syncthreads();
-    float mean[TM];
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      float s = 0.f;
-#pragma unroll
-      for (int w = 0; w < WGN; ++w) s += red[w * BM + wm * WTM + i * 32 + l32];
-      mean[i] = s * (1.0f / N);
-    }
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      float s = 0.f;
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float d = acc[i][j][r] - mean[i];
-          s += d * d;
-        }
-      s += wave_xor(s, 32);
-      if (hh == 0) red[wn * BM + wm * WTM + i * 32 + l32] = s;
-    }
-    __syncthreads();
-    T* __restrict__ Y = static_cast<T*>(g.Y);
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      float s = 0.f;
-#pragma unroll
-      for (int w = 0; w < WGN; ++w) s += red[w * BM + wm * WTM + i * 32 + l32];
-      const float rstd = 1.0f / sqrtf(s * (1.0f / N) + g.eps);
-      const int m = m0 + wm * WTM + i * 32 + l32;
-      if (m >= M) continue;
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int nl = wn * WTN + j * 32 + 8 * q + 4 * hh;
-          float o[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            o[e] = (acc[i][j][4 * q + e] - mean[i]) * rstd * g_s[nl + e] + b_s[nl + e];
-          TR::store4(Y + (int64_t)m * g.ldy + n0 + nl, o[0], o[1], o[2], o[3]);
-        }
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      const int m = m0 + wm * WTM + i * 32 + l32;
-      if (m >= M) continue;
-      int64_t orow = m;
-      if constexpr (EPI == EPI_OUT) {
-        if (g.out_T) orow = (int64_t)g.row_seq[m] * g.out_T + g.row_pos[m];
-      }
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int nl = wn * WTN + j * 32 + 8 * q + 4 * hh;
-          float o[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            o[e] = acc[i][j][4 * q + e] + bias_s[nl + e];
-            if constexpr (EPI == EPI_GELU) o[e] = gelu_tanh(o[e]);
-          }
-          if constexpr (EPI == EPI_OUT) {
-            *reinterpret_cast<f32x4*>(g.out + orow * g.N + n0 + nl) = f32x4{o[0], o[1], o[2], o[3]};
-          } else {
-            TR::store4(static_cast<T*>(g.Y) + orow * g.ldy + n0 + nl, o[0], o[1], o[2], o[3]);
-          }
-        }
-    }
-  }
 }
+
+#undef ALBERT_WAIT_BARRIER
 
 }  // namespace albert
