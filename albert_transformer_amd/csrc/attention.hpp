@@ -36,7 +36,7 @@ attention_kernel(AttnArgs a) {
   constexpr int KC = 128;                 // keys per staged chunk
   constexpr int VEC = 16 / sizeof(T);
   constexpr int LDKS = D + VEC;           // K rows, padded
-  constexpr int LDVT = KC + VEC;          // V^T rows, padded
+  constexpr int LDVT = KC + 4;            // V^T rows, padded (66 words for bf16)
   __shared__ __attribute__((aligned(16))) T Ks[KC * LDKS];
   __shared__ __attribute__((aligned(16))) T Vt[D * LDVT];
 
@@ -74,19 +74,24 @@ attention_kernel(AttnArgs a) {
       if (j < nk) v = *reinterpret_cast<const uint4*>(base + (int64_t)(c0 + j) * LDQKV + H + h * D + cc * VEC);
       *reinterpret_cast<uint4*>(Ks + j * LDKS + cc * VEC) = v;
     }
-    // V chunk, transposed [dim][key]
-    for (int idx = tid; idx < KC * (D / VEC); idx += 256) {
-      const int j = idx % KC, cc = idx / KC;
-      T tmp[VEC];
-      if (j < nk) {
-        *reinterpret_cast<uint4*>(tmp) =
-            *reinterpret_cast<const uint4*>(base + (int64_t)(c0 + j) * LDQKV + 2 * H + h * D + cc * VEC);
-      } else {
+    // V chunk, transposed [dim][key]: a task reads one 16-byte chunk of two
+    // consecutive key rows (coalesced along the rows) and writes words that
+    // each hold one dim for both keys.
+    for (int idx = tid; idx < (KC / 2) * (D / VEC); idx += 256) {
+      const int cc = idx % (D / VEC), p = idx / (D / VEC);
+      const int j = 2 * p;
+      T t0[VEC], t1[VEC];
+      uint4 u0 = make_uint4(0, 0, 0, 0), u1 = make_uint4(0, 0, 0, 0);
+      if (j < nk) u0 = *reinterpret_cast<const uint4*>(base + (int64_t)(c0 + j) * LDQKV + 2 * H + h * D + cc * VEC);
+      if (j + 1 < nk) u1 = *reinterpret_cast<const uint4*>(base + (int64_t)(c0 + j + 1) * LDQKV + 2 * H + h * D + cc * VEC);
+      *reinterpret_cast<uint4*>(t0) = u0;
+      *reinterpret_cast<uint4*>(t1) = u1;
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) tmp[e] = (T)0.0f;
+      for (int e = 0; e < VEC; ++e) {
+        T* dst = Vt + (cc * VEC + e) * LDVT + j;
+        dst[0] = t0[e];
+        dst[1] = t1[e];
       }
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) Vt[(cc * VEC + e) * LDVT + j] = tmp[e];
     }
     __syncthreads();
 
