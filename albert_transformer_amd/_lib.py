@@ -27,7 +27,8 @@ TAPS = {"status": 0, "cu": 1, "row_seq": 2, "row_pos": 3, "emb": 4, "x": 5,
 EXPORTS = ("albert_default_config", "albert_tensor_name", "albert_tensor_shape",
            "albert_load_weights", "albert_workspace_bytes", "albert_encode",
            "albert_encode_varlen", "albert_read_status", "albert_tap", "albert_free",
-           "albert_status_str", "albert_time_kernel", "albert_kernel_time")
+           "albert_status_str", "albert_time_kernel", "albert_kernel_time",
+           "albert_durations", "albert_expand_workspace_bytes", "albert_expand")
 KERNEL_KINDS = ("embed", "proj", "qkv", "attn", "attn_out_ln", "ffn1_gelu", "ffn2_ln", "out")
 
 
@@ -83,6 +84,12 @@ def lib():
     L.albert_time_kernel.restype = i32
     L.albert_kernel_time.argtypes = [vp, ctypes.POINTER(i32), ctypes.POINTER(ctypes.c_double)]
     L.albert_kernel_time.restype = i32
+    L.albert_durations.argtypes = [vp, i32, i32, ctypes.c_float, vp, vp]
+    L.albert_durations.restype = i32
+    L.albert_expand_workspace_bytes.argtypes = [i32]
+    L.albert_expand_workspace_bytes.restype = sz
+    L.albert_expand.argtypes = [vp, vp, vp, i32, i32, i32, vp, i64, vp, vp, sz, vp, ctypes.c_uint]
+    L.albert_expand.restype = i32
     _LIB = L
     return L
 
@@ -228,6 +235,46 @@ class Encoder:
         if rc != OK:
             raise AlbertError(rc, "albert_encode_varlen")
         return out
+
+
+def durations(logits, speed: float = 1.0, dur=None, stream=None):
+    """Durations from duration logits [total, K] (CUDA fp32) -> int32 [total]."""
+    import torch
+    total, K = logits.shape
+    if dur is None:
+        dur = torch.empty(total, dtype=torch.int32, device="cuda")
+    rc = lib().albert_durations(_ptr(logits), total, K, float(speed), _ptr(dur), _stream(stream))
+    if rc != OK:
+        raise AlbertError(rc, "albert_durations")
+    return dur
+
+
+def expand_workspace_bytes(total: int) -> int:
+    return int(lib().albert_expand_workspace_bytes(total))
+
+
+def expand_raw(feat, dur, cu_tok, max_frames, out, cu_frames, ws, stream=None, flags=0,
+               ws_bytes=None) -> int:
+    """Length regulation on caller tensors; returns the status code."""
+    total, C = feat.shape
+    nb = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
+    return lib().albert_expand(_ptr(feat), _ptr(dur), _ptr(cu_tok), cu_tok.numel() - 1, total, C,
+                               _ptr(out), int(max_frames), _ptr(cu_frames), _ptr(ws), nb,
+                               _stream(stream), flags)
+
+
+def expand(feat, dur, cu_tok, max_frames, stream=None):
+    """feat fp32 [total, C], dur int32 [total], cu_tok int32 [n+1] (CUDA)
+    -> (frames fp32 [A, C], cu_frames int32 [n+1])."""
+    import torch
+    total, C = feat.shape
+    out = torch.empty((int(max_frames), C), dtype=torch.float32, device="cuda")
+    cuf = torch.empty(cu_tok.numel(), dtype=torch.int32, device="cuda")
+    ws = torch.empty(expand_workspace_bytes(total), dtype=torch.uint8, device="cuda")
+    rc = expand_raw(feat, dur, cu_tok, max_frames, out, cuf, ws, stream)
+    if rc != OK:
+        raise AlbertError(rc, "albert_expand")
+    return out[: int(cuf[-1].item())], cuf
 
 
 def read_status(ws, stream=None) -> int:

@@ -21,6 +21,7 @@
 
 #include "albert.h"
 #include "attention.hpp"
+#include "duration.hpp"
 #include "gemm.hpp"
 #include "prologue.hpp"
 
@@ -519,6 +520,70 @@ int albert_kernel_time(albert_ctx* ctx, int* launches, double* total_ms) {
   *launches = ctx->n_timed;
   *total_ms = sum;
   return ALBERT_OK;
+}
+
+int albert_durations(const float* logits, int total, int K, float speed, int32_t* dur,
+                     void* stream) {
+  if (!logits || !dur || total < 1 || K < 1 || !std::isfinite(speed) || speed <= 0.f)
+    return ALBERT_E_ARG;
+  if (overlaps(dur, (size_t)total * 4, logits, (size_t)total * K * 4)) return ALBERT_E_ALIAS;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipLaunchKernelGGL(durations_kernel, dim3((unsigned)((total + 3) / 4)), dim3(256), 0, s, logits,
+                     total, K, 1.0f / speed, dur);
+  return hipGetLastError() == hipSuccess ? ALBERT_OK : ALBERT_E_HIP;
+}
+
+namespace {
+struct ExpandLayout {
+  size_t status, excl, block_sum, total;
+  int nblocks;
+};
+ExpandLayout expand_plan(int total) {
+  ExpandLayout L{};
+  L.nblocks = (total + 1023) / 1024;
+  size_t off = 0;
+  L.status = off; off += kAlign;
+  L.excl = off; off += align_up((size_t)total * 8, kAlign);
+  L.block_sum = off; off += align_up((size_t)L.nblocks * 8, kAlign);
+  L.total = off;
+  return L;
+}
+}  // namespace
+
+size_t albert_expand_workspace_bytes(int total) {
+  return total < 1 ? 0 : expand_plan(total).total;
+}
+
+int albert_expand(const float* feat, const int32_t* dur, const int32_t* cu_tok, int n, int total,
+                  int C, float* out, int64_t max_frames, int32_t* cu_frames, void* ws,
+                  size_t ws_bytes, void* stream, unsigned flags) {
+  if (!feat || !dur || !cu_tok || !out || !cu_frames || !ws || n < 1 || total < 1 || C < 4 ||
+      C % 4 != 0 || max_frames < 1 || max_frames > INT32_MAX || ((uintptr_t)ws % kAlign) != 0)
+    return ALBERT_E_ARG;
+  const ExpandLayout L = expand_plan(total);
+  if (ws_bytes < L.total) return ALBERT_E_WORKSPACE;
+  const size_t out_b = (size_t)max_frames * C * 4, cuf_b = (size_t)(n + 1) * 4;
+  const size_t feat_b = (size_t)total * C * 4, dur_b = (size_t)total * 4;
+  if (overlaps(out, out_b, feat, feat_b) || overlaps(out, out_b, dur, dur_b) ||
+      overlaps(out, out_b, cu_tok, cuf_b) || overlaps(out, out_b, ws, L.total) ||
+      overlaps(out, out_b, cu_frames, cuf_b) || overlaps(cu_frames, cuf_b, feat, feat_b) ||
+      overlaps(cu_frames, cuf_b, dur, dur_b) || overlaps(cu_frames, cuf_b, cu_tok, cuf_b) ||
+      overlaps(cu_frames, cuf_b, ws, L.total))
+    return ALBERT_E_ALIAS;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* w = static_cast<char*>(ws);
+  int* status = reinterpret_cast<int*>(w + L.status);
+  int64_t* excl = reinterpret_cast<int64_t*>(w + L.excl);
+  int64_t* bsum = reinterpret_cast<int64_t*>(w + L.block_sum);
+  hipLaunchKernelGGL(set_status_kernel, dim3(1), dim3(1), 0, s, status);
+  hipLaunchKernelGGL(dur_scan_local_kernel, dim3(L.nblocks), dim3(1024), 0, s, dur, total, excl,
+                     bsum, status);
+  hipLaunchKernelGGL(dur_scan_blocks_kernel, dim3(1), dim3(1024), 0, s, bsum, L.nblocks, excl,
+                     cu_tok, n, total, max_frames, cu_frames, status);
+  hipLaunchKernelGGL(expand_kernel, dim3((unsigned)((total + 3) / 4)), dim3(256), 0, s, feat, dur,
+                     excl, bsum, total, C, out, status);
+  const int rc = hipGetLastError() == hipSuccess ? ALBERT_OK : ALBERT_E_HIP;
+  return finish(rc, ws, s, flags);
 }
 
 void albert_free(albert_ctx* ctx) {

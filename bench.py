@@ -118,6 +118,41 @@ def cpu_baseline(wl, got, budget_s: float):
     return base, parity
 
 
+def measure_length_regulation(steps: int = 20) -> dict:
+    """Duration rule + frame expansion on the packed-workload shape (63k
+    tokens x 512 fp32, durations from 8 synthetic logit channels).  HBM
+    bound: bytes = token rows read once + frame rows written."""
+    import torch
+    import albert_transformer_amd as A
+    wl = synth.make_workload(5)
+    rng = np.random.default_rng(55)
+    feat = torch.from_numpy(rng.normal(0, 0.5, (wl.tokens, O)).astype(np.float32)).cuda()
+    logits = torch.from_numpy(rng.normal(0.4, 1.0, (wl.tokens, 8)).astype(np.float32)).cuda()
+    cu = torch.from_numpy(wl.cu_seqlens).cuda()
+    dur = A.durations(logits, 1.0)
+    frames = int(dur.sum().item())
+    out = torch.empty((frames, O), dtype=torch.float32, device="cuda")
+    cuf = torch.empty(wl.n_seq + 1, dtype=torch.int32, device="cuda")
+    ws = torch.empty(A.expand_workspace_bytes(wl.tokens), dtype=torch.uint8, device="cuda")
+    assert A.expand_raw(feat, dur, cu, frames, out, cuf, ws) == A.OK
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(steps):
+        A.expand_raw(feat, dur, cu, frames, out, cuf, ws, flags=A.ASYNC)
+    e1.record()
+    torch.cuda.synchronize()
+    assert A.read_status(ws) == A.OK
+    ms = e0.elapsed_time(e1) / steps
+    nbytes = wl.tokens * O * 4 + frames * O * 4 + wl.tokens * 4 * 3
+    return {"workload": f"{wl.n_seq} packed sequences, {wl.tokens} tokens x {O} fp32 -> "
+                        f"{frames} frames", "ms_per_call": round(ms, 4),
+            "frames_per_s": round(frames / (ms * 1e-3), 1),
+            "roofline": {"bound": "hbm", "achieved": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                         "peak": 8000.0, "unit": "GB/s",
+                         "frac": round(nbytes / (ms * 1e-3) / 1e9 / 8000.0, 4)}}
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -211,6 +246,7 @@ def main(argv=None) -> int:
     got = out.cpu().numpy()
     base, parity = (cpu_baseline(wl, got, args.cpu_seconds) if args.cpu_seconds > 0
                     else (None, None))
+    length_reg = measure_length_regulation() if args.config == 3 else None
 
     line = {
         "metric": METRIC,
@@ -250,6 +286,7 @@ def main(argv=None) -> int:
         "kernels_ms_per_step": {k: round(v["ms_per_step"], 4) for k, v in per_kind.items()},
         "cpu_baseline": base,
         "parity_sample": parity,
+        "length_regulation": length_reg,
         "source_sha": source_hash(),
     }
     print(json.dumps(line), flush=True)

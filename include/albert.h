@@ -201,6 +201,41 @@ int albert_time_kernel(albert_ctx* ctx, int kind, int max_launches);
  * since albert_time_kernel() and their summed duration in milliseconds. */
 int albert_kernel_time(albert_ctx* ctx, int* launches, double* total_ms);
 
+/* ---- Length regulation (the step after the encoder) -----------------------
+ * Kokoro expands token-level features to audio-aligned frames by integer
+ * durations ("How Kokoro TTS Works and Where CKE Stands", section "The time
+ * axis is where a circuit becomes difficult"; the [p1,p2,p3], d=[2,1,3] ->
+ * [p1,p1,p2,p3,p3,p3] example of "Qwen3-TTS and Kokoro: Two Routes from Text
+ * to Speech", section "Path one").  These calls need no context. */
+
+/* Durations from duration logits: dur[t] = max(1, rint(sum_k sigmoid(
+ * logits[t,k]) / speed)), fp32 arithmetic, rounding half to even.
+ * logits dev fp32 [total, K]; dur dev int32 [total] (written).
+ * total >= 1, K >= 1, speed finite and > 0.  Returns after enqueueing. */
+int albert_durations(const float* logits, int total, int K, float speed, int32_t* dur,
+                     void* hip_stream);
+
+/* Workspace bytes for albert_expand over `total` tokens (0 if total < 1). */
+size_t albert_expand_workspace_bytes(int total);
+
+/* Expand packed token features to frames.
+ * feat      dev fp32 [total, C], C a multiple of 4.
+ * dur       dev int32 [total], every value >= 1.
+ * cu_tok    dev int32 [n + 1] token offsets of the n sequences (cu[0] = 0,
+ *           cu[n] = total, every sequence non-empty).
+ * out       dev fp32 [max_frames, C]: row cu_frames[s] + r holds the feature
+ *           row of the token whose frames cover it, tokens in order; rows
+ *           past the frame count A = sum dur are not written.
+ * cu_frames dev int32 [n + 1] (written): first frame of each sequence, with
+ *           cu_frames[n] = A.
+ * ws        workspace of albert_expand_workspace_bytes(total) bytes,
+ *           256-byte aligned.
+ * Durations < 1, bad offsets or A > max_frames give ALBERT_E_LENGTH with
+ * `out` and `cu_frames` unchanged.  Flags and status as albert_encode. */
+int albert_expand(const float* feat, const int32_t* dur, const int32_t* cu_tok, int n,
+                  int total, int C, float* out, int64_t max_frames, int32_t* cu_frames,
+                  void* ws, size_t ws_bytes, void* hip_stream, unsigned flags);
+
 /* Release the context's device memory.  NULL is accepted. */
 void albert_free(albert_ctx* ctx);
 
