@@ -151,9 +151,14 @@ void gemm_big(GemmArgs g, int64_t max_rows, int grid_cap, hipStream_t s) {
   else
     launch_gemm<T, 256, 256, 2, 2, 128, 2, EPI, false>(g, max_rows, grid_cap, s);
 }
+// 128-row tiles need at least a full wave of them; smaller batches use
+// 64-row tiles (4 waves, one per SIMD) to spread over more CUs.
 template <typename T>
 void gemm_ln(GemmArgs g, int64_t max_rows, int grid_cap, hipStream_t s) {
-  launch_gemm<T, 128, 768, 2, 4, 64, 2, EPI_LN, false>(g, max_rows, grid_cap, s);
+  if ((max_rows + 127) / 128 >= grid_cap)
+    launch_gemm<T, 128, 768, 2, 4, 64, 2, EPI_LN, false>(g, max_rows, grid_cap, s);
+  else
+    launch_gemm<T, 64, 768, 1, 4, 64, 2, EPI_LN, false>(g, max_rows, grid_cap, s);
 }
 
 // Launch `fn` on stream s, bracketed by timing events when `kind` is the
