@@ -10,5 +10,6 @@ from .albert_oracle import (  # noqa: F401
     bf16_round, prepare_weights, validate, layer_norm, gelu_tanh, softmax,
     dense, attention, shared_layer, embed_ln, encode_sequence, encode,
     encode_varlen, expand_durations, duration_from_logits, param_counts,
+    group_schedule, layer_set,
     OracleError,
 )

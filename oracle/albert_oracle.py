@@ -77,7 +77,9 @@ def prepare_weights(w: dict, dtype: str) -> dict:
     out = {}
     for name, t in w.items():
         t32 = np.asarray(t, dtype=np.float32)
-        if dtype == "bf16" and name in _MATRIX_NAMES:
+        head, _, rest = name.partition(".")
+        role = rest if head[:1] == "g" and head[1:].isdigit() else name
+        if dtype == "bf16" and role in _MATRIX_NAMES:
             out[name] = bf16_round(t32)
         else:
             out[name] = t32.astype(np.float64)
@@ -217,16 +219,41 @@ def shared_layer(h, W: dict, cfg, taps: dict | None = None) -> np.ndarray:
     return out
 
 
+def group_schedule(n_iter: int, n_groups: int) -> list:
+    """Which weight set each of the n_iter layer executions uses.
+
+    [ALBERT] "What ALBERT Changed", part 2: besides full sharing, ALBERT can
+    keep several distinct weight sets, each reused over a block of layers.
+    Reading: the blocks are contiguous and as equal as integers allow,
+    execution i (from 0) using set floor(i * G / n_iter); G = 1 is full
+    sharing and G = n_iter gives every execution its own set.
+    """
+    if n_groups < 1 or (n_iter > 0 and n_groups > n_iter):
+        raise OracleError("E_ARG", f"{n_groups} weight sets for {n_iter} executions")
+    return [i * n_groups // n_iter for i in range(n_iter)]
+
+
+def layer_set(W: dict, cfg, g: int) -> dict:
+    """The layer tensors of weight set g under their plain names."""
+    if getattr(cfg, "n_groups", 1) == 1:
+        return W
+    pre = f"g{g}."
+    return {k[len(pre):]: v for k, v in W.items() if k.startswith(pre)}
+
+
 def encode_sequence(ids_seq, W: dict, cfg, n_iter: int | None = None,
                     taps: dict | None = None) -> np.ndarray:
     """Encode one sequence of valid IDs: returns [L, out_dim].
 
     [ALBERT] "Inside One Real ALBERT Layer" and "What ALBERT Changed", part 2:
     embedding + LayerNorm, the E->H projection, then `n_iter` executions of
-    one shared layer, each on the previous execution's output and all with
-    the same weights, then the H->512 projection.
+    the shared layer, each on the previous execution's output (all with the
+    same weights, or with the weight set ``group_schedule`` assigns), then
+    the H->512 projection.
     """
     n_iter = cfg.n_iter if n_iter is None else n_iter
+    sched = group_schedule(n_iter, getattr(cfg, "n_groups", 1))
+    sets = [layer_set(W, cfg, g) for g in range(getattr(cfg, "n_groups", 1))]
     e = embed_ln(ids_seq, W, cfg)
     h = dense(e, W["proj.w"], W["proj.b"])
     if taps is not None:
@@ -234,7 +261,7 @@ def encode_sequence(ids_seq, W: dict, cfg, n_iter: int | None = None,
         taps["x0"] = h
     for it in range(n_iter):
         layer_taps = {} if taps is not None else None
-        h = shared_layer(h, W, cfg, layer_taps)
+        h = shared_layer(h, sets[sched[it]], cfg, layer_taps)
         if taps is not None:
             taps[f"iter{it}"] = dict(layer_taps, out=h)
     return dense(h, W["out.w"], W["out.b"])

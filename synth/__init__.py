@@ -30,6 +30,8 @@ TENSOR_NAMES = (
     "ffn_ln.g", "ffn_ln.b",
     "out.w", "out.b",
 )
+# The tensors of one transformer layer (indices 7..22 above).
+LAYER_NAMES = TENSOR_NAMES[7:23]
 
 
 @dataclass(frozen=True)
@@ -45,6 +47,7 @@ class Config:
     n_iter: int = 12
     out_dim: int = 512
     ln_eps: float = 1e-12
+    n_groups: int = 1           # distinct layer weight sets (Kokoro: one)
 
     def shapes(self) -> dict:
         E, H, F, O = self.emb, self.hidden, self.ffn, self.out_dim
@@ -63,13 +66,35 @@ class Config:
 
 KOKORO = Config()
 
+
+def tensor_names(cfg: Config = KOKORO) -> tuple:
+    """Canonical tensor order for cfg.n_groups layer weight sets.
+
+    One set: TENSOR_NAMES.  G > 1 sets: the seven embedding/projection
+    tensors, then the 16 layer tensors of set 0, 1, ..., G-1 named
+    "g<set>.<name>", then the output projection.
+    """
+    if cfg.n_groups == 1:
+        return TENSOR_NAMES
+    names = list(TENSOR_NAMES[:7])
+    for g in range(cfg.n_groups):
+        names += [f"g{g}.{n}" for n in LAYER_NAMES]
+    return tuple(names + list(TENSOR_NAMES[23:]))
+
+
+def base_name(name: str) -> str:
+    """Strip a "g<set>." prefix: the tensor's role in the layer."""
+    head, _, rest = name.partition(".")
+    return rest if head[:1] == "g" and head[1:].isdigit() else name
+
 # A tiny configuration for brute-force cross checks.
 TINY = Config(vocab=11, max_pos=6, n_types=2, emb=4, hidden=8, heads=2,
               head_dim=4, ffn=16, n_iter=3, out_dim=4)
 
 
 def make_weights(cfg: Config = KOKORO, seed: int = WEIGHT_SEED) -> dict:
-    """Draw every tensor in canonical order from one generator.
+    """Draw every tensor in canonical order (``tensor_names``) from one
+    generator.
 
     Matrices, tables and biases ~ N(0, 0.02); LayerNorm gains 1 + N(0, 0.01)
     and shifts N(0, 0.01).  Drawn in float64, returned as float32.
@@ -77,8 +102,8 @@ def make_weights(cfg: Config = KOKORO, seed: int = WEIGHT_SEED) -> dict:
     rng = np.random.default_rng(seed)
     shapes = cfg.shapes()
     out = {}
-    for name in TENSOR_NAMES:
-        shp = shapes[name]
+    for name in tensor_names(cfg):
+        shp = shapes[base_name(name)]
         if name.endswith(".g"):
             a = 1.0 + rng.normal(0.0, 0.01, size=shp)
         elif name.endswith("ln.b"):

@@ -190,11 +190,23 @@ def test_layer_matches_torch_post_norm_encoder_layer():
     assert np.max(np.abs(got - ref)) < 1e-11
 
 
-def _hf_albert(W, n_iter=12):
+_HF_LAYER = (("attention.query.weight", "q.w"), ("attention.query.bias", "q.b"),
+             ("attention.key.weight", "k.w"), ("attention.key.bias", "k.b"),
+             ("attention.value.weight", "v.w"), ("attention.value.bias", "v.b"),
+             ("attention.dense.weight", "o.w"), ("attention.dense.bias", "o.b"),
+             ("attention.LayerNorm.weight", "attn_ln.g"),
+             ("attention.LayerNorm.bias", "attn_ln.b"),
+             ("ffn.weight", "ffn1.w"), ("ffn.bias", "ffn1.b"),
+             ("ffn_output.weight", "ffn2.w"), ("ffn_output.bias", "ffn2.b"),
+             ("full_layer_layer_norm.weight", "ffn_ln.g"),
+             ("full_layer_layer_norm.bias", "ffn_ln.b"))
+
+
+def _hf_albert(W, n_iter=12, n_groups=1):
     transformers = pytest.importorskip("transformers")
     cfg = transformers.AlbertConfig(
         vocab_size=178, embedding_size=128, hidden_size=768, num_hidden_layers=n_iter,
-        num_hidden_groups=1, num_attention_heads=12, intermediate_size=2048,
+        num_hidden_groups=n_groups, num_attention_heads=12, intermediate_size=2048,
         inner_group_num=1, hidden_act="gelu_new", hidden_dropout_prob=0.0,
         attention_probs_dropout_prob=0.0, max_position_embeddings=512,
         type_vocab_size=2, layer_norm_eps=1e-12)
@@ -209,17 +221,10 @@ def _hf_albert(W, n_iter=12):
         "encoder.embedding_hidden_mapping_in.weight": "proj.w",
         "encoder.embedding_hidden_mapping_in.bias": "proj.b",
     }
-    pre = "encoder.albert_layer_groups.0.albert_layers.0."
-    sd.update({pre + "attention.query.weight": "q.w", pre + "attention.query.bias": "q.b",
-               pre + "attention.key.weight": "k.w", pre + "attention.key.bias": "k.b",
-               pre + "attention.value.weight": "v.w", pre + "attention.value.bias": "v.b",
-               pre + "attention.dense.weight": "o.w", pre + "attention.dense.bias": "o.b",
-               pre + "attention.LayerNorm.weight": "attn_ln.g",
-               pre + "attention.LayerNorm.bias": "attn_ln.b",
-               pre + "ffn.weight": "ffn1.w", pre + "ffn.bias": "ffn1.b",
-               pre + "ffn_output.weight": "ffn2.w", pre + "ffn_output.bias": "ffn2.b",
-               pre + "full_layer_layer_norm.weight": "ffn_ln.g",
-               pre + "full_layer_layer_norm.bias": "ffn_ln.b"})
+    for g in range(n_groups):
+        pre = f"encoder.albert_layer_groups.{g}.albert_layers.0."
+        ours = "" if n_groups == 1 else f"g{g}."
+        sd.update({pre + hf: ours + name for hf, name in _HF_LAYER})
     params = dict(m.named_parameters())
     assert set(params) == set(sd)
     with torch.no_grad():
@@ -246,6 +251,85 @@ def test_encoder_matches_hf_albert_shared_group(dtype):
         L = int(wl.lengths[b])
         assert np.max(np.abs(got[b, :L] - ref[b, :L])) < 1e-11
         assert np.all(got[b, L:] == 0.0)
+
+
+@pytest.mark.parametrize("G,dtype", [(3, "f32"), (5, "bf16"), (12, "f32")])
+def test_grouped_encoder_matches_hf_albert_groups(G, dtype):
+    """ALBERT's intermediate grouping: the Hugging Face model with G hidden
+    groups (one layer each) over 12 hidden layers is the same function as
+    the oracle with G weight sets."""
+    cfg = synth.Config(n_groups=G)
+    W = _w64(cfg, dtype=dtype)
+    m = _hf_albert(W, n_groups=G)
+    wl = synth.random_padded(13, B=2, T=20, lo=6, hi=20)
+    ids = torch.from_numpy(wl.ids.astype(np.int64))
+    am = (torch.arange(wl.T)[None, :] < torch.from_numpy(wl.lengths)[:, None]).long()
+    with torch.no_grad():
+        hid = m(input_ids=ids, attention_mask=am, token_type_ids=torch.zeros_like(ids)).last_hidden_state
+    ref = hid.numpy() @ W["out.w"].T + W["out.b"]
+    got = oracle.encode(wl.ids, wl.lengths, W, cfg)
+    for b in range(2):
+        L = int(wl.lengths[b])
+        assert np.max(np.abs(got[b, :L] - ref[b, :L])) < 1e-11
+
+
+def test_group_schedule_blocks():
+    """Sets are used in contiguous, near-equal blocks, in order, each set at
+    least once; one set is full sharing and n_iter sets are distinct layers.
+    For depths up to 17 the schedule equals the Hugging Face model's
+    (which divides in floating point; beyond that its rounding can move a
+    block boundary by one execution)."""
+    for N in range(1, 25):
+        for G in range(1, N + 1):
+            s = oracle.group_schedule(N, G)
+            assert s[0] == 0 and s[-1] == G - 1
+            assert all(b - a in (0, 1) for a, b in zip(s, s[1:]))
+            counts = np.bincount(s, minlength=G)
+            assert counts.min() >= 1 and counts.max() - counts.min() <= 1
+            if N <= 17:
+                assert s == [int(i / (N / G)) for i in range(N)]
+    assert oracle.group_schedule(12, 1) == [0] * 12
+    assert oracle.group_schedule(12, 12) == list(range(12))
+    assert oracle.group_schedule(12, 3) == [0] * 4 + [1] * 4 + [2] * 4
+    assert oracle.group_schedule(0, 1) == []
+    for N, G in ((4, 5), (12, 0), (1, 2)):
+        with pytest.raises(oracle.OracleError):
+            oracle.group_schedule(N, G)
+
+
+def test_grouped_brute_force_and_identical_sets():
+    """Tiny shapes: the grouped oracle equals the loop brute force given the
+    per-execution layer list; G identical sets equal full sharing exactly."""
+    rng = np.random.default_rng(5)
+    for G, order in ((2, [0, 0, 1]), (3, [0, 1, 2])):
+        cfg = synth.Config(**{**synth.TINY.__dict__, "n_groups": G})
+        W = _w64(cfg, seed=31 + G)
+        sets = [oracle.layer_set(W, cfg, g) for g in range(G)]
+        layers = [{k: sets[g][k] for k in brute.LAYER_KEYS} for g in order]
+        for L in (1, 3, 4):
+            ids = rng.integers(0, cfg.vocab, L)
+            got = oracle.encode_sequence(ids, W, cfg)
+            ref = np.array(brute.encode_brute(ids, W, cfg, layers=layers))
+            assert np.max(np.abs(got - ref)) < 1e-12
+    cfg1 = synth.TINY
+    W1 = _w64(cfg1, seed=40)
+    cfg3 = synth.Config(**{**synth.TINY.__dict__, "n_groups": 3})
+    W3 = {n: W1[synth.base_name(n)] for n in synth.tensor_names(cfg3)}
+    ids = np.array([1, 2, 3, 4])
+    assert np.array_equal(oracle.encode_sequence(ids, W3, cfg3),
+                          oracle.encode_sequence(ids, W1, cfg1))
+
+
+def test_one_set_draws_are_unchanged_by_grouping():
+    """G = 1 keeps the canonical names and draws; with G sets, set 0 is
+    drawn first, right after the projection, so it equals the G = 1 layer."""
+    w1 = synth.make_weights(synth.TINY, seed=3)
+    assert tuple(w1) == synth.TENSOR_NAMES
+    cfg2 = synth.Config(**{**synth.TINY.__dict__, "n_groups": 2})
+    w2 = synth.make_weights(cfg2, seed=3)
+    for n in synth.LAYER_NAMES:
+        assert np.array_equal(w2["g0." + n], w1[n])
+    assert not np.array_equal(w2["g1.q.w"], w1["q.w"])
 
 
 def test_brute_force_agrees_on_tiny_shapes():
