@@ -24,8 +24,8 @@ N_TENSORS = 25
 TAPS = {"status": 0, "cu": 1, "row_seq": 2, "row_pos": 3, "emb": 4, "x": 5,
         "qkv": 6, "ctx": 7, "x1": 8, "g": 9}
 
-EXPORTS = ("albert_default_config", "albert_tensor_name", "albert_tensor_shape",
-           "albert_load_weights", "albert_workspace_bytes", "albert_encode",
+EXPORTS = ("albert_default_config", "albert_n_tensors", "albert_tensor_name",
+           "albert_tensor_shape", "albert_load_weights", "albert_workspace_bytes", "albert_encode",
            "albert_encode_varlen", "albert_read_status", "albert_tap", "albert_free",
            "albert_status_str", "albert_time_kernel", "albert_kernel_time",
            "albert_durations", "albert_expand_workspace_bytes", "albert_expand")
@@ -37,8 +37,8 @@ class Config(ctypes.Structure):
                 ("n_types", ctypes.c_int32), ("emb", ctypes.c_int32),
                 ("hidden", ctypes.c_int32), ("heads", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("ffn", ctypes.c_int32),
-                ("n_iter", ctypes.c_int32), ("out_dim", ctypes.c_int32),
-                ("ln_eps", ctypes.c_float)]
+                ("n_iter", ctypes.c_int32), ("n_groups", ctypes.c_int32),
+                ("out_dim", ctypes.c_int32), ("ln_eps", ctypes.c_float)]
 
 
 _LIB = None
@@ -56,7 +56,9 @@ def lib():
     vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
     L.albert_default_config.argtypes = [ctypes.POINTER(Config)]
     L.albert_default_config.restype = i32
-    L.albert_tensor_name.argtypes = [i32]
+    L.albert_n_tensors.argtypes = [ctypes.POINTER(Config)]
+    L.albert_n_tensors.restype = i32
+    L.albert_tensor_name.argtypes = [ctypes.POINTER(Config), i32]
     L.albert_tensor_name.restype = ctypes.c_char_p
     L.albert_tensor_shape.argtypes = [ctypes.POINTER(Config), i32,
                                       ctypes.POINTER(i64), ctypes.POINTER(i64)]
@@ -126,8 +128,9 @@ class Encoder:
     """One device-resident copy of the encoder weights (an albert_ctx).
 
     weights: dict of canonical name -> float32 numpy array (see
-    ``synth.TENSOR_NAMES``); dtype "bf16" or "f32"; config overrides as
-    keyword arguments (e.g. n_iter=1).
+    ``synth.tensor_names``: with n_groups = G > 1 the layer tensors of set g
+    are named "g<g>.<name>"); dtype "bf16" or "f32"; config overrides as
+    keyword arguments (e.g. n_iter=1, n_groups=3).
     """
 
     def __init__(self, weights: dict, dtype: str = "bf16", stream=None, **cfg):
@@ -135,20 +138,29 @@ class Encoder:
         L = lib()
         self.cfg = default_config(**cfg)
         self.dtype = dtype
-        names = [L.albert_tensor_name(i).decode() for i in range(N_TENSORS)]
+        cf = ctypes.byref(self.cfg)
+        nt = L.albert_n_tensors(cf)
+        if nt < 0:
+            raise AlbertError(E_ARG, "albert_n_tensors")
+        names = []
+        for i in range(nt):
+            n = L.albert_tensor_name(cf, i).decode()
+            if self.cfg.n_groups > 1 and 7 <= i < 7 + 16 * self.cfg.n_groups:
+                n = f"g{(i - 7) // 16}.{n}"
+            names.append(n)
         self._host = []
         for i, n in enumerate(names):
             a = np.ascontiguousarray(np.asarray(weights[n], dtype=np.float32))
             r, c = ctypes.c_int64(), ctypes.c_int64()
-            rc = L.albert_tensor_shape(ctypes.byref(self.cfg), i, ctypes.byref(r), ctypes.byref(c))
+            rc = L.albert_tensor_shape(cf, i, ctypes.byref(r), ctypes.byref(c))
             if rc != OK:
                 raise AlbertError(rc, "albert_tensor_shape")
             if a.size != r.value * c.value:
                 raise ValueError(f"{n}: expected {r.value}x{c.value}, got {a.shape}")
             self._host.append(a)
-        ptrs = (ctypes.c_void_p * N_TENSORS)(*[a.ctypes.data for a in self._host])
+        ptrs = (ctypes.c_void_p * nt)(*[a.ctypes.data for a in self._host])
         h = ctypes.c_void_p()
-        rc = L.albert_load_weights(ctypes.byref(h), ctypes.byref(self.cfg), ptrs,
+        rc = L.albert_load_weights(ctypes.byref(h), cf, ptrs,
                                    BF16 if dtype == "bf16" else F32, _stream(stream))
         self._host = None
         if rc != OK:

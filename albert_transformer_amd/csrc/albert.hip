@@ -8,7 +8,8 @@
 //   projection into `out` (+ zeroing of padded rows).
 // The same weight pointers serve every execution of the shared layer (page
 // "ALBERT: How Kokoro's Phoneme Encoder Works", "Cross-layer parameter
-// sharing"); only the activations change.
+// sharing"); only the activations change.  With intermediate grouping (G
+// weight sets) execution i takes set floor(i * G / n_iter).
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -27,6 +28,12 @@
 
 using namespace albert;
 
+// Device pointers of one layer weight set (matrices in dtype, vectors fp32).
+struct LayerW {
+  const void *qkv_w, *o_w, *ffn1_w, *ffn2_w;
+  const float *qkv_b, *o_b, *ln1_g, *ln1_b, *ffn1_b, *ffn2_b, *ln2_g, *ln2_b;
+};
+
 struct albert_ctx {
   albert_config cfg;
   int dtype;
@@ -34,9 +41,9 @@ struct albert_ctx {
   int grid_cap;  // persistent GEMM grid: CUs rounded down to a multiple of 8
   void* mem;
   // device pointers (tables/matrices in dtype, vectors fp32)
-  const void *word, *pos, *type, *proj_w, *qkv_w, *o_w, *ffn1_w, *ffn2_w, *out_w;
-  const float *emb_g, *emb_b, *proj_b, *qkv_b, *o_b, *ln1_g, *ln1_b, *ffn1_b, *ffn2_b,
-      *ln2_g, *ln2_b, *out_b;
+  const void *word, *pos, *type, *proj_w, *out_w;
+  const float *emb_g, *emb_b, *proj_b, *out_b;
+  std::vector<LayerW> layers;  // n_groups weight sets
   // optional kernel timing (albert_time_kernel)
   int time_kind = -1;
   int n_timed = 0;
@@ -53,10 +60,20 @@ const char* const kNames[ALBERT_N_TENSORS] = {
     "q.w", "q.b", "k.w", "k.b", "v.w", "v.b", "o.w", "o.b", "attn_ln.g", "attn_ln.b",
     "ffn1.w", "ffn1.b", "ffn2.w", "ffn2.b", "ffn_ln.g", "ffn_ln.b", "out.w", "out.b"};
 
+// Role (index into kNames) of tensor i under c's number of weight sets.
+int role_of(const albert_config& c, int i) {
+  const int G = c.n_groups;
+  if (i < 0) return -1;
+  if (i < 7) return i;
+  if (i < 7 + ALBERT_LAYER_TENSORS * G) return 7 + (i - 7) % ALBERT_LAYER_TENSORS;
+  if (i < 9 + ALBERT_LAYER_TENSORS * G) return 23 + (i - 7 - ALBERT_LAYER_TENSORS * G);
+  return -1;
+}
+
 bool shape_of(const albert_config& c, int i, int64_t* r, int64_t* k) {
   const int64_t E = c.emb, H = c.hidden, F = c.ffn, O = c.out_dim;
   int64_t rows = 0, cols = 1;
-  switch (i) {
+  switch (role_of(c, i)) {
     case 0: rows = c.vocab; cols = E; break;
     case 1: rows = c.max_pos; cols = E; break;
     case 2: rows = c.n_types; cols = E; break;
@@ -86,7 +103,8 @@ bool config_ok(const albert_config& c) {
   return c.emb == 128 && c.hidden == 768 && c.heads == 12 && c.head_dim == 64 &&
          c.vocab >= 1 && c.max_pos >= 1 && c.max_pos <= 512 && c.n_types >= 1 &&
          c.ffn >= 256 && c.ffn % 256 == 0 && c.out_dim >= 256 && c.out_dim % 256 == 0 &&
-         c.n_iter >= 0 && std::isfinite(c.ln_eps) && c.ln_eps > 0.f;
+         c.n_iter >= 0 && c.n_groups >= 1 && c.n_groups <= std::max(c.n_iter, 1) &&
+         std::isfinite(c.ln_eps) && c.ln_eps > 0.f;
 }
 
 uint16_t f32_to_bf16_bits(float f) {
@@ -220,8 +238,9 @@ int run(albert_ctx* c, const int32_t* ids, const int32_t* lens_or_cu, int n_seq,
 
   const int qtiles = (max_len + 127) / 128;
   for (int it = 0; it < cf.n_iter; ++it) {
+    const LayerW& lw = c->layers[(size_t)((int64_t)it * cf.n_groups / cf.n_iter)];
     g = base;  // fused Q|K|V projection
-    g.X = X; g.ldx = H; g.W = c->qkv_w; g.bias = c->qkv_b; g.Y = QKV; g.ldy = 3 * H;
+    g.X = X; g.ldx = H; g.W = lw.qkv_w; g.bias = lw.qkv_b; g.Y = QKV; g.ldy = 3 * H;
     g.N = 3 * H; g.K = H;
     timed(c, ALBERT_K_QKV, s, [&] { gemm_big<T, EPI_BIAS>(g, max_rows, c->grid_cap, s); });
 
@@ -231,18 +250,18 @@ int run(albert_ctx* c, const int32_t* ids, const int32_t* lens_or_cu, int n_seq,
     });
 
     g = base;  // output projection + residual + LayerNorm
-    g.X = CTX; g.ldx = H; g.W = c->o_w; g.bias = c->o_b; g.R = X; g.ldr = H;
-    g.ln_g = c->ln1_g; g.ln_b = c->ln1_b; g.Y = X1; g.ldy = H; g.N = H; g.K = H;
+    g.X = CTX; g.ldx = H; g.W = lw.o_w; g.bias = lw.o_b; g.R = X; g.ldr = H;
+    g.ln_g = lw.ln1_g; g.ln_b = lw.ln1_b; g.Y = X1; g.ldy = H; g.N = H; g.K = H;
     timed(c, ALBERT_K_ATTN_OUT_LN, s, [&] { gemm_ln<T>(g, max_rows, c->grid_cap, s); });
 
     g = base;  // FFN 768 -> 2048 + GELU
-    g.X = X1; g.ldx = H; g.W = c->ffn1_w; g.bias = c->ffn1_b; g.Y = G; g.ldy = F;
+    g.X = X1; g.ldx = H; g.W = lw.ffn1_w; g.bias = lw.ffn1_b; g.Y = G; g.ldy = F;
     g.N = F; g.K = H;
     timed(c, ALBERT_K_FFN1_GELU, s, [&] { gemm_big<T, EPI_GELU>(g, max_rows, c->grid_cap, s); });
 
     g = base;  // FFN 2048 -> 768 + residual + LayerNorm
-    g.X = G; g.ldx = F; g.W = c->ffn2_w; g.bias = c->ffn2_b; g.R = X1; g.ldr = H;
-    g.ln_g = c->ln2_g; g.ln_b = c->ln2_b; g.Y = X; g.ldy = H; g.N = H; g.K = F;
+    g.X = G; g.ldx = F; g.W = lw.ffn2_w; g.bias = lw.ffn2_b; g.R = X1; g.ldr = H;
+    g.ln_g = lw.ln2_g; g.ln_b = lw.ln2_b; g.Y = X; g.ldy = H; g.N = H; g.K = F;
     timed(c, ALBERT_K_FFN2_LN, s, [&] { gemm_ln<T>(g, max_rows, c->grid_cap, s); });
   }
 
@@ -272,12 +291,19 @@ extern "C" {
 
 int albert_default_config(albert_config* cfg) {
   if (!cfg) return ALBERT_E_ARG;
-  *cfg = albert_config{178, 512, 2, 128, 768, 12, 64, 2048, 12, 512, 1e-12f};
+  *cfg = albert_config{178, 512, 2, 128, 768, 12, 64, 2048, 12, 1, 512, 1e-12f};
   return ALBERT_OK;
 }
 
-const char* albert_tensor_name(int index) {
-  return (index >= 0 && index < ALBERT_N_TENSORS) ? kNames[index] : nullptr;
+int albert_n_tensors(const albert_config* cfg) {
+  if (!cfg || !config_ok(*cfg)) return -1;
+  return 9 + ALBERT_LAYER_TENSORS * cfg->n_groups;
+}
+
+const char* albert_tensor_name(const albert_config* cfg, int index) {
+  if (!cfg || !config_ok(*cfg)) return nullptr;
+  const int r = role_of(*cfg, index);
+  return r < 0 ? nullptr : kNames[r];
 }
 
 int albert_tensor_shape(const albert_config* cfg, int index, int64_t* rows, int64_t* cols) {
@@ -293,8 +319,9 @@ int albert_load_weights(albert_ctx** out_ctx, const albert_config* cfg,
     return ALBERT_E_ARG;
   const albert_config c = *cfg;
   const size_t es = dtype == ALBERT_BF16 ? 2 : 4;
-  int64_t rows[ALBERT_N_TENSORS], cols[ALBERT_N_TENSORS];
-  for (int i = 0; i < ALBERT_N_TENSORS; ++i) {
+  const int G = c.n_groups, NT = 9 + ALBERT_LAYER_TENSORS * G;
+  std::vector<int64_t> rows(NT), cols(NT);
+  for (int i = 0; i < NT; ++i) {
     if (!host[i]) return ALBERT_E_ARG;
     shape_of(c, i, &rows[i], &cols[i]);
     for (int64_t e = 0; e < rows[i] * cols[i]; ++e)
@@ -303,31 +330,38 @@ int albert_load_weights(albert_ctx** out_ctx, const albert_config* cfg,
   const int64_t H = c.hidden;
 
   // Device image: segments in the order below, each 256-byte aligned.
+  // Per weight set: Q|K|V packed into one [3H, H] matrix (queries scaled)
+  // and one [3H] bias, then o, attn LN, ffn1, ffn2, ffn LN.
+  enum { S_WORD, S_POS, S_TYPE, S_EMB_G, S_EMB_B, S_PROJ_W, S_PROJ_B, S_OUT_W, S_OUT_B, S_LAYER0 };
+  enum { L_QKV_W, L_QKV_B, L_O_W, L_O_B, L_LN1_G, L_LN1_B, L_F1_W, L_F1_B, L_F2_W, L_F2_B,
+         L_LN2_G, L_LN2_B, L_SEGS };
   struct Seg { size_t off, bytes; };
   std::vector<Seg> seg;
   size_t off = 0;
   auto add = [&](size_t bytes) { seg.push_back({off, bytes}); off += align_up(bytes, kAlign); };
-  add((size_t)c.vocab * c.emb * es);       // 0 word
-  add((size_t)c.max_pos * c.emb * es);     // 1 pos
-  add((size_t)c.n_types * c.emb * es);     // 2 type
-  add((size_t)c.emb * 4);                  // 3 emb g
-  add((size_t)c.emb * 4);                  // 4 emb b
-  add((size_t)H * c.emb * es);             // 5 proj w
-  add((size_t)H * 4);                      // 6 proj b
-  add((size_t)3 * H * H * es);             // 7 qkv w
-  add((size_t)3 * H * 4);                  // 8 qkv b
-  add((size_t)H * H * es);                 // 9 o w
-  add((size_t)H * 4);                      // 10 o b
-  add((size_t)H * 4);                      // 11 ln1 g
-  add((size_t)H * 4);                      // 12 ln1 b
-  add((size_t)c.ffn * H * es);             // 13 ffn1 w
-  add((size_t)c.ffn * 4);                  // 14 ffn1 b
-  add((size_t)H * c.ffn * es);             // 15 ffn2 w
-  add((size_t)H * 4);                      // 16 ffn2 b
-  add((size_t)H * 4);                      // 17 ln2 g
-  add((size_t)H * 4);                      // 18 ln2 b
-  add((size_t)c.out_dim * H * es);         // 19 out w
-  add((size_t)c.out_dim * 4);              // 20 out b
+  add((size_t)c.vocab * c.emb * es);       // word
+  add((size_t)c.max_pos * c.emb * es);     // pos
+  add((size_t)c.n_types * c.emb * es);     // type
+  add((size_t)c.emb * 4);                  // emb g
+  add((size_t)c.emb * 4);                  // emb b
+  add((size_t)H * c.emb * es);             // proj w
+  add((size_t)H * 4);                      // proj b
+  add((size_t)c.out_dim * H * es);         // out w
+  add((size_t)c.out_dim * 4);              // out b
+  for (int g = 0; g < G; ++g) {
+    add((size_t)3 * H * H * es);           // qkv w
+    add((size_t)3 * H * 4);                // qkv b
+    add((size_t)H * H * es);               // o w
+    add((size_t)H * 4);                    // o b
+    add((size_t)H * 4);                    // ln1 g
+    add((size_t)H * 4);                    // ln1 b
+    add((size_t)c.ffn * H * es);           // ffn1 w
+    add((size_t)c.ffn * 4);                // ffn1 b
+    add((size_t)H * c.ffn * es);           // ffn2 w
+    add((size_t)H * 4);                    // ffn2 b
+    add((size_t)H * 4);                    // ln2 g
+    add((size_t)H * 4);                    // ln2 b
+  }
   std::vector<unsigned char> img(off, 0);
 
   auto put_mat = [&](int s, const float* src, int64_t n, float scale, size_t elem_off) {
@@ -347,31 +381,36 @@ int albert_load_weights(albert_ctx** out_ctx, const albert_config* cfg,
     for (int64_t e = 0; e < n; ++e) d[e] = src[e] * scale;
   };
   const float qscale = 1.0f / std::sqrt((float)c.head_dim);  // 1/8 for head_dim 64
-  put_mat(0, host[0], rows[0] * cols[0], 1.f, 0);
-  put_mat(1, host[1], rows[1] * cols[1], 1.f, 0);
-  put_mat(2, host[2], rows[2] * cols[2], 1.f, 0);
-  put_vec(3, host[3], c.emb, 1.f, 0);
-  put_vec(4, host[4], c.emb, 1.f, 0);
-  put_mat(5, host[5], H * c.emb, 1.f, 0);
-  put_vec(6, host[6], H, 1.f, 0);
-  put_mat(7, host[7], H * H, qscale, 0);
-  put_mat(7, host[9], H * H, 1.f, (size_t)(H * H));
-  put_mat(7, host[11], H * H, 1.f, (size_t)(2 * H * H));
-  put_vec(8, host[8], H, qscale, 0);
-  put_vec(8, host[10], H, 1.f, (size_t)H);
-  put_vec(8, host[12], H, 1.f, (size_t)(2 * H));
-  put_mat(9, host[13], H * H, 1.f, 0);
-  put_vec(10, host[14], H, 1.f, 0);
-  put_vec(11, host[15], H, 1.f, 0);
-  put_vec(12, host[16], H, 1.f, 0);
-  put_mat(13, host[17], (int64_t)c.ffn * H, 1.f, 0);
-  put_vec(14, host[18], c.ffn, 1.f, 0);
-  put_mat(15, host[19], H * c.ffn, 1.f, 0);
-  put_vec(16, host[20], H, 1.f, 0);
-  put_vec(17, host[21], H, 1.f, 0);
-  put_vec(18, host[22], H, 1.f, 0);
-  put_mat(19, host[23], (int64_t)c.out_dim * H, 1.f, 0);
-  put_vec(20, host[24], c.out_dim, 1.f, 0);
+  put_mat(S_WORD, host[0], rows[0] * cols[0], 1.f, 0);
+  put_mat(S_POS, host[1], rows[1] * cols[1], 1.f, 0);
+  put_mat(S_TYPE, host[2], rows[2] * cols[2], 1.f, 0);
+  put_vec(S_EMB_G, host[3], c.emb, 1.f, 0);
+  put_vec(S_EMB_B, host[4], c.emb, 1.f, 0);
+  put_mat(S_PROJ_W, host[5], H * c.emb, 1.f, 0);
+  put_vec(S_PROJ_B, host[6], H, 1.f, 0);
+  const int out_i = 7 + ALBERT_LAYER_TENSORS * G;
+  put_mat(S_OUT_W, host[out_i], (int64_t)c.out_dim * H, 1.f, 0);
+  put_vec(S_OUT_B, host[out_i + 1], c.out_dim, 1.f, 0);
+  for (int g = 0; g < G; ++g) {
+    const float* const* t = host + 7 + ALBERT_LAYER_TENSORS * g;  // q.w .. ffn_ln.b
+    const int s0 = S_LAYER0 + L_SEGS * g;
+    put_mat(s0 + L_QKV_W, t[0], H * H, qscale, 0);
+    put_mat(s0 + L_QKV_W, t[2], H * H, 1.f, (size_t)(H * H));
+    put_mat(s0 + L_QKV_W, t[4], H * H, 1.f, (size_t)(2 * H * H));
+    put_vec(s0 + L_QKV_B, t[1], H, qscale, 0);
+    put_vec(s0 + L_QKV_B, t[3], H, 1.f, (size_t)H);
+    put_vec(s0 + L_QKV_B, t[5], H, 1.f, (size_t)(2 * H));
+    put_mat(s0 + L_O_W, t[6], H * H, 1.f, 0);
+    put_vec(s0 + L_O_B, t[7], H, 1.f, 0);
+    put_vec(s0 + L_LN1_G, t[8], H, 1.f, 0);
+    put_vec(s0 + L_LN1_B, t[9], H, 1.f, 0);
+    put_mat(s0 + L_F1_W, t[10], (int64_t)c.ffn * H, 1.f, 0);
+    put_vec(s0 + L_F1_B, t[11], c.ffn, 1.f, 0);
+    put_mat(s0 + L_F2_W, t[12], H * c.ffn, 1.f, 0);
+    put_vec(s0 + L_F2_B, t[13], H, 1.f, 0);
+    put_vec(s0 + L_LN2_G, t[14], H, 1.f, 0);
+    put_vec(s0 + L_LN2_B, t[15], H, 1.f, 0);
+  }
 
   albert_ctx* ctx = new (std::nothrow) albert_ctx();
   if (!ctx) return ALBERT_E_ARG;
@@ -396,14 +435,21 @@ int albert_load_weights(albert_ctx** out_ctx, const albert_config* cfg,
   char* m = static_cast<char*>(ctx->mem);
   auto P = [&](int sidx) { return (const void*)(m + seg[sidx].off); };
   auto Pf = [&](int sidx) { return (const float*)(m + seg[sidx].off); };
-  ctx->word = P(0); ctx->pos = P(1); ctx->type = P(2);
-  ctx->emb_g = Pf(3); ctx->emb_b = Pf(4);
-  ctx->proj_w = P(5); ctx->proj_b = Pf(6);
-  ctx->qkv_w = P(7); ctx->qkv_b = Pf(8);
-  ctx->o_w = P(9); ctx->o_b = Pf(10); ctx->ln1_g = Pf(11); ctx->ln1_b = Pf(12);
-  ctx->ffn1_w = P(13); ctx->ffn1_b = Pf(14); ctx->ffn2_w = P(15); ctx->ffn2_b = Pf(16);
-  ctx->ln2_g = Pf(17); ctx->ln2_b = Pf(18);
-  ctx->out_w = P(19); ctx->out_b = Pf(20);
+  ctx->word = P(S_WORD); ctx->pos = P(S_POS); ctx->type = P(S_TYPE);
+  ctx->emb_g = Pf(S_EMB_G); ctx->emb_b = Pf(S_EMB_B);
+  ctx->proj_w = P(S_PROJ_W); ctx->proj_b = Pf(S_PROJ_B);
+  ctx->out_w = P(S_OUT_W); ctx->out_b = Pf(S_OUT_B);
+  ctx->layers.resize(G);
+  for (int g = 0; g < G; ++g) {
+    const int s0 = S_LAYER0 + L_SEGS * g;
+    LayerW& lw = ctx->layers[g];
+    lw.qkv_w = P(s0 + L_QKV_W); lw.qkv_b = Pf(s0 + L_QKV_B);
+    lw.o_w = P(s0 + L_O_W); lw.o_b = Pf(s0 + L_O_B);
+    lw.ln1_g = Pf(s0 + L_LN1_G); lw.ln1_b = Pf(s0 + L_LN1_B);
+    lw.ffn1_w = P(s0 + L_F1_W); lw.ffn1_b = Pf(s0 + L_F1_B);
+    lw.ffn2_w = P(s0 + L_F2_W); lw.ffn2_b = Pf(s0 + L_F2_B);
+    lw.ln2_g = Pf(s0 + L_LN2_G); lw.ln2_b = Pf(s0 + L_LN2_B);
+  }
   *out_ctx = ctx;
   return ALBERT_OK;
 }

@@ -9,6 +9,8 @@
  *   LayerNormed -> 128->768 projection -> n_iter executions of ONE shared
  *   post-LayerNorm transformer layer (12 heads of 64, bidirectional masked
  *   attention, 768->2048->768 tanh-GELU FFN) -> 768->512 projection.
+ * ALBERT's intermediate grouping (several layer weight sets, each reused
+ * over a block of executions) is the n_groups option of albert_config.
  *
  * Every call takes plain pointers and sizes.  Unless stated otherwise:
  *   - "dev" pointers are device memory on the current HIP device,
@@ -60,13 +62,19 @@ typedef struct albert_config {
   int32_t head_dim; /* per-head width (must be 64)                         */
   int32_t ffn;      /* FFN width (Kokoro: 2048; multiple of 256)           */
   int32_t n_iter;   /* executions of the shared layer (Kokoro: 12; >= 0)   */
+  int32_t n_groups; /* distinct layer weight sets G (Kokoro: 1, i.e. full
+                       sharing); 1 <= G <= max(n_iter, 1).  Execution i
+                       (from 0) uses set floor(i * G / n_iter): contiguous,
+                       near-equal blocks of executions per set ("What ALBERT
+                       Changed", part 2: intermediate grouping)             */
   int32_t out_dim;  /* output width (Kokoro: 512; multiple of 256)         */
   float ln_eps;     /* LayerNorm epsilon (Kokoro: 1e-12)                   */
 } albert_config;
 
-/* Number of weight tensors and their canonical order (index: name [shape]).
- * Linear weights are [out, in] row-major, y_j = b_j + sum_i x_i W[j][i]
- * (contract A of "Qwen3-TTS and Kokoro: Two Routes from Text to Speech").
+/* Weight tensors and their canonical order (index: name [shape]) for one
+ * layer weight set (n_groups = 1).  Linear weights are [out, in] row-major,
+ * y_j = b_j + sum_i x_i W[j][i] (contract A of "Qwen3-TTS and Kokoro: Two
+ * Routes from Text to Speech").
  *   0 emb.word [vocab,E]    1 emb.pos [max_pos,E]   2 emb.type [n_types,E]
  *   3 emb.ln.g [E]          4 emb.ln.b [E]
  *   5 proj.w [H,E]          6 proj.b [H]
@@ -76,26 +84,39 @@ typedef struct albert_config {
  *  21 ffn_ln.g [H] 22 ffn_ln.b [H]
  *  23 out.w [O,H] 24 out.b [O]                                            */
 #define ALBERT_N_TENSORS 25
+/* With G = n_groups sets, indices 7..22 repeat once per set: tensor 7+16g+j
+ * is tensor 7+j of set g (0 <= j < 16), and out.w, out.b move to 7+16G and
+ * 8+16G, for albert_n_tensors(cfg) = 9 + 16G tensors in all. */
+#define ALBERT_LAYER_TENSORS 16
 
 typedef struct albert_ctx albert_ctx; /* opaque; owns the device weights */
 
 /* Fill *cfg with the Kokoro configuration. */
 int albert_default_config(albert_config* cfg);
 
-/* Canonical name of tensor `index` (NULL if out of range). */
-const char* albert_tensor_name(int index);
+/* Number of weight tensors under cfg (9 + 16 * n_groups), or -1 for a bad
+ * config. */
+int albert_n_tensors(const albert_config* cfg);
+
+/* Canonical name of tensor `index` under cfg, NULL for a bad index or
+ * config.  A layer tensor's name is its role ("q.w", ...); its weight set
+ * is (index - 7) / 16. */
+const char* albert_tensor_name(const albert_config* cfg, int index);
 
 /* Shape of tensor `index` under cfg: writes rows/cols (cols = 1 for
  * vectors).  Returns ALBERT_E_ARG for a bad index or config. */
 int albert_tensor_shape(const albert_config* cfg, int index, int64_t* rows, int64_t* cols);
 
 /* Create a context holding ONE copy of the encoder weights on the current
- * device -- one weight set serves all n_iter executions of the shared layer
- * (page "ALBERT: How Kokoro's Phoneme Encoder Works", "Cross-layer parameter
- * sharing", and the canonical-name weight binding of "How CKE Represents It").
+ * device -- one layer weight set serves all n_iter executions of the shared
+ * layer (page "ALBERT: How Kokoro's Phoneme Encoder Works", "Cross-layer
+ * parameter sharing", and the canonical-name weight binding of "How CKE
+ * Represents It"); with n_groups = G each of the G sets serves its block of
+ * executions.
  *
- * host_tensors: ALBERT_N_TENSORS host pointers to fp32 arrays in canonical
- *   order and shape.  They are read during the call and may be freed after.
+ * host_tensors: albert_n_tensors(cfg) host pointers to fp32 arrays in
+ *   canonical order and shape.  They are read during the call and may be
+ *   freed after.
  * dtype: ALBERT_BF16 stores tables and weight matrices as bfloat16 (round to
  *   nearest even); ALBERT_F32 stores them as given.  Biases and LayerNorm
  *   vectors are fp32 in both.  The query weights and bias are stored scaled

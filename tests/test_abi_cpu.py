@@ -44,27 +44,51 @@ def test_default_config_and_tensor_table(L):
     c = A.default_config()
     k = synth.KOKORO
     for f in ("vocab", "max_pos", "n_types", "emb", "hidden", "heads", "head_dim",
-              "ffn", "n_iter", "out_dim"):
+              "ffn", "n_iter", "n_groups", "out_dim"):
         assert getattr(c, f) == getattr(k, f), f
     assert abs(c.ln_eps - 1e-12) < 1e-18
+    assert L.albert_n_tensors(ctypes.byref(c)) == len(synth.TENSOR_NAMES) == 25
     shapes = k.shapes()
     for i, name in enumerate(synth.TENSOR_NAMES):
-        assert L.albert_tensor_name(i).decode() == name
+        assert L.albert_tensor_name(ctypes.byref(c), i).decode() == name
         r, cc = ctypes.c_int64(), ctypes.c_int64()
         assert L.albert_tensor_shape(ctypes.byref(c), i, ctypes.byref(r), ctypes.byref(cc)) == 0
         shp = shapes[name]
         assert (r.value, cc.value) == (shp[0], shp[1] if len(shp) == 2 else 1)
-    assert L.albert_tensor_name(25) is None
-    assert L.albert_tensor_name(-1) is None
+    assert L.albert_tensor_name(ctypes.byref(c), 25) is None
+    assert L.albert_tensor_name(ctypes.byref(c), -1) is None
+
+
+@pytest.mark.parametrize("G", [2, 3, 12])
+def test_grouped_tensor_table(L, G):
+    """With G weight sets the layer tensors repeat per set, in the order
+    synth.tensor_names draws them."""
+    import albert_transformer_amd as A
+    c = A.default_config(n_groups=G)
+    cfg = synth.Config(n_groups=G)
+    names = synth.tensor_names(cfg)
+    assert L.albert_n_tensors(ctypes.byref(c)) == len(names) == 9 + 16 * G
+    shapes = cfg.shapes()
+    for i, name in enumerate(names):
+        assert L.albert_tensor_name(ctypes.byref(c), i).decode() == synth.base_name(name)
+        r, cc = ctypes.c_int64(), ctypes.c_int64()
+        assert L.albert_tensor_shape(ctypes.byref(c), i, ctypes.byref(r), ctypes.byref(cc)) == 0
+        shp = shapes[synth.base_name(name)]
+        assert (r.value, cc.value) == (shp[0], shp[1] if len(shp) == 2 else 1)
+    assert L.albert_tensor_name(ctypes.byref(c), len(names)) is None
 
 
 def test_config_rejections(L):
     import albert_transformer_amd as A
     r, cc = ctypes.c_int64(), ctypes.c_int64()
     for bad in (dict(hidden=1024), dict(heads=8), dict(ffn=1000), dict(out_dim=100),
-                dict(max_pos=513), dict(n_iter=-1), dict(emb=64)):
+                dict(max_pos=513), dict(n_iter=-1), dict(emb=64), dict(n_groups=0),
+                dict(n_groups=13), dict(n_iter=4, n_groups=5)):
         c = A.default_config(**bad)
         assert L.albert_tensor_shape(ctypes.byref(c), 0, ctypes.byref(r), ctypes.byref(cc)) == A.E_ARG
+        assert L.albert_n_tensors(ctypes.byref(c)) == -1
+    # n_iter = 0 keeps one weight set
+    assert L.albert_n_tensors(ctypes.byref(A.default_config(n_iter=0))) == 25
     h = ctypes.c_void_p()
     ptrs = (ctypes.c_void_p * 25)()
     c = A.default_config(hidden=1024)
