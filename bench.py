@@ -83,12 +83,12 @@ def traffic_for(kind: str, config: int):
     return rec["fetch_bytes"] + rec["write_bytes"]
 
 
-def cpu_baseline(wl, got, budget_s: float):
+def cpu_baseline(wl, got, budget_s: float, cfg=synth.KOKORO, weights=None):
     """Time the float64 oracle on this host over whole sequences of the same
     workload until `budget_s` seconds have passed; compare the GPU rows."""
     import oracle
     from threadpoolctl import threadpool_info
-    W = oracle.prepare_weights(synth.make_weights(), wl.dtype)
+    W = oracle.prepare_weights(synth.make_weights() if weights is None else weights, wl.dtype)
     threads = max([i.get("num_threads", 1) for i in threadpool_info()
                    if i.get("user_api") == "blas"] or [1])
     order = np.random.default_rng(7).permutation(wl.n_seq)
@@ -101,7 +101,7 @@ def cpu_baseline(wl, got, budget_s: float):
             ids, rows = wl.ids[a:a + L], got[a:a + L]
         else:
             ids, rows = wl.ids[s, :L], got[s, :L]
-        ref = oracle.encode_sequence(ids, W, synth.KOKORO)
+        ref = oracle.encode_sequence(ids, W, cfg)
         tokens += L
         done += 1
         d = rows.astype(np.float64) - ref
@@ -161,6 +161,8 @@ def main(argv=None) -> int:
     ap.add_argument("--config", type=int, default=3, help="workload 1..5 (3 = headline)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="wall budget of the oracle CPU baseline (0 = skip)")
+    ap.add_argument("--groups", type=int, default=1,
+                    help="distinct layer weight sets (1 = Kokoro's full sharing)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run one plain device copy of this size first (counter scaling)")
     args = ap.parse_args(argv)
@@ -176,7 +178,9 @@ def main(argv=None) -> int:
     torch.cuda.set_device(0)
     wl = synth.make_workload(args.config)
     dtype = wl.dtype
-    enc = A.Encoder(synth.make_weights(), dtype)
+    cfg = synth.Config(n_groups=args.groups)
+    weights = synth.make_weights(cfg)
+    enc = A.Encoder(weights, dtype, n_groups=args.groups)
     ids = torch.from_numpy(wl.ids).cuda()
     if wl.packed:
         cu = torch.from_numpy(wl.cu_seqlens).cuda()
@@ -244,9 +248,9 @@ def main(argv=None) -> int:
     achieved = kernel_flops(dominant, wl.lengths) / (launch_ms * 1e-3) / 1e12
 
     got = out.cpu().numpy()
-    base, parity = (cpu_baseline(wl, got, args.cpu_seconds) if args.cpu_seconds > 0
+    base, parity = (cpu_baseline(wl, got, args.cpu_seconds, cfg, weights) if args.cpu_seconds > 0
                     else (None, None))
-    length_reg = measure_length_regulation() if args.config == 3 else None
+    length_reg = measure_length_regulation() if args.config == 3 and args.groups == 1 else None
 
     line = {
         "metric": METRIC,
@@ -269,6 +273,7 @@ def main(argv=None) -> int:
             "tokens_per_step": tokens,
             "padded_slots_per_step": wl.rows,
             "shared_layer_executions": NITER,
+            "layer_weight_sets": args.groups,
         },
         "tflops_end_to_end": round(flops_step / (ms_step * 1e-3) / 1e12, 2),
         "mfma_frac_end_to_end": round(flops_step / (ms_step * 1e-3) / 1e12 / peak, 4),
@@ -279,7 +284,7 @@ def main(argv=None) -> int:
             "peak": peak,
             "unit": "TFLOP/s",
             "frac": round(achieved / peak, 4),
-            "traffic": traffic_for(dominant, args.config),
+            "traffic": traffic_for(dominant, args.config) if args.groups == 1 else None,
             "ms_per_launch": round(launch_ms, 5),
             "launches_timed": n_dom,
         },
