@@ -10,6 +10,7 @@ from .albert_oracle import (  # noqa: F401
     bf16_round, prepare_weights, validate, layer_norm, gelu_tanh, softmax,
     dense, attention, shared_layer, embed_ln, encode_sequence, encode,
     encode_varlen, expand_durations, duration_from_logits, param_counts,
-    group_schedule, layer_set,
+    group_schedule, layer_set, encode_features, encode_fp8_features, e4m3_round,
+    fp8_row_exponents, fp8_quantize_rows, E4M3_MAX,
     OracleError,
 )

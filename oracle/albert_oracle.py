@@ -20,7 +20,10 @@ Sources (the pages this follows):
             mathematical contracts", contract A (a biased projection
             y_j = b_j + sum_i x_i W[j,i], weights stored [out, in]).
   [HAILO]   "Kokoro-82M-encoder-hailo10h" model card -- "What this is": the
-            GELU is the tanh approximation and contains a cubic.
+            GELU is the tanh approximation and contains a cubic; "Eval
+            results": low-precision fidelity is scored with N(0,1) inputs fed
+            at the embedding LayerNorm output ([128,128] per sample) and the
+            per-sample cosine of the flattened [128,512] outputs.
 
 Everything is evaluated in float64.  For the bf16 path the oracle consumes the
 exact weight values the GPU consumes (matrices and tables rounded to bf16 by
@@ -64,6 +67,52 @@ def bf16_round(x) -> np.ndarray:
     return u.astype(np.uint32).view(np.float32).astype(np.float64)
 
 
+E4M3_MAX = 448.0
+
+
+def e4m3_round(x) -> np.ndarray:
+    """Round to the nearest OCP FP8 E4M3 value, ties to even, saturating.
+
+    E4M3 has 4 exponent bits (bias 7) and 3 stored mantissa bits: normal
+    values m * 2^(e-3) with 8 <= m < 16 and -6 <= e <= 8, subnormals
+    m * 2^-9 with m < 8, largest finite 448 (the all-ones pattern is NaN,
+    so there is no infinity).  Reading for the low-precision variant:
+    magnitudes beyond 448 saturate to 448.  Works in float64 on any input.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    a = np.minimum(np.abs(x), E4M3_MAX)
+    _, e = np.frexp(a)                      # a = f * 2^e, 0.5 <= f < 1
+    step = np.ldexp(1.0, np.maximum(e - 1, -6) - 3)  # spacing at a's binade
+    r = np.minimum(np.round(a / step) * step, E4M3_MAX)  # np.round: half to even
+    return np.copysign(r, x)
+
+
+def fp8_row_exponents(w) -> np.ndarray:
+    """Per-output-row power-of-two scale for an [out, in] weight matrix.
+
+    Reading for the low-precision variant: row j is stored as
+    e4m3(W[j, :] * 2^k_j) with the largest integer k_j such that
+    max_i |W[j, i]| * 2^k_j <= 448 (k_j = 0 for an all-zero row), and the
+    product is multiplied back by 2^-k_j, which is exact.
+    """
+    w = np.asarray(w, dtype=np.float64)
+    m = np.abs(w).max(axis=1)
+    k = np.zeros(m.shape, dtype=np.int64)
+    nz = m > 0
+    k[nz] = np.floor(np.log2(E4M3_MAX / m[nz])).astype(np.int64)
+    # settle log2's rounding at exact powers of two
+    k[nz] += (m[nz] * np.ldexp(1.0, k[nz] + 1) <= E4M3_MAX).astype(np.int64)
+    k[nz] -= (m[nz] * np.ldexp(1.0, k[nz]) > E4M3_MAX).astype(np.int64)
+    return k
+
+
+def fp8_quantize_rows(w) -> np.ndarray:
+    """The weight values the low-precision variant multiplies with."""
+    w = np.asarray(w, dtype=np.float64)
+    sc = np.ldexp(1.0, fp8_row_exponents(w))[:, None]
+    return e4m3_round(w * sc) / sc
+
+
 def prepare_weights(w: dict, dtype: str) -> dict:
     """Widen the float32 weight set to float64, as the given path stores it.
 
@@ -71,15 +120,19 @@ def prepare_weights(w: dict, dtype: str) -> dict:
     dtype "bf16": tables and linear weight matrices rounded to bf16 first;
     biases and LayerNorm gains/shifts kept in float32 (the library's storage
     rule, so that both sides see identical parameter values).
+    dtype "fp8": tables rounded to bf16, linear weight matrices quantized
+    per row to E4M3 (``fp8_quantize_rows``), vectors kept in float32.
     """
-    if dtype not in ("f32", "bf16"):
+    if dtype not in ("f32", "bf16", "fp8"):
         raise ValueError(dtype)
     out = {}
     for name, t in w.items():
         t32 = np.asarray(t, dtype=np.float32)
         head, _, rest = name.partition(".")
         role = rest if head[:1] == "g" and head[1:].isdigit() else name
-        if dtype == "bf16" and role in _MATRIX_NAMES:
+        if dtype == "fp8" and role in _MATRIX_NAMES and role.endswith(".w"):
+            out[name] = fp8_quantize_rows(t32)
+        elif dtype in ("bf16", "fp8") and role in _MATRIX_NAMES:
             out[name] = bf16_round(t32)
         else:
             out[name] = t32.astype(np.float64)
@@ -308,6 +361,66 @@ def encode_varlen(ids, cu_seqlens, W: dict, cfg, n_iter: int | None = None,
         a, b = int(cu[s]), int(cu[s + 1])
         out[a:b] = encode_sequence(ids[a:b], W, cfg, n_iter)
     return out
+
+
+def encode_features(x_ln, W: dict, cfg, n_iter: int | None = None) -> np.ndarray:
+    """Encode from the embedding LayerNorm output [L, E] of one sequence.
+
+    The split the Hailo deployment uses ([HAILO] "What this is not": the
+    embedding and its LayerNorm run elsewhere and the encoder block starts
+    at the projection): E->H projection, the layer executions, H->512.
+    """
+    n_iter = cfg.n_iter if n_iter is None else n_iter
+    sched = group_schedule(n_iter, getattr(cfg, "n_groups", 1))
+    sets = [layer_set(W, cfg, g) for g in range(getattr(cfg, "n_groups", 1))]
+    h = dense(x_ln, W["proj.w"], W["proj.b"])
+    for it in range(n_iter):
+        h = shared_layer(h, sets[sched[it]], cfg)
+    return dense(h, W["out.w"], W["out.b"])
+
+
+def _bf16_of(x):
+    """bf16 storage of a float64 activation (rounded via float32)."""
+    return bf16_round(np.asarray(x, dtype=np.float64).astype(np.float32))
+
+
+# Storage roundings of the low-precision variant (module level so that a
+# test can replace them with the identity).
+fp8_operand = e4m3_round
+fp8_store = _bf16_of
+
+
+def encode_fp8_features(x_ln, W8: dict, cfg, n_iter: int | None = None) -> np.ndarray:
+    """The low-precision (FP8) variant from the LayerNorm output [L, E].
+
+    Same steps as ``encode_features``; what changes is where values are
+    rounded (the variant's definition, a reading of "FP8 GEMM operands"):
+    every matrix-product input is an E4M3 value (``fp8_operand``) and every
+    stored activation that is not a product input -- the residual stream,
+    Q|K|V -- is bf16 (``fp8_store``).  W8 comes from
+    prepare_weights(..., "fp8").  Products, biases, softmax, GELU and
+    LayerNorm are exact (float64) here.
+    """
+    n_iter = cfg.n_iter if n_iter is None else n_iter
+    sched = group_schedule(n_iter, getattr(cfg, "n_groups", 1))
+    sets = [layer_set(W8, cfg, g) for g in range(getattr(cfg, "n_groups", 1))]
+    op, st = fp8_operand, fp8_store
+    y = dense(op(x_ln), W8["proj.w"], W8["proj.b"])
+    h, h8 = st(y), op(y)
+    for it in range(n_iter):
+        Wl = sets[sched[it]]
+        q = st(dense(h8, Wl["q.w"], Wl["q.b"]))
+        k = st(dense(h8, Wl["k.w"], Wl["k.b"]))
+        v = st(dense(h8, Wl["v.w"], Wl["v.b"]))
+        c8 = op(attention(q, k, v, cfg.heads))
+        y = layer_norm(h + dense(c8, Wl["o.w"], Wl["o.b"]), Wl["attn_ln.g"], Wl["attn_ln.b"],
+                       cfg.ln_eps)
+        h1, h18 = st(y), op(y)
+        g8 = op(gelu_tanh(dense(h18, Wl["ffn1.w"], Wl["ffn1.b"])))
+        y = layer_norm(h1 + dense(g8, Wl["ffn2.w"], Wl["ffn2.b"]), Wl["ffn_ln.g"], Wl["ffn_ln.b"],
+                       cfg.ln_eps)
+        h, h8 = st(y), op(y)
+    return dense(h8, W8["out.w"], W8["out.b"])
 
 
 def duration_from_logits(logits, speed: float = 1.0) -> np.ndarray:
