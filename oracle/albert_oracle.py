@@ -92,8 +92,9 @@ def fp8_row_exponents(w) -> np.ndarray:
 
     Reading for the low-precision variant: row j is stored as
     e4m3(W[j, :] * 2^k_j) with the largest integer k_j such that
-    max_i |W[j, i]| * 2^k_j <= 448 (k_j = 0 for an all-zero row), and the
-    product is multiplied back by 2^-k_j, which is exact.
+    max_i |W[j, i]| * 2^k_j <= 448 (k_j = 0 for an all-zero row, and at most
+    127 so that 2^-k_j is an E8M0 scale), and the product is multiplied back
+    by 2^-k_j, which is exact.
     """
     w = np.asarray(w, dtype=np.float64)
     m = np.abs(w).max(axis=1)
@@ -103,7 +104,8 @@ def fp8_row_exponents(w) -> np.ndarray:
     # settle log2's rounding at exact powers of two
     k[nz] += (m[nz] * np.ldexp(1.0, k[nz] + 1) <= E4M3_MAX).astype(np.int64)
     k[nz] -= (m[nz] * np.ldexp(1.0, k[nz]) > E4M3_MAX).astype(np.int64)
-    return k
+    # an E8M0 scale 2^-k needs k <= 127 (rows below 448 * 2^-127 keep k = 127)
+    return np.minimum(k, 127)
 
 
 def fp8_quantize_rows(w) -> np.ndarray:
