@@ -392,7 +392,8 @@ fp8_operand = e4m3_round
 fp8_store = _bf16_of
 
 
-def encode_fp8_features(x_ln, W8: dict, cfg, n_iter: int | None = None) -> np.ndarray:
+def encode_fp8_features(x_ln, W8: dict, cfg, n_iter: int | None = None,
+                        taps: dict | None = None) -> np.ndarray:
     """The low-precision (FP8) variant from the LayerNorm output [L, E].
 
     Same steps as ``encode_features``; what changes is where values are
@@ -401,27 +402,36 @@ def encode_fp8_features(x_ln, W8: dict, cfg, n_iter: int | None = None) -> np.nd
     stored activation that is not a product input -- the residual stream,
     Q|K|V -- is bf16 (``fp8_store``).  W8 comes from
     prepare_weights(..., "fp8").  Products, biases, softmax, GELU and
-    LayerNorm are exact (float64) here.
+    LayerNorm are exact (float64) here.  When `taps` is a dict, the values
+    before each rounding are stored in it: "x0" (projection), and for the
+    last execution "qkv", "ctx", "h1", "f1" (FFN1 output before GELU), "g"
+    (after GELU) and "out" (the execution's output).
     """
     n_iter = cfg.n_iter if n_iter is None else n_iter
     sched = group_schedule(n_iter, getattr(cfg, "n_groups", 1))
     sets = [layer_set(W8, cfg, g) for g in range(getattr(cfg, "n_groups", 1))]
     op, st = fp8_operand, fp8_store
     y = dense(op(x_ln), W8["proj.w"], W8["proj.b"])
+    if taps is not None:
+        taps["x0"] = y
     h, h8 = st(y), op(y)
     for it in range(n_iter):
         Wl = sets[sched[it]]
-        q = st(dense(h8, Wl["q.w"], Wl["q.b"]))
-        k = st(dense(h8, Wl["k.w"], Wl["k.b"]))
-        v = st(dense(h8, Wl["v.w"], Wl["v.b"]))
-        c8 = op(attention(q, k, v, cfg.heads))
+        qkv = [dense(h8, Wl[n + ".w"], Wl[n + ".b"]) for n in ("q", "k", "v")]
+        q, k, v = (st(t) for t in qkv)
+        c = attention(q, k, v, cfg.heads)
+        c8 = op(c)
         y = layer_norm(h + dense(c8, Wl["o.w"], Wl["o.b"]), Wl["attn_ln.g"], Wl["attn_ln.b"],
                        cfg.ln_eps)
         h1, h18 = st(y), op(y)
-        g8 = op(gelu_tanh(dense(h18, Wl["ffn1.w"], Wl["ffn1.b"])))
-        y = layer_norm(h1 + dense(g8, Wl["ffn2.w"], Wl["ffn2.b"]), Wl["ffn_ln.g"], Wl["ffn_ln.b"],
-                       cfg.ln_eps)
-        h, h8 = st(y), op(y)
+        f1 = dense(h18, Wl["ffn1.w"], Wl["ffn1.b"])
+        g8 = op(gelu_tanh(f1))
+        y2 = layer_norm(h1 + dense(g8, Wl["ffn2.w"], Wl["ffn2.b"]), Wl["ffn_ln.g"], Wl["ffn_ln.b"],
+                        cfg.ln_eps)
+        if taps is not None:
+            taps.update(qkv=np.concatenate(qkv, axis=1), ctx=c, h1=y, f1=f1, g=gelu_tanh(f1),
+                        out=y2)
+        h, h8 = st(y2), op(y2)
     return dense(h8, W8["out.w"], W8["out.b"])
 
 
