@@ -18,15 +18,16 @@ LIB_PATH = os.path.join(HERE, "libalbert.so")
 OK, E_ARG, E_WORKSPACE, E_LENGTH, E_ID, E_ALIAS, E_HIP = range(7)
 STATUS_NAMES = {OK: "OK", E_ARG: "E_ARG", E_WORKSPACE: "E_WORKSPACE",
                 E_LENGTH: "E_LENGTH", E_ID: "E_ID", E_ALIAS: "E_ALIAS", E_HIP: "E_HIP"}
-F32, BF16 = 0, 1
+F32, BF16, FP8 = 0, 1, 2
+DTYPES = {"f32": F32, "bf16": BF16, "fp8": FP8}
 ASYNC = 1
 N_TENSORS = 25
 TAPS = {"status": 0, "cu": 1, "row_seq": 2, "row_pos": 3, "emb": 4, "x": 5,
-        "qkv": 6, "ctx": 7, "x1": 8, "g": 9}
+        "qkv": 6, "ctx": 7, "x1": 8, "g": 9, "x8": 10, "x1_8": 11}
 
 EXPORTS = ("albert_default_config", "albert_n_tensors", "albert_tensor_name",
            "albert_tensor_shape", "albert_load_weights", "albert_workspace_bytes", "albert_encode",
-           "albert_encode_varlen", "albert_read_status", "albert_tap", "albert_free",
+           "albert_encode_varlen", "albert_encode_features", "albert_read_status", "albert_tap", "albert_free",
            "albert_status_str", "albert_time_kernel", "albert_kernel_time",
            "albert_durations", "albert_expand_workspace_bytes", "albert_expand")
 KERNEL_KINDS = ("embed", "proj", "qkv", "attn", "attn_out_ln", "ffn1_gelu", "ffn2_ln", "out")
@@ -73,6 +74,9 @@ def lib():
     L.albert_encode_varlen.argtypes = [vp, vp, vp, i32, i32, i32, vp, vp, sz, vp,
                                        ctypes.c_uint]
     L.albert_encode_varlen.restype = i32
+    L.albert_encode_features.argtypes = [vp, vp, vp, i32, i32, i32, vp, vp, sz, vp,
+                                         ctypes.c_uint]
+    L.albert_encode_features.restype = i32
     L.albert_read_status.argtypes = [vp, vp]
     L.albert_read_status.restype = i32
     L.albert_tap.argtypes = [vp, i32, i64, i32, ctypes.POINTER(sz), ctypes.POINTER(sz),
@@ -129,8 +133,9 @@ class Encoder:
 
     weights: dict of canonical name -> float32 numpy array (see
     ``synth.tensor_names``: with n_groups = G > 1 the layer tensors of set g
-    are named "g<g>.<name>"); dtype "bf16" or "f32"; config overrides as
-    keyword arguments (e.g. n_iter=1, n_groups=3).
+    are named "g<g>.<name>"); dtype "bf16", "fp8" (E4M3 matrix-product
+    operands) or "f32"; config overrides as keyword arguments (e.g.
+    n_iter=1, n_groups=3).
     """
 
     def __init__(self, weights: dict, dtype: str = "bf16", stream=None, **cfg):
@@ -160,8 +165,7 @@ class Encoder:
             self._host.append(a)
         ptrs = (ctypes.c_void_p * nt)(*[a.ctypes.data for a in self._host])
         h = ctypes.c_void_p()
-        rc = L.albert_load_weights(ctypes.byref(h), cf, ptrs,
-                                   BF16 if dtype == "bf16" else F32, _stream(stream))
+        rc = L.albert_load_weights(ctypes.byref(h), cf, ptrs, DTYPES[dtype], _stream(stream))
         self._host = None
         if rc != OK:
             raise AlbertError(rc, "albert_load_weights")
@@ -221,6 +225,28 @@ class Encoder:
         nb = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
         return lib().albert_encode_varlen(self.handle, _ptr(ids), _ptr(cu), n, total, max_len,
                                           _ptr(out), _ptr(ws), nb, _stream(stream), flags)
+
+    def encode_features_raw(self, x, cu, max_len, out, ws, stream=None, flags=0,
+                            ws_bytes=None, n=None, total=None) -> int:
+        """Packed call from embedding LayerNorm output x fp32 [total, 128]."""
+        n = cu.numel() - 1 if n is None else n
+        total = x.shape[0] if total is None else total
+        nb = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
+        return lib().albert_encode_features(self.handle, _ptr(x), _ptr(cu), n, total, max_len,
+                                            _ptr(out), _ptr(ws), nb, _stream(stream), flags)
+
+    def encode_features(self, x, cu, max_len, out=None, ws=None, stream=None):
+        """x fp32 [total, 128], cu int32 [n+1] (CUDA tensors) -> fp32 [total, 512]."""
+        import torch
+        total = x.shape[0]
+        if out is None:
+            out = torch.empty(total, self.cfg.out_dim, dtype=torch.float32, device="cuda")
+        if ws is None:
+            ws = self.new_workspace(cu.numel() - 1, total)
+        rc = self.encode_features_raw(x, cu, max_len, out, ws, stream)
+        if rc != OK:
+            raise AlbertError(rc, "albert_encode_features")
+        return out
 
     def encode(self, ids, lengths, out=None, ws=None, stream=None):
         """ids int32 [B, T], lengths int32 [B] (CUDA tensors) -> fp32 [B, T, 512]."""

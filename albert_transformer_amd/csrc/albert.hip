@@ -28,9 +28,11 @@
 
 using namespace albert;
 
-// Device pointers of one layer weight set (matrices in dtype, vectors fp32).
+// Device pointers of one layer weight set (matrices in dtype -- E4M3 codes
+// plus per-row E8M0 exponents under ALBERT_FP8 -- vectors fp32).
 struct LayerW {
   const void *qkv_w, *o_w, *ffn1_w, *ffn2_w;
+  const unsigned char *qkv_e, *o_e, *ffn1_e, *ffn2_e;
   const float *qkv_b, *o_b, *ln1_g, *ln1_b, *ffn1_b, *ffn2_b, *ln2_g, *ln2_b;
 };
 
@@ -42,6 +44,7 @@ struct albert_ctx {
   void* mem;
   // device pointers (tables/matrices in dtype, vectors fp32)
   const void *word, *pos, *type, *proj_w, *out_w;
+  const unsigned char *proj_e, *out_e;
   const float *emb_g, *emb_b, *proj_b, *out_b;
   std::vector<LayerW> layers;  // n_groups weight sets
   // optional kernel timing (albert_time_kernel)
@@ -115,27 +118,63 @@ uint16_t f32_to_bf16_bits(float f) {
   return (uint16_t)(u >> 16);
 }
 
+// OCP FP8 E4M3 code of a finite value: round to nearest even on the 3-bit
+// mantissa grid of the value's binade (subnormals share the 2^-6 binade),
+// magnitudes of 448 and beyond saturate to 448 (0x7E; 0x7F is NaN).
+uint8_t f32_to_e4m3(double v) {
+  const uint8_t sign = std::signbit(v) ? 0x80 : 0x00;
+  const double a = std::fabs(v);
+  if (a >= 448.0) return sign | 0x7E;
+  int e = 0;
+  std::frexp(a, &e);                 // a = f * 2^e, 0.5 <= f < 1
+  int E = std::max(e - 1, -6);
+  double q = std::nearbyint(std::ldexp(a, 3 - E));  // ties to even
+  if (q >= 16.0) { q *= 0.5; E += 1; }              // rounded up into the next binade
+  if (q < 8.0) return sign | (uint8_t)q;            // subnormal (E == -6) or zero
+  return sign | (uint8_t)(((E + 7) << 3) | ((int)q - 8));
+}
+
+// Largest k with max|row| * 2^k <= 448 (0 for a zero row), within the
+// E8M0 range used here.
+int e4m3_row_exp(const float* row, int64_t n, float scale) {
+  double m = 0.0;
+  for (int64_t i = 0; i < n; ++i) m = std::max(m, std::fabs((double)row[i] * scale));
+  if (m == 0.0) return 0;
+  int k = (int)std::floor(std::log2(448.0 / m));
+  while (m * std::ldexp(1.0, k + 1) <= 448.0) ++k;
+  while (m * std::ldexp(1.0, k) > 448.0) --k;
+  return std::min(k, 127);
+}
+
 struct Layout {
-  size_t status, cu, row_seq, row_pos, emb, x, x1, qkv, ctx, g, total;
+  size_t status, cu, row_seq, row_pos, emb, x, x1, x8, x18, qkv, ctx, g, total;
   int64_t rows_cap;
 };
 
+// Bytes per stored element / per matrix-product operand element.
+size_t store_bytes(int dtype) { return dtype == ALBERT_F32 ? 4 : 2; }
+size_t operand_bytes(int dtype) { return dtype == ALBERT_FP8 ? 1 : store_bytes(dtype); }
+
 Layout plan(const albert_ctx* c, int n_seq, int64_t max_rows) {
   Layout L{};
-  const size_t es = c->dtype == ALBERT_BF16 ? 2 : 4;
+  const size_t es = store_bytes(c->dtype), eo = operand_bytes(c->dtype);
+  const bool f8 = c->dtype == ALBERT_FP8;
   const int64_t rows = (int64_t)align_up((size_t)max_rows, 256);
+  const size_t H = (size_t)c->cfg.hidden;
   size_t off = 0;
   L.rows_cap = rows;
   L.status = off; off += kAlign;
   L.cu = off; off += align_up((size_t)(n_seq + 1) * 4, kAlign);
   L.row_seq = off; off += align_up((size_t)rows * 4, kAlign);
   L.row_pos = off; off += align_up((size_t)rows * 4, kAlign);
-  L.emb = off; off += align_up((size_t)rows * c->cfg.emb * es, kAlign);
-  L.x = off; off += align_up((size_t)rows * c->cfg.hidden * es, kAlign);
-  L.x1 = off; off += align_up((size_t)rows * c->cfg.hidden * es, kAlign);
-  L.qkv = off; off += align_up((size_t)rows * 3 * c->cfg.hidden * es, kAlign);
-  L.ctx = off; off += align_up((size_t)rows * c->cfg.hidden * es, kAlign);
-  L.g = off; off += align_up((size_t)rows * c->cfg.ffn * es, kAlign);
+  L.emb = off; off += align_up((size_t)rows * c->cfg.emb * eo, kAlign);
+  L.x = off; off += align_up((size_t)rows * H * es, kAlign);
+  L.x1 = off; off += align_up((size_t)rows * H * es, kAlign);
+  L.x8 = off; off += f8 ? align_up((size_t)rows * H, kAlign) : 0;
+  L.x18 = off; off += f8 ? align_up((size_t)rows * H, kAlign) : 0;
+  L.qkv = off; off += align_up((size_t)rows * 3 * H * es, kAlign);
+  L.ctx = off; off += align_up((size_t)rows * H * eo, kAlign);
+  L.g = off; off += align_up((size_t)rows * c->cfg.ffn * eo, kAlign);
   L.total = off;
   return L;
 }
@@ -148,35 +187,44 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
 
 // Persistent launch: one block per CU at most (a multiple of 8, so that the
 // kernel's XCD-aware tile numbering is a bijection), each walking its tiles.
-template <typename T, int BM, int BN, int WGM, int WGN, int RB, int STAGES, int EPI, bool DEFER>
+template <typename T, bool F8, int BM, int BN, int WGM, int WGN, int RB, int STAGES, int EPI,
+          bool DEFER>
 void launch_gemm(GemmArgs g, int64_t max_rows, int grid_cap, hipStream_t s) {
   g.n_tiles = g.N / BN;
   const int64_t tiles = (max_rows + BM - 1) / BM * g.n_tiles;
   const int64_t grid = std::min<int64_t>((tiles + 7) / 8 * 8, grid_cap);
-  hipLaunchKernelGGL((gemm_kernel<T, BM, BN, WGM, WGN, RB, STAGES, EPI, DEFER>),
+  hipLaunchKernelGGL((gemm_kernel<T, F8, BM, BN, WGM, WGN, RB, STAGES, EPI, DEFER>),
                      dim3((unsigned)grid), dim3(WGM * WGN * 64), 0, s, g);
 }
 
 // Large tiles for plain and GELU epilogues; full-row tiles for LayerNorm.
 // bf16 bias/GELU GEMMs with at least 12 (an even number of) K slices keep
 // each tile's outputs in registers and write them during the next tile.
-template <typename T, int EPI>
+// E4M3 operands stage 64-byte rows (one 64-deep MFMA step per slice).
+template <typename T, bool F8, int EPI>
 void gemm_big(GemmArgs g, int64_t max_rows, int grid_cap, hipStream_t s) {
-  constexpr bool can_defer = std::is_same<T, bf16>::value && (EPI == EPI_BIAS || EPI == EPI_GELU);
-  const int slices = g.K / (128 / (int)sizeof(T));
-  if (can_defer && slices >= 12 && slices % 2 == 0)
-    launch_gemm<T, 256, 256, 2, 2, 128, 2, EPI, can_defer>(g, max_rows, grid_cap, s);
+  constexpr bool can_defer =
+      std::is_same<T, bf16>::value && !F8 && (EPI == EPI_BIAS || EPI == EPI_GELU);
+  constexpr int RB = F8 ? 64 : 128;
+  const int slices = g.K * (F8 ? 1 : (int)sizeof(T)) / RB;
+  if (can_defer && slices >= 12 && slices % 2 == 0 && !g.Y8)
+    launch_gemm<T, F8, 256, 256, 2, 2, RB, 2, EPI, can_defer>(g, max_rows, grid_cap, s);
   else
-    launch_gemm<T, 256, 256, 2, 2, 128, 2, EPI, false>(g, max_rows, grid_cap, s);
+    launch_gemm<T, F8, 256, 256, 2, 2, RB, 2, EPI, false>(g, max_rows, grid_cap, s);
 }
 // 128-row tiles need at least a full wave of them; smaller batches use
 // 64-row tiles (4 waves, one per SIMD) to spread over more CUs.
-template <typename T>
+// (E4M3 fragments are too wide for the 8-wave tile's register budget, so the
+// low-precision variant always uses the 4-wave one.)
+template <typename T, bool F8>
 void gemm_ln(GemmArgs g, int64_t max_rows, int grid_cap, hipStream_t s) {
-  if ((max_rows + 127) / 128 >= grid_cap)
-    launch_gemm<T, 128, 768, 2, 4, 64, 2, EPI_LN, false>(g, max_rows, grid_cap, s);
-  else
-    launch_gemm<T, 64, 768, 1, 4, 64, 2, EPI_LN, false>(g, max_rows, grid_cap, s);
+  if constexpr (!F8) {
+    if ((max_rows + 127) / 128 >= grid_cap) {
+      launch_gemm<T, F8, 128, 768, 2, 4, 64, 2, EPI_LN, false>(g, max_rows, grid_cap, s);
+      return;
+    }
+  }
+  launch_gemm<T, F8, 64, 768, 1, 4, 64, 2, EPI_LN, false>(g, max_rows, grid_cap, s);
 }
 
 // Launch `fn` on stream s, bracketed by timing events when `kind` is the
@@ -192,9 +240,13 @@ void timed(albert_ctx* c, int kind, hipStream_t s, Fn&& fn) {
   }
 }
 
-template <typename T>
+// One request.  T is the storage type; F8 selects E4M3 matrix-product
+// operands (ALBERT_FP8).  feats != null: packed rows of embedding LayerNorm
+// output replace the IDs and the embedding.
+template <typename T, bool F8>
 int run(albert_ctx* c, const int32_t* ids, const int32_t* lens_or_cu, int n_seq, int pad_T,
-        int64_t max_rows, int max_len, float* out, void* ws, hipStream_t s) {
+        int64_t max_rows, int max_len, float* out, void* ws, hipStream_t s,
+        const float* feats = nullptr) {
   const albert_config& cf = c->cfg;
   const Layout L = plan(c, n_seq, max_rows);
   char* w = static_cast<char*>(ws);
@@ -202,12 +254,17 @@ int run(albert_ctx* c, const int32_t* ids, const int32_t* lens_or_cu, int n_seq,
   int* cu = reinterpret_cast<int*>(w + L.cu);
   int* row_seq = reinterpret_cast<int*>(w + L.row_seq);
   int* row_pos = reinterpret_cast<int*>(w + L.row_pos);
-  T* emb = reinterpret_cast<T*>(w + L.emb);
+  void* emb = w + L.emb;          // operand of the input projection
   T* X = reinterpret_cast<T*>(w + L.x);
   T* X1 = reinterpret_cast<T*>(w + L.x1);
   T* QKV = reinterpret_cast<T*>(w + L.qkv);
-  T* CTX = reinterpret_cast<T*>(w + L.ctx);
-  T* G = reinterpret_cast<T*>(w + L.g);
+  void* CTX = w + L.ctx;          // operand of the output projection
+  void* G = w + L.g;              // operand of FFN2
+  // operands of the Q|K|V and FFN1 products, and their E4M3 copies
+  void* X8 = F8 ? static_cast<void*>(w + L.x8) : static_cast<void*>(X);
+  void* X18 = F8 ? static_cast<void*>(w + L.x18) : static_cast<void*>(X1);
+  void* Y8 = F8 ? X8 : nullptr;
+  void* Y18 = F8 ? X18 : nullptr;
   const int H = cf.hidden, F = cf.ffn;
   const int* m_ptr = cu + n_seq;
 
@@ -217,14 +274,22 @@ int run(albert_ctx* c, const int32_t* ids, const int32_t* lens_or_cu, int n_seq,
   else
     hipLaunchKernelGGL(derive_packed_kernel, dim3(1), dim3(1024), 0, s, lens_or_cu, n_seq,
                        (int)max_rows, max_len, cu, status);
-  hipLaunchKernelGGL(rows_ids_kernel, dim3(n_seq), dim3(256), 0, s, ids, cu, pad_T, cf.vocab,
-                     row_seq, row_pos, status);
-  timed(c, ALBERT_K_EMBED, s, [&] {
-    hipLaunchKernelGGL(embed_ln_kernel<T>, dim3((unsigned)((max_rows + 15) / 16)), dim3(256), 0,
-                       s, ids, pad_T, row_seq, row_pos, m_ptr, (const T*)c->word,
-                       (const T*)c->pos, (const T*)c->type, c->emb_g, c->emb_b, cf.ln_eps, emb,
-                       status);
-  });
+  if (feats) {
+    timed(c, ALBERT_K_EMBED, s, [&] {
+      hipLaunchKernelGGL((features_in_kernel<T, F8>),
+                         dim3((unsigned)((max_rows * cf.emb / 4 + 255) / 256)), dim3(256), 0, s,
+                         feats, m_ptr, emb, status);
+    });
+  } else {
+    hipLaunchKernelGGL(rows_ids_kernel, dim3(n_seq), dim3(256), 0, s, ids, cu, pad_T, cf.vocab,
+                       row_seq, row_pos, status);
+    timed(c, ALBERT_K_EMBED, s, [&] {
+      hipLaunchKernelGGL((embed_ln_kernel<T, F8>), dim3((unsigned)((max_rows + 15) / 16)),
+                         dim3(256), 0, s, ids, pad_T, row_seq, row_pos, m_ptr, (const T*)c->word,
+                         (const T*)c->pos, (const T*)c->type, c->emb_g, c->emb_b, cf.ln_eps, emb,
+                         status);
+    });
+  }
 
   GemmArgs base{};
   base.status = status;
@@ -232,47 +297,60 @@ int run(albert_ctx* c, const int32_t* ids, const int32_t* lens_or_cu, int n_seq,
   base.eps = cf.ln_eps;
 
   GemmArgs g = base;  // input projection E -> H
-  g.X = emb; g.ldx = cf.emb; g.W = c->proj_w; g.bias = c->proj_b; g.Y = X; g.ldy = H;
-  g.N = H; g.K = cf.emb;
-  timed(c, ALBERT_K_PROJ, s, [&] { gemm_big<T, EPI_BIAS>(g, max_rows, c->grid_cap, s); });
+  g.X = emb; g.ldx = cf.emb; g.W = c->proj_w; g.wexp = c->proj_e; g.bias = c->proj_b;
+  g.Y = X; g.ldy = H; g.Y8 = Y8; g.ldy8 = H; g.N = H; g.K = cf.emb;
+  timed(c, ALBERT_K_PROJ, s, [&] { gemm_big<T, F8, EPI_BIAS>(g, max_rows, c->grid_cap, s); });
 
   const int qtiles = (max_len + 127) / 128;
   for (int it = 0; it < cf.n_iter; ++it) {
     const LayerW& lw = c->layers[(size_t)((int64_t)it * cf.n_groups / cf.n_iter)];
     g = base;  // fused Q|K|V projection
-    g.X = X; g.ldx = H; g.W = lw.qkv_w; g.bias = lw.qkv_b; g.Y = QKV; g.ldy = 3 * H;
-    g.N = 3 * H; g.K = H;
-    timed(c, ALBERT_K_QKV, s, [&] { gemm_big<T, EPI_BIAS>(g, max_rows, c->grid_cap, s); });
+    g.X = X8; g.ldx = H; g.W = lw.qkv_w; g.wexp = lw.qkv_e; g.bias = lw.qkv_b; g.Y = QKV;
+    g.ldy = 3 * H; g.N = 3 * H; g.K = H;
+    timed(c, ALBERT_K_QKV, s, [&] { gemm_big<T, F8, EPI_BIAS>(g, max_rows, c->grid_cap, s); });
 
     AttnArgs a{QKV, CTX, cu, status};
     timed(c, ALBERT_K_ATTN, s, [&] {
-      hipLaunchKernelGGL(attention_kernel<T>, dim3(n_seq, cf.heads, qtiles), dim3(256), 0, s, a);
+      hipLaunchKernelGGL((attention_kernel<T, F8>), dim3(n_seq, cf.heads, qtiles), dim3(256), 0,
+                         s, a);
     });
 
     g = base;  // output projection + residual + LayerNorm
-    g.X = CTX; g.ldx = H; g.W = lw.o_w; g.bias = lw.o_b; g.R = X; g.ldr = H;
-    g.ln_g = lw.ln1_g; g.ln_b = lw.ln1_b; g.Y = X1; g.ldy = H; g.N = H; g.K = H;
-    timed(c, ALBERT_K_ATTN_OUT_LN, s, [&] { gemm_ln<T>(g, max_rows, c->grid_cap, s); });
+    g.X = CTX; g.ldx = H; g.W = lw.o_w; g.wexp = lw.o_e; g.bias = lw.o_b; g.R = X; g.ldr = H;
+    g.ln_g = lw.ln1_g; g.ln_b = lw.ln1_b; g.Y = X1; g.ldy = H; g.Y8 = Y18; g.ldy8 = H;
+    g.N = H; g.K = H;
+    timed(c, ALBERT_K_ATTN_OUT_LN, s, [&] { gemm_ln<T, F8>(g, max_rows, c->grid_cap, s); });
 
     g = base;  // FFN 768 -> 2048 + GELU
-    g.X = X1; g.ldx = H; g.W = lw.ffn1_w; g.bias = lw.ffn1_b; g.Y = G; g.ldy = F;
-    g.N = F; g.K = H;
-    timed(c, ALBERT_K_FFN1_GELU, s, [&] { gemm_big<T, EPI_GELU>(g, max_rows, c->grid_cap, s); });
+    g.X = X18; g.ldx = H; g.W = lw.ffn1_w; g.wexp = lw.ffn1_e; g.bias = lw.ffn1_b; g.Y = G;
+    g.ldy = F; g.N = F; g.K = H;
+    timed(c, ALBERT_K_FFN1_GELU, s, [&] { gemm_big<T, F8, EPI_GELU>(g, max_rows, c->grid_cap, s); });
 
     g = base;  // FFN 2048 -> 768 + residual + LayerNorm
-    g.X = G; g.ldx = F; g.W = lw.ffn2_w; g.bias = lw.ffn2_b; g.R = X1; g.ldr = H;
-    g.ln_g = lw.ln2_g; g.ln_b = lw.ln2_b; g.Y = X; g.ldy = H; g.N = H; g.K = F;
-    timed(c, ALBERT_K_FFN2_LN, s, [&] { gemm_ln<T>(g, max_rows, c->grid_cap, s); });
+    g.X = G; g.ldx = F; g.W = lw.ffn2_w; g.wexp = lw.ffn2_e; g.bias = lw.ffn2_b; g.R = X1;
+    g.ldr = H; g.ln_g = lw.ln2_g; g.ln_b = lw.ln2_b; g.Y = X; g.ldy = H; g.Y8 = Y8; g.ldy8 = H;
+    g.N = H; g.K = F;
+    timed(c, ALBERT_K_FFN2_LN, s, [&] { gemm_ln<T, F8>(g, max_rows, c->grid_cap, s); });
   }
 
   g = base;  // output projection H -> 512, fp32, into the caller's rows
-  g.X = X; g.ldx = H; g.W = c->out_w; g.bias = c->out_b; g.out = out;
+  g.X = X8; g.ldx = H; g.W = c->out_w; g.wexp = c->out_e; g.bias = c->out_b; g.out = out;
   g.row_seq = row_seq; g.row_pos = row_pos; g.out_T = pad_T; g.N = cf.out_dim; g.K = H;
-  timed(c, ALBERT_K_OUT, s, [&] { gemm_big<T, EPI_OUT>(g, max_rows, c->grid_cap, s); });
+  timed(c, ALBERT_K_OUT, s, [&] { gemm_big<T, F8, EPI_OUT>(g, max_rows, c->grid_cap, s); });
   if (pad_T)
     hipLaunchKernelGGL(zero_pad_rows_kernel, dim3(n_seq), dim3(256), 0, s, out, cu, pad_T,
                        cf.out_dim, status);
   return hipGetLastError() == hipSuccess ? ALBERT_OK : ALBERT_E_HIP;
+}
+
+// Dispatch on the context's dtype.
+template <typename... A>
+int run_any(albert_ctx* c, A... args) {
+  switch (c->dtype) {
+    case ALBERT_BF16: return run<bf16, false>(c, args...);
+    case ALBERT_FP8: return run<bf16, true>(c, args...);
+    default: return run<float, false>(c, args...);
+  }
 }
 
 int finish(int rc, const void* ws, hipStream_t s, unsigned flags) {
@@ -315,10 +393,13 @@ int albert_load_weights(albert_ctx** out_ctx, const albert_config* cfg,
                         const float* const* host, int dtype, void* stream) {
   if (!out_ctx) return ALBERT_E_ARG;
   *out_ctx = nullptr;
-  if (!cfg || !host || !config_ok(*cfg) || (dtype != ALBERT_F32 && dtype != ALBERT_BF16))
+  if (!cfg || !host || !config_ok(*cfg) ||
+      (dtype != ALBERT_F32 && dtype != ALBERT_BF16 && dtype != ALBERT_FP8))
     return ALBERT_E_ARG;
   const albert_config c = *cfg;
-  const size_t es = dtype == ALBERT_BF16 ? 2 : 4;
+  const bool f8 = dtype == ALBERT_FP8;
+  const size_t es = store_bytes(dtype);   // tables
+  const size_t em = operand_bytes(dtype); // weight matrices
   const int G = c.n_groups, NT = 9 + ALBERT_LAYER_TENSORS * G;
   std::vector<int64_t> rows(NT), cols(NT);
   for (int i = 0; i < NT; ++i) {
@@ -331,10 +412,13 @@ int albert_load_weights(albert_ctx** out_ctx, const albert_config* cfg,
 
   // Device image: segments in the order below, each 256-byte aligned.
   // Per weight set: Q|K|V packed into one [3H, H] matrix (queries scaled)
-  // and one [3H] bias, then o, attn LN, ffn1, ffn2, ffn LN.
-  enum { S_WORD, S_POS, S_TYPE, S_EMB_G, S_EMB_B, S_PROJ_W, S_PROJ_B, S_OUT_W, S_OUT_B, S_LAYER0 };
+  // and one [3H] bias, then o, attn LN, ffn1, ffn2, ffn LN.  Under
+  // ALBERT_FP8 every matrix also has a segment of per-row E8M0 exponents
+  // (empty otherwise).
+  enum { S_WORD, S_POS, S_TYPE, S_EMB_G, S_EMB_B, S_PROJ_W, S_PROJ_B, S_OUT_W, S_OUT_B,
+         S_PROJ_E, S_OUT_E, S_LAYER0 };
   enum { L_QKV_W, L_QKV_B, L_O_W, L_O_B, L_LN1_G, L_LN1_B, L_F1_W, L_F1_B, L_F2_W, L_F2_B,
-         L_LN2_G, L_LN2_B, L_SEGS };
+         L_LN2_G, L_LN2_B, L_QKV_E, L_O_E, L_F1_E, L_F2_E, L_SEGS };
   struct Seg { size_t off, bytes; };
   std::vector<Seg> seg;
   size_t off = 0;
@@ -344,23 +428,29 @@ int albert_load_weights(albert_ctx** out_ctx, const albert_config* cfg,
   add((size_t)c.n_types * c.emb * es);     // type
   add((size_t)c.emb * 4);                  // emb g
   add((size_t)c.emb * 4);                  // emb b
-  add((size_t)H * c.emb * es);             // proj w
+  add((size_t)H * c.emb * em);             // proj w
   add((size_t)H * 4);                      // proj b
-  add((size_t)c.out_dim * H * es);         // out w
+  add((size_t)c.out_dim * H * em);         // out w
   add((size_t)c.out_dim * 4);              // out b
+  add(f8 ? (size_t)H : 0);                 // proj exponents
+  add(f8 ? (size_t)c.out_dim : 0);         // out exponents
   for (int g = 0; g < G; ++g) {
-    add((size_t)3 * H * H * es);           // qkv w
+    add((size_t)3 * H * H * em);           // qkv w
     add((size_t)3 * H * 4);                // qkv b
-    add((size_t)H * H * es);               // o w
+    add((size_t)H * H * em);               // o w
     add((size_t)H * 4);                    // o b
     add((size_t)H * 4);                    // ln1 g
     add((size_t)H * 4);                    // ln1 b
-    add((size_t)c.ffn * H * es);           // ffn1 w
+    add((size_t)c.ffn * H * em);           // ffn1 w
     add((size_t)c.ffn * 4);                // ffn1 b
-    add((size_t)H * c.ffn * es);           // ffn2 w
+    add((size_t)H * c.ffn * em);           // ffn2 w
     add((size_t)H * 4);                    // ffn2 b
     add((size_t)H * 4);                    // ln2 g
     add((size_t)H * 4);                    // ln2 b
+    add(f8 ? (size_t)3 * H : 0);           // qkv exponents
+    add(f8 ? (size_t)H : 0);               // o exponents
+    add(f8 ? (size_t)c.ffn : 0);           // ffn1 exponents
+    add(f8 ? (size_t)H : 0);               // ffn2 exponents
   }
   std::vector<unsigned char> img(off, 0);
 
@@ -380,33 +470,52 @@ int albert_load_weights(albert_ctx** out_ctx, const albert_config* cfg,
     float* d = reinterpret_cast<float*>(img.data() + seg[s].off) + elem_off;
     for (int64_t e = 0; e < n; ++e) d[e] = src[e] * scale;
   };
+  // A weight matrix [rows, cols] placed at row row_off of segment s: in the
+  // storage dtype, or (ALBERT_FP8) as E4M3 codes of each row times 2^k with
+  // the exponent 127 - k in segment se.
+  auto put_w = [&](int s, int se, const float* src, int64_t rows, int64_t cols, float scale,
+                   int64_t row_off) {
+    if (!f8) {
+      put_mat(s, src, rows * cols, scale, (size_t)(row_off * cols));
+      return;
+    }
+    unsigned char* d = img.data() + seg[s].off + row_off * cols;
+    unsigned char* ex = img.data() + seg[se].off + row_off;
+    for (int64_t r = 0; r < rows; ++r) {
+      const float* row = src + r * cols;
+      const int k = e4m3_row_exp(row, cols, scale);
+      ex[r] = (unsigned char)(127 - k);
+      for (int64_t i = 0; i < cols; ++i)
+        d[r * cols + i] = f32_to_e4m3(std::ldexp((double)(row[i] * scale), k));
+    }
+  };
   const float qscale = 1.0f / std::sqrt((float)c.head_dim);  // 1/8 for head_dim 64
   put_mat(S_WORD, host[0], rows[0] * cols[0], 1.f, 0);
   put_mat(S_POS, host[1], rows[1] * cols[1], 1.f, 0);
   put_mat(S_TYPE, host[2], rows[2] * cols[2], 1.f, 0);
   put_vec(S_EMB_G, host[3], c.emb, 1.f, 0);
   put_vec(S_EMB_B, host[4], c.emb, 1.f, 0);
-  put_mat(S_PROJ_W, host[5], H * c.emb, 1.f, 0);
+  put_w(S_PROJ_W, S_PROJ_E, host[5], H, c.emb, 1.f, 0);
   put_vec(S_PROJ_B, host[6], H, 1.f, 0);
   const int out_i = 7 + ALBERT_LAYER_TENSORS * G;
-  put_mat(S_OUT_W, host[out_i], (int64_t)c.out_dim * H, 1.f, 0);
+  put_w(S_OUT_W, S_OUT_E, host[out_i], c.out_dim, H, 1.f, 0);
   put_vec(S_OUT_B, host[out_i + 1], c.out_dim, 1.f, 0);
   for (int g = 0; g < G; ++g) {
     const float* const* t = host + 7 + ALBERT_LAYER_TENSORS * g;  // q.w .. ffn_ln.b
     const int s0 = S_LAYER0 + L_SEGS * g;
-    put_mat(s0 + L_QKV_W, t[0], H * H, qscale, 0);
-    put_mat(s0 + L_QKV_W, t[2], H * H, 1.f, (size_t)(H * H));
-    put_mat(s0 + L_QKV_W, t[4], H * H, 1.f, (size_t)(2 * H * H));
+    put_w(s0 + L_QKV_W, s0 + L_QKV_E, t[0], H, H, qscale, 0);
+    put_w(s0 + L_QKV_W, s0 + L_QKV_E, t[2], H, H, 1.f, H);
+    put_w(s0 + L_QKV_W, s0 + L_QKV_E, t[4], H, H, 1.f, 2 * H);
     put_vec(s0 + L_QKV_B, t[1], H, qscale, 0);
     put_vec(s0 + L_QKV_B, t[3], H, 1.f, (size_t)H);
     put_vec(s0 + L_QKV_B, t[5], H, 1.f, (size_t)(2 * H));
-    put_mat(s0 + L_O_W, t[6], H * H, 1.f, 0);
+    put_w(s0 + L_O_W, s0 + L_O_E, t[6], H, H, 1.f, 0);
     put_vec(s0 + L_O_B, t[7], H, 1.f, 0);
     put_vec(s0 + L_LN1_G, t[8], H, 1.f, 0);
     put_vec(s0 + L_LN1_B, t[9], H, 1.f, 0);
-    put_mat(s0 + L_F1_W, t[10], (int64_t)c.ffn * H, 1.f, 0);
+    put_w(s0 + L_F1_W, s0 + L_F1_E, t[10], c.ffn, H, 1.f, 0);
     put_vec(s0 + L_F1_B, t[11], c.ffn, 1.f, 0);
-    put_mat(s0 + L_F2_W, t[12], H * c.ffn, 1.f, 0);
+    put_w(s0 + L_F2_W, s0 + L_F2_E, t[12], H, c.ffn, 1.f, 0);
     put_vec(s0 + L_F2_B, t[13], H, 1.f, 0);
     put_vec(s0 + L_LN2_G, t[14], H, 1.f, 0);
     put_vec(s0 + L_LN2_B, t[15], H, 1.f, 0);
@@ -439,6 +548,8 @@ int albert_load_weights(albert_ctx** out_ctx, const albert_config* cfg,
   ctx->emb_g = Pf(S_EMB_G); ctx->emb_b = Pf(S_EMB_B);
   ctx->proj_w = P(S_PROJ_W); ctx->proj_b = Pf(S_PROJ_B);
   ctx->out_w = P(S_OUT_W); ctx->out_b = Pf(S_OUT_B);
+  auto Pe = [&](int sidx) { return (const unsigned char*)(m + seg[sidx].off); };
+  ctx->proj_e = Pe(S_PROJ_E); ctx->out_e = Pe(S_OUT_E);
   ctx->layers.resize(G);
   for (int g = 0; g < G; ++g) {
     const int s0 = S_LAYER0 + L_SEGS * g;
@@ -449,6 +560,8 @@ int albert_load_weights(albert_ctx** out_ctx, const albert_config* cfg,
     lw.ffn1_w = P(s0 + L_F1_W); lw.ffn1_b = Pf(s0 + L_F1_B);
     lw.ffn2_w = P(s0 + L_F2_W); lw.ffn2_b = Pf(s0 + L_F2_B);
     lw.ln2_g = Pf(s0 + L_LN2_G); lw.ln2_b = Pf(s0 + L_LN2_B);
+    lw.qkv_e = Pe(s0 + L_QKV_E); lw.o_e = Pe(s0 + L_O_E);
+    lw.ffn1_e = Pe(s0 + L_F1_E); lw.ffn2_e = Pe(s0 + L_F2_E);
   }
   *out_ctx = ctx;
   return ALBERT_OK;
@@ -473,9 +586,7 @@ int albert_encode(albert_ctx* ctx, const int32_t* ids, const int32_t* lengths, i
       overlaps(out, out_bytes, lengths, (size_t)B * 4) || overlaps(out, out_bytes, ws, need))
     return ALBERT_E_ALIAS;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const int rc = ctx->dtype == ALBERT_BF16
-                     ? run<bf16>(ctx, ids, lengths, B, T, rows, T, out, ws, s)
-                     : run<float>(ctx, ids, lengths, B, T, rows, T, out, ws, s);
+  const int rc = run_any(ctx, ids, lengths, B, T, rows, T, out, ws, s, (const float*)nullptr);
   return finish(rc, ws, s, flags);
 }
 
@@ -494,9 +605,29 @@ int albert_encode_varlen(albert_ctx* ctx, const int32_t* ids, const int32_t* cu_
       overlaps(out, out_bytes, ws, need))
     return ALBERT_E_ALIAS;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const int rc = ctx->dtype == ALBERT_BF16
-                     ? run<bf16>(ctx, ids, cu_seqlens, n, 0, total, max_len, out, ws, s)
-                     : run<float>(ctx, ids, cu_seqlens, n, 0, total, max_len, out, ws, s);
+  const int rc = run_any(ctx, ids, cu_seqlens, n, 0, (int64_t)total, max_len, out, ws, s,
+                         (const float*)nullptr);
+  return finish(rc, ws, s, flags);
+}
+
+int albert_encode_features(albert_ctx* ctx, const float* x, const int32_t* cu_seqlens, int n,
+                           int total, int max_len, float* out, void* ws, size_t ws_bytes,
+                           void* stream, unsigned flags) {
+  if (ctx && n == 0 && total == 0) return ALBERT_OK;  // empty batch
+  if (!ctx || !x || !cu_seqlens || !out || !ws || n < 1 || total < 1 || max_len < 1 ||
+      max_len > ctx->cfg.max_pos || ((uintptr_t)ws % kAlign) != 0 || ((uintptr_t)x % 16) != 0 ||
+      !device_matches(ctx))
+    return ALBERT_E_ARG;
+  const size_t need = plan(ctx, n, total).total;
+  if (ws_bytes < need) return ALBERT_E_WORKSPACE;
+  const size_t out_bytes = (size_t)total * ctx->cfg.out_dim * 4;
+  if (overlaps(out, out_bytes, x, (size_t)total * ctx->cfg.emb * 4) ||
+      overlaps(out, out_bytes, cu_seqlens, (size_t)(n + 1) * 4) ||
+      overlaps(out, out_bytes, ws, need))
+    return ALBERT_E_ALIAS;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int rc = run_any(ctx, (const int32_t*)nullptr, cu_seqlens, n, 0, (int64_t)total, max_len,
+                         out, ws, s, x);
   return finish(rc, ws, s, flags);
 }
 
@@ -514,21 +645,25 @@ int albert_tap(const albert_ctx* ctx, int n_seq, int64_t max_rows, int tap, size
                size_t* bytes, int64_t* row_stride) {
   if (!ctx || !offset || !bytes || !row_stride || n_seq < 1 || max_rows < 1) return ALBERT_E_ARG;
   const Layout L = plan(ctx, n_seq, max_rows);
-  const size_t es = ctx->dtype == ALBERT_BF16 ? 2 : 4;
+  const size_t es = store_bytes(ctx->dtype), eo = operand_bytes(ctx->dtype);
   const albert_config& c = ctx->cfg;
   const size_t R = (size_t)max_rows;
+  if ((tap == ALBERT_TAP_X8 || tap == ALBERT_TAP_X1_8) && ctx->dtype != ALBERT_FP8)
+    return ALBERT_E_ARG;
   switch (tap) {
     case ALBERT_TAP_STATUS: *offset = L.status; *bytes = 4; *row_stride = 0; break;
     case ALBERT_TAP_CU: *offset = L.cu; *bytes = (size_t)(n_seq + 1) * 4; *row_stride = 0; break;
     case ALBERT_TAP_ROW_SEQ: *offset = L.row_seq; *bytes = R * 4; *row_stride = 0; break;
     case ALBERT_TAP_ROW_POS: *offset = L.row_pos; *bytes = R * 4; *row_stride = 0; break;
-    case ALBERT_TAP_EMB: *offset = L.emb; *bytes = R * c.emb * es; *row_stride = c.emb; break;
+    case ALBERT_TAP_EMB: *offset = L.emb; *bytes = R * c.emb * eo; *row_stride = c.emb; break;
     case ALBERT_TAP_X: *offset = L.x; *bytes = R * c.hidden * es; *row_stride = c.hidden; break;
     case ALBERT_TAP_QKV:
       *offset = L.qkv; *bytes = R * 3 * c.hidden * es; *row_stride = 3 * c.hidden; break;
-    case ALBERT_TAP_CTX: *offset = L.ctx; *bytes = R * c.hidden * es; *row_stride = c.hidden; break;
+    case ALBERT_TAP_CTX: *offset = L.ctx; *bytes = R * c.hidden * eo; *row_stride = c.hidden; break;
     case ALBERT_TAP_X1: *offset = L.x1; *bytes = R * c.hidden * es; *row_stride = c.hidden; break;
-    case ALBERT_TAP_G: *offset = L.g; *bytes = R * c.ffn * es; *row_stride = c.ffn; break;
+    case ALBERT_TAP_G: *offset = L.g; *bytes = R * c.ffn * eo; *row_stride = c.ffn; break;
+    case ALBERT_TAP_X8: *offset = L.x8; *bytes = R * c.hidden; *row_stride = c.hidden; break;
+    case ALBERT_TAP_X1_8: *offset = L.x18; *bytes = R * c.hidden; *row_stride = c.hidden; break;
     default: return ALBERT_E_ARG;
   }
   return ALBERT_OK;

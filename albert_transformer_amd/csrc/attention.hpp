@@ -14,7 +14,8 @@
 // and 16 keys of every 32-key block: the running max and sum of the online
 // softmax need only the partner half-wave, and the probabilities feed the
 // second MFMA (O^T = V^T P^T) directly from registers, with V^T read from
-// LDS in the matching key order.
+// LDS in the matching key order.  With F8 the context is written as E4M3
+// codes (its one consumer is the output projection's matrix product).
 #pragma once
 
 #include "common.hpp"
@@ -23,12 +24,12 @@ namespace albert {
 
 struct AttnArgs {
   const void* qkv;    // [M, 3H]: q*(1/8) | k | v, head h at h*64
-  void* ctx;          // [M, H]
+  void* ctx;          // [M, H] (T, or E4M3 codes)
   const int* cu;      // [n_seq + 1]
   const int* status;
 };
 
-template <typename T>
+template <typename T, bool F8>
 __global__ void __launch_bounds__(256)
 attention_kernel(AttnArgs a) {
   typedef Tr<T> TR;
@@ -142,14 +143,14 @@ attention_kernel(AttnArgs a) {
   lrun += wave_xor(lrun, 32);
   if (qi >= L) return;
   const float inv = 1.0f / lrun;
-  T* __restrict__ out = static_cast<T*>(a.ctx) + ((int64_t)start + qi) * H + h * D;
+  const int64_t orow = ((int64_t)start + qi) * H + h * D;
 #pragma unroll
   for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int d = dt * 32 + 8 * q + 4 * hh;
-      TR::store4(out + d, o[dt][4 * q + 0] * inv, o[dt][4 * q + 1] * inv,
-                 o[dt][4 * q + 2] * inv, o[dt][4 * q + 3] * inv);
+      store4_as<T, F8>(a.ctx, orow + d, o[dt][4 * q + 0] * inv, o[dt][4 * q + 1] * inv,
+                       o[dt][4 * q + 2] * inv, o[dt][4 * q + 3] * inv);
     }
 }
 

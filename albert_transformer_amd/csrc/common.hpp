@@ -1,7 +1,9 @@
 // Device-side building blocks shared by the encoder's HIP kernels (gfx950).
 //
 // Storage types: __bf16 (the production path) or float (the fp32 debug
-// path).  All arithmetic outside the matrix cores is fp32.
+// path); the low-precision variant keeps bf16 storage and feeds the matrix
+// products OCP FP8 E4M3 operands.  All arithmetic outside the matrix cores
+// is fp32.
 //
 // Matrix-core conventions used by every kernel here (CDNA 32x32 MFMA):
 //   D[32x32] += A[32xK] * B[Kx32], wave64.
@@ -15,6 +17,10 @@
 //   8*(r/4) + 4*h + (r%4).
 //   bf16: one v_mfma_f32_32x32x16_bf16 per K step of 16.
 //   fp32: eight v_mfma_f32_32x32x2_f32, element s of each lane in the s-th.
+//   E4M3: one v_mfma_scale_f32_32x32x64_f8f6f4 per K step of 64, each lane
+//   supplying 32 consecutive elements (again any k permutation shared by A
+//   and B is harmless); A's per-lane E8M0 scale multiplies its row by a
+//   power of two.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -27,6 +33,8 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned char fp8;  // one OCP FP8 E4M3 code
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegInf = -__builtin_inff();
@@ -125,6 +133,41 @@ template <> struct Tr<float> {
     return *reinterpret_cast<const f32x4*>(p);
   }
 };
+
+template <> struct Tr<fp8> {
+  typedef i32x8 frag;  // 32 E4M3 codes: one lane's share of a 64-deep K step
+  static __device__ __forceinline__ frag load2(const fp8* p0, const fp8* p1) {
+    const int4 a = *reinterpret_cast<const int4*>(p0);
+    const int4 b = *reinterpret_cast<const int4*>(p1);
+    frag f;
+    f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
+    f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+    return f;
+  }
+  // c += (A * 2^(sa - 127)) * B with E4M3 A and B (format code 0 for both);
+  // sa is the E8M0 exponent of this lane's A row, B is unscaled (127).
+  static __device__ __forceinline__ void mma_s(f32x16& c, const frag& a, const frag& b, int sa) {
+    c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, sa, 0, 127);
+  }
+};
+
+// Four fp32 values -> four E4M3 codes in memory order, rounding to nearest
+// even; magnitudes beyond 448 (the largest finite code) saturate first.
+__device__ __forceinline__ uint32_t pack_e4m3x4(float a, float b, float c, float d) {
+  const float lo = -448.f, hi = 448.f;
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(fminf(fmaxf(a, lo), hi), fminf(fmaxf(b, lo), hi), 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(fminf(fmaxf(c, lo), hi), fminf(fmaxf(d, lo), hi), w, true);
+  return (uint32_t)w;
+}
+
+// Store four values at element idx of an array of T, or of E4M3 codes.
+template <typename T, bool F8>
+__device__ __forceinline__ void store4_as(void* base, int64_t idx, float a, float b, float c, float d) {
+  if constexpr (F8)
+    *reinterpret_cast<uint32_t*>(static_cast<fp8*>(base) + idx) = pack_e4m3x4(a, b, c, d);
+  else
+    Tr<T>::store4(static_cast<T*>(base) + idx, a, b, c, d);
+}
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 

@@ -42,6 +42,14 @@
 // numbered so that each XCD (workgroups are dealt to the 8 XCDs
 // round-robin) gets a contiguous range, features fastest, so blocks running
 // together on one XCD share X rows and weight columns in that XCD's L2.
+//
+// Low precision (F8).  X and W are OCP FP8 E4M3 codes and each weight row
+// carries a power-of-two scale (an E8M0 exponent, applied by the matrix
+// core as A's per-row scale, so the product is exact up to accumulation).
+// Outputs keep the storage type T except the GELU output, whose only
+// consumer is the next product (E4M3); the bias and LayerNorm epilogues can
+// also write an E4M3 copy of their output (Y8) for the next product while Y
+// stays the bf16 residual stream.
 #pragma once
 
 #include <type_traits>
@@ -56,9 +64,12 @@ struct GemmArgs {
   const void* X;       // [M, K] activations, row stride ldx (elements)
   int64_t ldx;
   const void* W;       // [N, K] weights, row stride K
+  const unsigned char* wexp;  // F8: [N] E8M0 exponent of each weight row
   const float* bias;   // [N]
   void* Y;             // [M, N] output (EPI_BIAS / EPI_GELU / EPI_LN), stride ldy
   int64_t ldy;
+  void* Y8;            // F8, EPI_BIAS (not deferred) / EPI_LN: E4M3 copy of Y, or null
+  int64_t ldy8;
   const void* R;       // [M, N] residual (EPI_LN), stride ldr
   int64_t ldr;
   const float* ln_g;   // [N] (EPI_LN)
@@ -89,36 +100,47 @@ __device__ __forceinline__ int swz_key(int row) {
 // then meet the other waves of the block.
 #define ALBERT_WAIT_BARRIER(N) asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory")
 
-template <typename T, int BM, int BN, int WGM, int WGN, int RB, int STAGES, int EPI, bool DEFER>
+template <typename T, bool F8, int BM, int BN, int WGM, int WGN, int RB, int STAGES, int EPI,
+          bool DEFER>
 __global__ void __launch_bounds__(WGM * WGN * 64)
 gemm_kernel(GemmArgs g) {
-  typedef Tr<T> TR;
+  typedef typename std::conditional<F8, fp8, T>::type TO;  // operand codes
+  typedef Tr<TO> TR;                                         // operand fragments
+  typedef Tr<T> TS;                                          // storage
+  constexpr int ES = sizeof(TO);
   constexpr int NW = WGM * WGN;
   constexpr int NT = NW * 64;
-  constexpr int CH = 16 / sizeof(T);          // elements per 16-byte chunk
+  constexpr int CH = 16 / ES;                 // elements per 16-byte chunk
   constexpr int CPR = RB / 16;                // chunks per staged row
-  constexpr int BK = RB / sizeof(T);          // K elements per slice
+  constexpr int BK = RB / ES;                 // K elements per slice
+  constexpr int KS = F8 ? 64 : 16;            // K per MFMA step
+  constexpr int FE = F8 ? 32 : 8;             // elements per lane per step
+  constexpr bool YF8 = F8 && EPI == EPI_GELU; // output stored as E4M3 codes
+  constexpr int YES = YF8 ? 1 : (int)sizeof(T);
   constexpr int RPI = 1024 / RB;              // rows one DMA instruction fills
   constexpr int NINST = (BM + BN) / RPI;      // DMA instructions per slice
   constexpr int IPW = NINST / NW;             // ... per wave
   constexpr int STAGE = (BM + BN) * RB;       // bytes per slice
   constexpr int WTM = BM / WGM, WTN = BN / WGN;
   constexpr int TM = WTM / 32, TN = WTN / 32;
-  constexpr int KSTEPS = BK / 16;             // MFMA k-steps per slice
-  constexpr int FCH = 8 / CH;                 // chunks per fragment (1 bf16, 2 fp32)
+  constexpr int KSTEPS = BK / KS;             // MFMA k-steps per slice
+  constexpr int FCH = FE / CH;                // chunks per fragment (1 bf16, 2 fp32 / E4M3)
   constexpr int NVEC = EPI == EPI_LN ? 3 : 1; // bias (+ LayerNorm gain, shift)
   constexpr int VPT = (BN + NT - 1) / NT;     // vector elements per thread
   static_assert(NINST % NW == 0, "DMA split");
   static_assert((BM / RPI) % NW == 0, "each DMA slot must be all-X or all-W");
   static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be 32-aligned");
   static_assert(RB == 64 || RB == 128, "row bytes");
+  static_assert(KSTEPS >= 1, "slice shorter than one MFMA step");
   static_assert(STAGES >= 2 && STAGES <= 4, "stages");
   static_assert(IPW * (STAGES - 2) <= 63, "vmcnt range");
   static_assert(CPR == 8 ? (NW % 2 == 0) : true, "swizzle key must not depend on i");
-  // Deferred stores: bf16 outputs of tile i are kept in registers and written
-  // in NB batches of SB stores during the first NB K-slices of tile i+1.
-  constexpr int NST = TM * TN * 4;            // 8-byte stores per lane per tile
+  // Deferred stores: bf16 (or E4M3) outputs of tile i are kept in registers
+  // and written in NB batches of SB stores during the first NB K-slices of
+  // tile i+1.
+  constexpr int NST = TM * TN * 4;            // 8- (4-) byte stores per lane per tile
   constexpr int NB = 8, SB = NST / NB;
+  constexpr int HW = YF8 ? 1 : 2;             // 32-bit words per store
   static_assert(!DEFER || (std::is_same<T, bf16>::value && STAGES == 2 &&
                            (EPI == EPI_BIAS || EPI == EPI_GELU) && NST % NB == 0 &&
                            SB <= 63 && TN % (NB / TM) == 0),
@@ -151,19 +173,26 @@ gemm_kernel(GemmArgs g) {
   // ------------------------------------------------------- per-tile state
   int m0 = 0, n0 = 0;
   __amdgpu_buffer_rsrc_t xr, wr;
+  int sc[TN];  // F8: E8M0 exponents of this lane's weight rows
+#pragma unroll
+  for (int j = 0; j < TN; ++j) sc[j] = 127;
   // Buffer resources over the tile's rows: the hardware range check turns
   // reads of X rows at or past M into zeros (their results are never stored).
   auto setup = [&](int t) __attribute__((always_inline)) {
     m0 = (t / g.n_tiles) * BM;
     n0 = (t % g.n_tiles) * BN;
-    const char* Xt = static_cast<const char*>(g.X) + (int64_t)m0 * g.ldx * (int64_t)sizeof(T);
-    const char* Wt = static_cast<const char*>(g.W) + (int64_t)n0 * g.K * (int64_t)sizeof(T);
-    const int64_t xbytes = (int64_t)(M - m0) * g.ldx * (int64_t)sizeof(T);
-    const int64_t wbytes = (int64_t)(g.N - n0) * g.K * (int64_t)sizeof(T);
+    const char* Xt = static_cast<const char*>(g.X) + (int64_t)m0 * g.ldx * (int64_t)ES;
+    const char* Wt = static_cast<const char*>(g.W) + (int64_t)n0 * g.K * (int64_t)ES;
+    const int64_t xbytes = (int64_t)(M - m0) * g.ldx * (int64_t)ES;
+    const int64_t wbytes = (int64_t)(g.N - n0) * g.K * (int64_t)ES;
     const int xrec = __builtin_amdgcn_readfirstlane((int)(xbytes > 0x7fffffff ? 0x7fffffff : xbytes));
     const int wrec = __builtin_amdgcn_readfirstlane((int)(wbytes > 0x7fffffff ? 0x7fffffff : wbytes));
     xr = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(Xt), (short)0, xrec, kRsrcWord3);
     wr = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(Wt), (short)0, wrec, kRsrcWord3);
+    if constexpr (F8) {
+#pragma unroll
+      for (int j = 0; j < TN; ++j) sc[j] = g.wexp[n0 + wn * WTN + j * 32 + l32];
+    }
   };
 
   // DMA sources.  Instruction i of this wave fills rows q*RPI .. q*RPI+RPI-1
@@ -174,12 +203,12 @@ gemm_kernel(GemmArgs g) {
   // every load.
   const int lrow = lane / CPR;
   const int lchunk = (lane % CPR) ^ swz_key<RB>(wave * RPI + lrow);
-  const int xoff = lrow * (int)g.ldx * (int)sizeof(T) + lchunk * 16;
-  const int woff = lrow * g.K * (int)sizeof(T) + lchunk * 16;
-  const int xrow_b = (int)g.ldx * (int)sizeof(T);  // bytes per X row
-  const int wrow_b = g.K * (int)sizeof(T);
+  const int xoff = lrow * (int)g.ldx * ES + lchunk * 16;
+  const int woff = lrow * g.K * ES + lchunk * 16;
+  const int xrow_b = (int)g.ldx * ES;  // bytes per X row
+  const int wrow_b = g.K * ES;
   auto issue = [&](char* buf, int k0) __attribute__((always_inline)) {
-    int kb = k0 * (int)sizeof(T);
+    int kb = k0 * ES;
     // keep the per-slice offset opaque so the compiler does not precompute
     // (and keep live) every slice's per-instruction offsets
     asm volatile("" : "+s"(kb));
@@ -238,7 +267,7 @@ gemm_kernel(GemmArgs g) {
 #pragma unroll
   for (int j = 0; j < KSTEPS; ++j)
 #pragma unroll
-    for (int f = 0; f < FCH; ++f) coff[j][f] = (((j * 16 + hh * 8) / CH + f) ^ key) * 16;
+    for (int f = 0; f < FCH; ++f) coff[j][f] = (((j * KS + hh * FE) / CH + f) ^ key) * 16;
 
   f32x16 acc[TM][TN];
 
@@ -246,7 +275,7 @@ gemm_kernel(GemmArgs g) {
   // they belong to (rows at or past M fall outside it and are dropped by the
   // hardware range check, so every batch issues the same number of stores),
   // and per-row byte offsets.  Before the first tile the resource is empty.
-  uint32_t held[DEFER ? TM : 1][DEFER ? TN : 1][4][2];
+  uint32_t held[DEFER ? TM : 1][DEFER ? TN : 1][4][HW];
   __amdgpu_buffer_rsrc_t yr = __builtin_amdgcn_make_buffer_rsrc(g.Y, (short)0, 0, kRsrcWord3);
   int hoff[TM];
 #pragma unroll
@@ -257,7 +286,9 @@ gemm_kernel(GemmArgs g) {
 #pragma unroll
       for (int j = 0; j < TN; ++j)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) held[i][j][q][0] = held[i][j][q][1] = 0u;
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int w = 0; w < HW; ++w) held[i][j][q][w] = 0u;
   }
   // batch b: token tile i = b / (NB/TM), column tiles j in [jb, jb + TN/(NB/TM))
   auto store_batch = [&](int b) __attribute__((always_inline)) {
@@ -268,9 +299,14 @@ gemm_kernel(GemmArgs g) {
       for (int jj = 0; jj < JPB; ++jj)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-          u32x2 v = {held[i][jb + jj][q][0], held[i][jb + jj][q][1]};
-          __builtin_amdgcn_raw_buffer_store_b64(v, yr, hoff[i] + ((jb + jj) * 32 + 8 * q) * 2, 0, 0);
+          const int off = hoff[i] + ((jb + jj) * 32 + 8 * q) * YES;
+          if constexpr (HW == 2) {
+            typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+            u32x2 v = {held[i][jb + jj][q][0], held[i][jb + jj][q][1]};
+            __builtin_amdgcn_raw_buffer_store_b64(v, yr, off, 0, 0);
+          } else {
+            __builtin_amdgcn_raw_buffer_store_b32(held[i][jb + jj][q][0], yr, off, 0, 0);
+          }
         }
     }
   };
@@ -281,38 +317,73 @@ gemm_kernel(GemmArgs g) {
   // waves per SIMD (8 waves) have half the registers per wave, so they read
   // each k-step's fragments right before use instead.
   constexpr int PF = (NW <= 4 && !DEFER) ? 2 : 1;
-  auto compute = [&](const char* buf) __attribute__((always_inline)) {
-    typename TR::frag fx[PF][TM], fw[PF][TN];
-    auto ld = [&](int j, int b) __attribute__((always_inline)) {
-#pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        const char* p = buf + xrow + i * 32 * RB;
-        fx[b][i] = TR::load2(reinterpret_cast<const T*>(p + coff[j][0]),
-                             reinterpret_cast<const T*>(p + coff[j][FCH - 1]));
-      }
-#pragma unroll
-      for (int jj = 0; jj < TN; ++jj) {
-        const char* p = buf + wrow + jj * 32 * RB;
-        fw[b][jj] = TR::load2(reinterpret_cast<const T*>(p + coff[j][0]),
-                              reinterpret_cast<const T*>(p + coff[j][FCH - 1]));
-      }
+  // E4M3 fragments are twice as wide (8 VGPRs): a slice is one 64-deep
+  // step; the fragments of the shorter side (token or weight tiles) stay in
+  // registers while those of the longer side stream through two register
+  // sets.
+  auto compute_f8 = [&](const char* buf) __attribute__((always_inline)) {
+    constexpr bool ROWS_RESIDENT = TM <= TN;  // stream weight fragments
+    constexpr int NR = ROWS_RESIDENT ? TM : TN, NS = ROWS_RESIDENT ? TN : TM;
+    typename TR::frag fr[NR], fs[2];
+    auto ldf = [&](bool tok, int t) __attribute__((always_inline)) {
+      const char* p = buf + (tok ? xrow : wrow) + t * 32 * RB;
+      return TR::load2(reinterpret_cast<const TO*>(p + coff[0][0]),
+                       reinterpret_cast<const TO*>(p + coff[0][FCH - 1]));
     };
-    if constexpr (PF == 2) ld(0, 0);
 #pragma unroll
-    for (int j = 0; j < KSTEPS; ++j) {
-      if constexpr (PF == 2) {
-        if (j + 1 < KSTEPS) ld(j + 1, (j + 1) & 1);
-      } else {
-        ld(j, 0);
+    for (int r = 0; r < NR; ++r) fr[r] = ldf(ROWS_RESIDENT, r);
+    fs[0] = ldf(!ROWS_RESIDENT, 0);
+#pragma unroll
+    for (int t = 0; t < NS; ++t) {
+      if (t + 1 < NS) fs[(t + 1) & 1] = ldf(!ROWS_RESIDENT, t + 1);
+#pragma unroll
+      for (int r = 0; r < NR; ++r) {
+        const int i = ROWS_RESIDENT ? r : t, jj = ROWS_RESIDENT ? t : r;
+        const typename TR::frag& fx = ROWS_RESIDENT ? fr[r] : fs[t & 1];
+        const typename TR::frag& fw = ROWS_RESIDENT ? fs[t & 1] : fr[r];
+        if constexpr (F8) TR::mma_s(acc[i][jj], fw, fx, sc[jj]);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // then one LDS read
       }
+    }
+  };
+  auto compute = [&](const char* buf) __attribute__((always_inline)) {
+    if constexpr (F8) {
+      static_assert(KSTEPS == 1, "E4M3 slices hold one MFMA step");
+      compute_f8(buf);
+    } else {
+      typename TR::frag fx[PF][TM], fw[PF][TN];
+      auto ld = [&](int j, int b) __attribute__((always_inline)) {
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
+        for (int i = 0; i < TM; ++i) {
+          const char* p = buf + xrow + i * 32 * RB;
+          fx[b][i] = TR::load2(reinterpret_cast<const TO*>(p + coff[j][0]),
+                               reinterpret_cast<const TO*>(p + coff[j][FCH - 1]));
+        }
 #pragma unroll
         for (int jj = 0; jj < TN; ++jj) {
-          TR::mma(acc[i][jj], fw[j % PF][jj], fx[j % PF][i]);
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // then one LDS read
+          const char* p = buf + wrow + jj * 32 * RB;
+          fw[b][jj] = TR::load2(reinterpret_cast<const TO*>(p + coff[j][0]),
+                                reinterpret_cast<const TO*>(p + coff[j][FCH - 1]));
         }
+      };
+      if constexpr (PF == 2) ld(0, 0);
+#pragma unroll
+      for (int j = 0; j < KSTEPS; ++j) {
+        if constexpr (PF == 2) {
+          if (j + 1 < KSTEPS) ld(j + 1, (j + 1) & 1);
+        } else {
+          ld(j, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int jj = 0; jj < TN; ++jj) {
+            TR::mma(acc[i][jj], fw[j % PF][jj], fx[j % PF][i]);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // then one LDS read
+          }
+      }
     }
   };
 
@@ -336,7 +407,7 @@ gemm_kernel(GemmArgs g) {
         for (int j = 0; j < TN; ++j) {
           f32x4 rv[4];  // this column group's residual loads first, then one wait
 #pragma unroll
-          for (int q = 0; q < 4; ++q) rv[q] = TR::load4f(rrow + j * 32 + 8 * q);
+          for (int q = 0; q < 4; ++q) rv[q] = TS::load4f(rrow + j * 32 + 8 * q);
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const int nl = wn * WTN + j * 32 + 8 * q + 4 * hh;
@@ -393,21 +464,23 @@ gemm_kernel(GemmArgs g) {
 #pragma unroll
             for (int e = 0; e < 4; ++e)
               o[e] = (acc[i][j][4 * q + e] - mean[i]) * rstd * g_s[nl + e] + b_s[nl + e];
-            TR::store4(Y + (int64_t)m * g.ldy + en0 + nl, o[0], o[1], o[2], o[3]);
+            TS::store4(Y + (int64_t)m * g.ldy + en0 + nl, o[0], o[1], o[2], o[3]);
+            if constexpr (F8)
+              store4_as<T, true>(g.Y8, (int64_t)m * g.ldy8 + en0 + nl, o[0], o[1], o[2], o[3]);
           }
       }
       // the next tile's epilogue reuses `red`: everyone has read it
       asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     } else if constexpr (DEFER) {
       // pack into registers; stored during the next tile's K loop
-      char* ybase = static_cast<char*>(g.Y) + ((int64_t)em0 * g.ldy + en0) * (int64_t)sizeof(T);
-      const int64_t ybytes = (int64_t)(M - em0) * g.ldy * (int64_t)sizeof(T);
+      char* ybase = static_cast<char*>(g.Y) + ((int64_t)em0 * g.ldy + en0) * (int64_t)YES;
+      const int64_t ybytes = (int64_t)(M - em0) * g.ldy * (int64_t)YES;
       yr = __builtin_amdgcn_make_buffer_rsrc(
           ybase, (short)0,
           __builtin_amdgcn_readfirstlane((int)(ybytes > 0x7fffffff ? 0x7fffffff : ybytes)), kRsrcWord3);
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
-        hoff[i] = ((wm * WTM + i * 32 + l32) * (int)g.ldy + wn * WTN + 4 * hh) * (int)sizeof(T);
+        hoff[i] = ((wm * WTM + i * 32 + l32) * (int)g.ldy + wn * WTN + 4 * hh) * YES;
 #pragma unroll
         for (int j = 0; j < TN; ++j)
 #pragma unroll
@@ -419,10 +492,14 @@ gemm_kernel(GemmArgs g) {
               o[e] = acc[i][j][4 * q + e] + bias_s[nl + e];
               if constexpr (EPI == EPI_GELU) o[e] = gelu_tanh(o[e]);
             }
-            typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-            bf16x2 p0 = {(bf16)o[0], (bf16)o[1]}, p1 = {(bf16)o[2], (bf16)o[3]};
-            held[i][j][q][0] = __builtin_bit_cast(uint32_t, p0);
-            held[i][j][q][1] = __builtin_bit_cast(uint32_t, p1);
+            if constexpr (YF8) {
+              held[i][j][q][0] = pack_e4m3x4(o[0], o[1], o[2], o[3]);
+            } else {
+              typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+              bf16x2 p0 = {(bf16)o[0], (bf16)o[1]}, p1 = {(bf16)o[2], (bf16)o[3]};
+              held[i][j][q][0] = __builtin_bit_cast(uint32_t, p0);
+              held[i][j][q][HW - 1] = __builtin_bit_cast(uint32_t, p1);
+            }
           }
       }
     } else {
@@ -448,7 +525,10 @@ gemm_kernel(GemmArgs g) {
             if constexpr (EPI == EPI_OUT) {
               *reinterpret_cast<f32x4*>(g.out + orow * g.N + en0 + nl) = f32x4{o[0], o[1], o[2], o[3]};
             } else {
-              TR::store4(static_cast<T*>(g.Y) + orow * g.ldy + en0 + nl, o[0], o[1], o[2], o[3]);
+              store4_as<T, YF8>(g.Y, orow * g.ldy + en0 + nl, o[0], o[1], o[2], o[3]);
+              if constexpr (F8 && EPI == EPI_BIAS) {
+                if (g.Y8) store4_as<T, true>(g.Y8, orow * g.ldy8 + en0 + nl, o[0], o[1], o[2], o[3]);
+              }
             }
           }
       }

@@ -101,14 +101,15 @@ rows_ids_kernel(const int* __restrict__ ids, const int* __restrict__ cu, int pad
 
 // Three-table embedding + LayerNorm over E = 128 ("Inside One Real ALBERT
 // Layer", step 1): e = word[id] + pos[t] + type[0]; LN with the given eps.
-// 16 lanes per row, 8 channels per lane; fp32 arithmetic, output in T.
-template <typename T>
+// 16 lanes per row, 8 channels per lane; fp32 arithmetic, output in T (or
+// as E4M3 codes when F8: the output only feeds the projection's product).
+template <typename T, bool F8>
 __global__ void __launch_bounds__(256)
 embed_ln_kernel(const int* __restrict__ ids, int pad_T, const int* __restrict__ row_seq,
                 const int* __restrict__ row_pos, const int* __restrict__ m_ptr,
                 const T* __restrict__ word, const T* __restrict__ pos, const T* __restrict__ type,
                 const float* __restrict__ g, const float* __restrict__ bta, float eps,
-                T* __restrict__ out, const int* __restrict__ status) {
+                void* __restrict__ out, const int* __restrict__ status) {
   constexpr int E = 128;
   if (*status != ST_OK) return;
   const int M = *m_ptr;
@@ -139,16 +140,32 @@ embed_ln_kernel(const int* __restrict__ ids, int pad_T, const int* __restrict__ 
 #pragma unroll
   for (int m = 8; m >= 1; m >>= 1) s2 += __shfl_xor(s2, m, 16);
   const float rstd = 1.0f / sqrtf(s2 * (1.0f / E) + eps);
-  T* o = out + (int64_t)r * E + c0;
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
     const int c = c0 + 4 * q;
-    Tr<T>::store4(o + 4 * q,
-                  v[4 * q + 0] * rstd * g[c + 0] + bta[c + 0],
-                  v[4 * q + 1] * rstd * g[c + 1] + bta[c + 1],
-                  v[4 * q + 2] * rstd * g[c + 2] + bta[c + 2],
-                  v[4 * q + 3] * rstd * g[c + 3] + bta[c + 3]);
+    store4_as<T, F8>(out, (int64_t)r * E + c,
+                     v[4 * q + 0] * rstd * g[c + 0] + bta[c + 0],
+                     v[4 * q + 1] * rstd * g[c + 1] + bta[c + 1],
+                     v[4 * q + 2] * rstd * g[c + 2] + bta[c + 2],
+                     v[4 * q + 3] * rstd * g[c + 3] + bta[c + 3]);
   }
+}
+
+// Caller-supplied embedding LayerNorm output (fp32 [M, 128], packed rows)
+// converted to the projection's operand type: the split in which the
+// embedding runs elsewhere and the encoder block starts at the projection
+// ("Kokoro-82M-encoder-hailo10h", "What this is not").  Four channels per
+// thread.
+template <typename T, bool F8>
+__global__ void __launch_bounds__(256)
+features_in_kernel(const float* __restrict__ x, const int* __restrict__ m_ptr,
+                   void* __restrict__ out, const int* __restrict__ status) {
+  constexpr int E = 128;
+  if (*status != ST_OK) return;
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i >= (int64_t)(*m_ptr) * E) return;
+  const f32x4 v = *reinterpret_cast<const f32x4*>(x + i);
+  store4_as<T, F8>(out, i, v[0], v[1], v[2], v[3]);
 }
 
 // Padded output: rows t >= lengths[b] of out[B, T, n_out] are set to 0.

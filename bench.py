@@ -35,6 +35,8 @@ import synth  # noqa: E402
 METRIC = "encoded phoneme tokens/sec at B=256,T=128 bf16; % of MFMA roofline"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA (vendor figure)
 PEAK_F32_TFLOPS = 157.3     # MI355X dense fp32 MFMA
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA (vendor figure)
+PEAKS = {"bf16": PEAK_BF16_TFLOPS, "f32": PEAK_F32_TFLOPS, "fp8": PEAK_FP8_TFLOPS}
 H, E, F, O, NITER = 768, 128, 2048, 512, 12
 
 
@@ -83,12 +85,13 @@ def traffic_for(kind: str, config: int):
     return rec["fetch_bytes"] + rec["write_bytes"]
 
 
-def cpu_baseline(wl, got, budget_s: float, cfg=synth.KOKORO, weights=None):
+def cpu_baseline(wl, got, budget_s: float, cfg=synth.KOKORO, weights=None, dtype=None):
     """Time the float64 oracle on this host over whole sequences of the same
     workload until `budget_s` seconds have passed; compare the GPU rows."""
     import oracle
     from threadpoolctl import threadpool_info
-    W = oracle.prepare_weights(synth.make_weights() if weights is None else weights, wl.dtype)
+    dtype = wl.dtype if dtype is None else dtype
+    W = oracle.prepare_weights(synth.make_weights() if weights is None else weights, dtype)
     threads = max([i.get("num_threads", 1) for i in threadpool_info()
                    if i.get("user_api") == "blas"] or [1])
     order = np.random.default_rng(7).permutation(wl.n_seq)
@@ -101,7 +104,10 @@ def cpu_baseline(wl, got, budget_s: float, cfg=synth.KOKORO, weights=None):
             ids, rows = wl.ids[a:a + L], got[a:a + L]
         else:
             ids, rows = wl.ids[s, :L], got[s, :L]
-        ref = oracle.encode_sequence(ids, W, cfg)
+        if dtype == "fp8":  # the variant's own definition (its storage roundings)
+            ref = oracle.encode_fp8_features(oracle.embed_ln(ids, W, cfg), W, cfg)
+        else:
+            ref = oracle.encode_sequence(ids, W, cfg)
         tokens += L
         done += 1
         d = rows.astype(np.float64) - ref
@@ -153,6 +159,32 @@ def measure_length_regulation(steps: int = 20) -> dict:
                          "frac": round(nbytes / (ms * 1e-3) / 1e9 / 8000.0, 4)}}
 
 
+def hailo_fidelity(enc, cfg, weights, n: int = 16) -> dict:
+    """The Hailo card's fidelity method: n N(0,1) inputs [128,128] at the
+    LayerNorm output, per-sample cosine and MSE of the flattened [128,512]
+    output against full precision (the float64 oracle, unrounded weights)."""
+    import torch
+    import oracle
+    W64 = oracle.prepare_weights(weights, "f32")
+    x = np.random.default_rng(2024).normal(0, 1, (n * 128, 128))
+    cu = torch.from_numpy(np.arange(0, (n + 1) * 128, 128, dtype=np.int32)).cuda()
+    got = enc.encode_features(torch.from_numpy(x.astype(np.float32)).cuda(), cu, 128)
+    got = got.cpu().numpy().astype(np.float64)
+    cos, mse, lo, hi = [], [], [], []
+    for s in range(n):
+        sl = slice(128 * s, 128 * (s + 1))
+        ref = oracle.encode_features(x[sl], W64, cfg)
+        g = got[sl]
+        cos.append(float((g * ref).sum() / np.linalg.norm(g) / np.linalg.norm(ref)))
+        mse.append(float(np.mean((g - ref) ** 2)))
+        lo.append(float(g.min()))
+        hi.append(float(g.max()))
+    return {"method": "16 N(0,1) [128,128] inputs at the LayerNorm output, per-sample cosine "
+                      "of [128,512] vs float64", "cos_mean": round(float(np.mean(cos)), 5),
+            "cos_min": round(min(cos), 5), "cos_max": round(max(cos), 5),
+            "mse_mean": float(np.mean(mse)), "range": [round(min(lo), 3), round(max(hi), 3)]}
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -161,6 +193,8 @@ def main(argv=None) -> int:
     ap.add_argument("--config", type=int, default=3, help="workload 1..5 (3 = headline)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="wall budget of the oracle CPU baseline (0 = skip)")
+    ap.add_argument("--dtype", choices=("bf16", "fp8", "f32"), default=None,
+                    help="override the workload's compute type (fp8: E4M3 operands)")
     ap.add_argument("--groups", type=int, default=1,
                     help="distinct layer weight sets (1 = Kokoro's full sharing)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -177,7 +211,7 @@ def main(argv=None) -> int:
 
     torch.cuda.set_device(0)
     wl = synth.make_workload(args.config)
-    dtype = wl.dtype
+    dtype = wl.dtype if args.dtype is None else args.dtype
     cfg = synth.Config(n_groups=args.groups)
     weights = synth.make_weights(cfg)
     enc = A.Encoder(weights, dtype, n_groups=args.groups)
@@ -243,17 +277,19 @@ def main(argv=None) -> int:
     tokens = wl.tokens
     value = tokens * args.steps / elapsed
     flops_step = seq_flops(wl.lengths)
-    peak = PEAK_BF16_TFLOPS if dtype == "bf16" else PEAK_F32_TFLOPS
+    peak = PEAKS[dtype]
     launch_ms = ms_dom / max(n_dom, 1)
     achieved = kernel_flops(dominant, wl.lengths) / (launch_ms * 1e-3) / 1e12
 
     got = out.cpu().numpy()
-    base, parity = (cpu_baseline(wl, got, args.cpu_seconds, cfg, weights) if args.cpu_seconds > 0
+    base, parity = (cpu_baseline(wl, got, args.cpu_seconds, cfg, weights, dtype) if args.cpu_seconds > 0
                     else (None, None))
-    length_reg = measure_length_regulation() if args.config == 3 and args.groups == 1 else None
+    length_reg = (measure_length_regulation() if args.config == 3 and args.groups == 1
+                  and dtype == "bf16" else None)
+    fidelity = hailo_fidelity(enc, cfg, weights) if dtype == "fp8" else None
 
     line = {
-        "metric": METRIC,
+        "metric": METRIC if dtype == "bf16" else METRIC.replace(" bf16;", f" {dtype};"),
         "value": round(value, 1),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -292,6 +328,7 @@ def main(argv=None) -> int:
         "cpu_baseline": base,
         "parity_sample": parity,
         "length_regulation": length_reg,
+        "fp8_fidelity": fidelity,
         "source_sha": source_hash(),
     }
     print(json.dumps(line), flush=True)

@@ -45,8 +45,16 @@ enum albert_status {
 };
 
 /* Compute/storage type of tables, weight matrices and activations.
- * Accumulation, biases, LayerNorm, softmax and GELU are always fp32. */
-enum albert_dtype { ALBERT_F32 = 0, ALBERT_BF16 = 1 };
+ * Accumulation, biases, LayerNorm, softmax and GELU are always fp32.
+ * ALBERT_FP8 is the low-precision variant: every matrix-product input is an
+ * OCP FP8 E4M3 code (weights per output row times a power-of-two scale, so
+ * the largest magnitude of each row is at most 448; activations rounded to
+ * nearest even and saturated at +-448) while the residual stream, Q|K|V and
+ * the tables stay bf16 and attention runs on bf16 matrix cores.  Its
+ * fidelity is scored as on the page "Kokoro-82M-encoder-hailo10h" ("Eval
+ * results"): N(0,1) inputs at the embedding LayerNorm output, cosine of the
+ * [128,512] outputs against full precision. */
+enum albert_dtype { ALBERT_F32 = 0, ALBERT_BF16 = 1, ALBERT_FP8 = 2 };
 
 /* flags for albert_encode / albert_encode_varlen */
 #define ALBERT_ASYNC 1u /* return after enqueueing; read the status later
@@ -118,8 +126,11 @@ int albert_tensor_shape(const albert_config* cfg, int index, int64_t* rows, int6
  *   canonical order and shape.  They are read during the call and may be
  *   freed after.
  * dtype: ALBERT_BF16 stores tables and weight matrices as bfloat16 (round to
- *   nearest even); ALBERT_F32 stores them as given.  Biases and LayerNorm
- *   vectors are fp32 in both.  The query weights and bias are stored scaled
+ *   nearest even); ALBERT_F32 stores them as given; ALBERT_FP8 stores the
+ *   tables as bfloat16 and each weight matrix row j as E4M3 codes of
+ *   W[j,:] * 2^k_j (k_j the largest integer with max_i |W[j,i]| * 2^k_j
+ *   <= 448, 0 for a zero row) plus the exponent.  Biases and LayerNorm
+ *   vectors are fp32 in all three.  The query weights and bias are stored scaled
  *   by 1/sqrt(head_dim) = 1/8, a power of two, so the attention scores need
  *   no further scaling and the stored values are exact.
  * This is the only call that allocates device memory (and it synchronises
@@ -170,6 +181,19 @@ int albert_encode_varlen(albert_ctx* ctx, const int32_t* ids, const int32_t* cu_
                          int n, int total, int max_len, float* out, void* ws,
                          size_t ws_bytes, void* hip_stream, unsigned flags);
 
+/* Packed batch that starts from the embedding LayerNorm output instead of
+ * phoneme IDs: the encoder block without its embedding, as deployed when the
+ * embedding runs elsewhere ("Kokoro-82M-encoder-hailo10h", "What this is
+ * not"; the low-precision fidelity method of its "Eval results" feeds this
+ * point).
+ * x          dev fp32 [total, emb], row-major; rows packed as cu_seqlens
+ *            says.  Values are used as given (non-finite values propagate).
+ * Other arguments, validation (lengths only: there are no IDs), errors,
+ * workspace and flags as albert_encode_varlen. */
+int albert_encode_features(albert_ctx* ctx, const float* x, const int32_t* cu_seqlens, int n,
+                           int total, int max_len, float* out, void* ws, size_t ws_bytes,
+                           void* hip_stream, unsigned flags);
+
 /* Wait for hip_stream and return the device status word that the last
  * request enqueued with this workspace left there (ALBERT_E_HIP if the read
  * fails). */
@@ -178,7 +202,10 @@ int albert_read_status(const void* ws, void* hip_stream);
 /* Debug taps: where a request's intermediate tensors sit in the workspace
  * after it completes (checkpoints at fixed boundaries of the graph, in graph
  * order).  Rows are packed tokens (sequence s at rows cu[s]..cu[s+1]-1);
- * elements are the context's dtype (fp32 or bf16) unless noted.
+ * elements are the context's dtype (fp32 or bf16) unless noted.  Under
+ * ALBERT_FP8, EMB, CTX and G hold E4M3 codes (one byte each), X, QKV and X1
+ * are bf16, and taps 10 and 11 are the E4M3 copies of X and X1 that feed
+ * the next products (ALBERT_E_ARG for other dtypes).
  *   0 STATUS  int32 [1]          1 CU     int32 [n_seq + 1]
  *   2 ROW_SEQ int32 [rows]       3 ROW_POS int32 [rows]
  *   4 EMB  [rows, E]   embedding sum after LayerNorm
@@ -187,19 +214,22 @@ int albert_read_status(const void* ws, void* hip_stream);
  *   7 CTX  [rows, H]   last execution's attention context (token-major)
  *   8 X1   [rows, H]   last execution's post-attention LayerNorm output
  *   9 G    [rows, F]   last execution's GELU output
+ *  10 X8   [rows, H]   E4M3 copy of X (ALBERT_FP8 only)
+ *  11 X1_8 [rows, H]   E4M3 copy of X1 (ALBERT_FP8 only)
  * Writes the byte offset from ws, the byte size, and the row stride in
  * elements (0 for the int32 taps).  Host-only; enqueues nothing. */
 enum albert_tap {
   ALBERT_TAP_STATUS = 0, ALBERT_TAP_CU = 1, ALBERT_TAP_ROW_SEQ = 2,
   ALBERT_TAP_ROW_POS = 3, ALBERT_TAP_EMB = 4, ALBERT_TAP_X = 5,
-  ALBERT_TAP_QKV = 6, ALBERT_TAP_CTX = 7, ALBERT_TAP_X1 = 8, ALBERT_TAP_G = 9
+  ALBERT_TAP_QKV = 6, ALBERT_TAP_CTX = 7, ALBERT_TAP_X1 = 8, ALBERT_TAP_G = 9,
+  ALBERT_TAP_X8 = 10, ALBERT_TAP_X1_8 = 11
 };
 int albert_tap(const albert_ctx* ctx, int n_seq, int64_t max_rows, int tap,
                size_t* offset, size_t* bytes, int64_t* row_stride);
 
 /* Kernel kinds of the launch sequence, for albert_time_kernel(). */
 enum albert_kernel_kind {
-  ALBERT_K_EMBED = 0,       /* embedding sum + LayerNorm                    */
+  ALBERT_K_EMBED = 0,       /* embedding sum + LayerNorm (or features in)   */
   ALBERT_K_PROJ = 1,        /* 128 -> 768 input projection                  */
   ALBERT_K_QKV = 2,         /* fused Q|K|V projection, once per execution   */
   ALBERT_K_ATTN = 3,        /* masked-softmax attention, once per execution */

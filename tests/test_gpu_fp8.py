@@ -1,0 +1,316 @@
+"""GPU checks of the low-precision (FP8 E4M3 operand) variant and of the
+LayerNorm-output entry point, through the C ABI.
+
+Bit-exact where the two sides take the same decision from the same data:
+the E4M3 conversion of caller features and the per-row E4M3 weight codes.
+Where a code is decided from an accumulated value, the oracle's float64
+value and the kernel's value may fall on either side of a rounding
+boundary, so a code must be the rounding of some value within a window of
+the oracle's (rounding is monotone: it lies between the roundings of the
+window's ends).  The matrix cores' E4M3 dot products accumulate with less
+than fp32 precision (observed deviations up to about 2^-18 of the sum of
+the products' magnitudes), so the window is 2^-16 of that sum.
+
+After all 12 executions FP8 rounding amplifies such flips: perturbing every
+rounding input of the oracle's FP8 emulation by a relative 2^-22 moves its
+outputs by up to 0.095 (per-token cosine down to 0.9989), so full-depth
+parity allows twice that: max |err| <= 0.2 and per-token cosine >= 0.997.
+"""
+import functools
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+from _gpu import check, dev, row_cosines
+
+pytestmark = pytest.mark.gpu
+K = synth.KOKORO
+FP8_MAX_ABS = 0.2
+FP8_MIN_COS = 0.997
+NEAR_TIE = 2.0 ** -16
+
+
+@functools.lru_cache(maxsize=None)
+def _w32():
+    return synth.make_weights()
+
+
+@functools.lru_cache(maxsize=None)
+def _w8():
+    return oracle.prepare_weights(_w32(), "fp8")
+
+
+_ENC = {}
+
+
+def _enc(dtype="fp8", **cfg):
+    import albert_transformer_amd as A
+    key = (dtype, tuple(sorted(cfg.items())))
+    if key not in _ENC:
+        _ENC[key] = A.Encoder(_w32(), dtype, **cfg)
+    return _ENC[key]
+
+
+def _tap(enc, ws, n_seq, rows_cap, name, rows, codes):
+    """Workspace checkpoint as float64: E4M3 codes decoded, or bf16."""
+    import torch
+    off, nb, stride = enc.tap(n_seq, rows_cap, name)
+    raw = ws[off:off + nb].cpu()
+    t = raw.view(torch.float8_e4m3fn) if codes else raw.view(torch.bfloat16)
+    return t.view(-1, stride)[:rows].double().numpy()
+
+
+def _run_features(enc, x, lengths):
+    import torch
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    total = int(cu[-1])
+    out = torch.full((total, 512), float("nan"), device="cuda")
+    ws = enc.new_workspace(len(lengths), total)
+    rc = enc.encode_features_raw(dev(np.ascontiguousarray(x, np.float32)), dev(cu),
+                                 int(max(lengths)), out, ws)
+    assert rc == 0, rc
+    return out.cpu().numpy().astype(np.float64), ws, cu
+
+
+def _codes_agree(got, pre, mag):
+    """E4M3 values decided from `pre` (float64), a sum of terms whose
+    magnitudes add up to `mag`: each must be the rounding of some value
+    within mag * 2^-16 of pre; returns the fraction equal to pre's own
+    rounding."""
+    w = mag * NEAR_TIE
+    ref = oracle.e4m3_round(pre)
+    lo = oracle.e4m3_round(pre - w)
+    hi = oracle.e4m3_round(pre + w)
+    ok = (got >= lo) & (got <= hi)  # rounding is monotone
+    if not np.all(ok):
+        bad = np.argwhere(~ok)[:8]
+        rows = [f"at {tuple(i)}: pre={pre[tuple(i)]!r} got={got[tuple(i)]!r} ref={ref[tuple(i)]!r}"
+                for i in bad]
+        raise AssertionError(f"{int((~ok).sum())} codes differ away from a rounding boundary:\n"
+                             + "\n".join(rows))
+    return float(np.mean(got == ref))
+
+
+def _bf16_agree(got, pre, mag):
+    w = mag * NEAR_TIE
+    ref = oracle.bf16_round(pre.astype(np.float32))
+    lo = oracle.bf16_round((pre - w).astype(np.float32))
+    hi = oracle.bf16_round((pre + w).astype(np.float32))
+    ok = (got >= lo) & (got <= hi)
+    if not np.all(ok):
+        bad = np.argwhere(~ok)[:8]
+        rows = [f"at {tuple(i)}: pre={pre[tuple(i)]!r} mag={mag[tuple(i)]!r} got={got[tuple(i)]!r} "
+                f"ref={ref[tuple(i)]!r}" for i in bad]
+        raise AssertionError(f"{int((~ok).sum())} bf16 values differ away from a rounding "
+                             "boundary:\n" + "\n".join(rows))
+
+
+def test_e4m3_conversion_is_bitexact():
+    """Caller features go through the device's E4M3 conversion: every finite
+    code, midpoints (ties to even), their float32 neighbours, subnormals,
+    saturation beyond 448 and random values, against the oracle's rounding."""
+    import torch
+    codes = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).double().numpy()
+    fin = np.unique(codes[np.isfinite(codes)])
+    pos = fin[fin >= 0]
+    mids = ((pos[1:] + pos[:-1]) / 2).astype(np.float32)
+    rng = np.random.default_rng(5)
+    vals = np.concatenate([
+        fin, mids, -mids, np.nextafter(mids, np.float32(0)), np.nextafter(mids, np.float32(1e9)),
+        [448.0, 449.0, 464.0, 480.0, 1e4, -1e6, 3e38, -3e38, 2.0 ** -10, 3 * 2.0 ** -10, -0.0],
+        rng.normal(0, 1, 4000), rng.normal(0, 100, 2000), rng.uniform(-2.0 ** -6, 2.0 ** -6, 2000),
+    ]).astype(np.float32)
+    rows = (len(vals) + 127) // 128
+    x = np.zeros(rows * 128, np.float32)
+    x[:len(vals)] = vals
+    x = x.reshape(rows, 128)
+    lengths = [min(512, rows - s) for s in range(0, rows, 512)]
+    enc = _enc("fp8", n_iter=0)
+    _, ws, _ = _run_features(enc, x, lengths)
+    got = _tap(enc, ws, len(lengths), rows, "emb", rows, codes=True)
+    assert np.array_equal(got, oracle.e4m3_round(x.astype(np.float64)))
+
+
+def test_fp8_weight_codes_are_bitexact():
+    """Unit feature rows through the input projection (bias 0, no layer
+    execution) read back the stored weights: each must equal the oracle's
+    per-row E4M3 quantization, including an all-zero row, a row whose
+    maximum is exactly 448 * 2^-5, a tiny row and a large row."""
+    import albert_transformer_amd as A
+    w = {k: v.copy() for k, v in _w32().items()}
+    rng = np.random.default_rng(6)
+    w["proj.b"][:] = 0.0
+    w["proj.w"][0] = 0.0
+    w["proj.w"][1] *= 14.0 / np.abs(w["proj.w"][1]).max()
+    w["proj.w"][2] = rng.normal(0, 1e-30, 128)
+    w["proj.w"][3] = rng.normal(0, 300.0, 128)
+    enc = A.Encoder(w, "fp8", n_iter=0)
+    x = np.eye(128, dtype=np.float32)
+    _, ws, _ = _run_features(enc, x, [128])
+    got = _tap(enc, ws, 1, 128, "x", 128, codes=False)       # [i, j] = W8[j, i]
+    ref = oracle.fp8_quantize_rows(w["proj.w"].astype(np.float64))
+    assert np.array_equal(got, ref.T)
+    enc.close()
+
+
+def test_fp8_projection_stage_codes():
+    """No layer execution: the projection's bf16 output and its E4M3 copy
+    against the oracle, decision by decision; then the output projection."""
+    enc = _enc("fp8", n_iter=0)
+    rng = np.random.default_rng(7)
+    lengths = [128, 77, 1, 300]
+    x = rng.normal(0, 1, (sum(lengths), 128))
+    out, ws, cu = _run_features(enc, x, lengths)
+    rows = int(cu[-1])
+    x8 = _tap(enc, ws, len(lengths), rows, "x8", rows, codes=True)
+    xb = _tap(enc, ws, len(lengths), rows, "x", rows, codes=False)
+    refs, pres = [], []
+    for s in range(len(lengths)):
+        t = {}
+        refs.append(oracle.encode_fp8_features(x[cu[s]:cu[s + 1]], _w8(), K, n_iter=0, taps=t))
+        pres.append(t["x0"])
+    ref, pre = np.concatenate(refs), np.concatenate(pres)
+    W8 = _w8()
+    mag = np.abs(oracle.e4m3_round(x)) @ np.abs(W8["proj.w"]).T + np.abs(W8["proj.b"])
+    frac = _codes_agree(x8, pre, mag)
+    _bf16_agree(xb, pre, mag)
+    print(f"[fp8] projection codes decided exactly: {frac:.6f}", flush=True)
+    assert frac > 0.999
+    err = float(np.max(np.abs(out - ref)))
+    print(f"[fp8] n_iter=0 output max_abs={err:.3e}", flush=True)
+    assert err < 5e-3   # a few near-tie codes may differ (each ~3e-4 here)
+
+
+def test_fp8_one_execution_stages():
+    """One layer execution, every checkpoint against the oracle's FP8
+    emulation: bf16 stages within bf16 rounding, E4M3 stages by value."""
+    enc = _enc("fp8", n_iter=1)
+    rng = np.random.default_rng(8)
+    lengths = [128, 33, 1]
+    x = rng.normal(0, 1, (sum(lengths), 128))
+    out, ws, cu = _run_features(enc, x, lengths)
+    rows, n = int(cu[-1]), len(lengths)
+    taps = {name: _tap(enc, ws, n, rows, name, rows, codes)
+            for name, codes in (("qkv", False), ("ctx", True), ("x1", False), ("x1_8", True),
+                                ("g", True), ("x", False), ("x8", True))}
+    for s in range(n):
+        sl = slice(int(cu[s]), int(cu[s + 1]))
+        t = {}
+        ref = oracle.encode_fp8_features(x[sl], _w8(), K, n_iter=1, taps=t)
+        qkv = t["qkv"].copy()
+        qkv[:, :768] /= 8.0   # the library stores q pre-scaled by 1/sqrt(64)
+        pairs = (("qkv", qkv), ("ctx", oracle.e4m3_round(t["ctx"])), ("x1", t["h1"]),
+                 ("x1_8", oracle.e4m3_round(t["h1"])), ("g", oracle.e4m3_round(t["g"])),
+                 ("x", t["out"]), ("x8", oracle.e4m3_round(t["out"])))
+        for name, r in pairs:
+            g = taps[name][sl]
+            cos = float(np.min(row_cosines(g, r)))
+            err = float(np.max(np.abs(g - r)))
+            print(f"[fp8] seq{s} {name} max_abs={err:.3e} min_cos={cos:.6f}", flush=True)
+            assert cos > 0.995, (name, cos)
+            assert err < 0.15 * max(1.0, float(np.abs(r).max())), (name, err)
+        err = float(np.max(np.abs(out[sl] - ref)))
+        cos = float(np.min(row_cosines(out[sl], ref)))
+        print(f"[fp8] one execution seq{s} output max_abs={err:.3e} min_cos={cos:.6f}", flush=True)
+        assert err <= FP8_MAX_ABS and cos >= FP8_MIN_COS
+
+
+def test_fp8_full_depth_parity():
+    enc = _enc("fp8")
+    rng = np.random.default_rng(9)
+    lengths = [128, 64, 257, 1]
+    x = rng.normal(0, 1, (sum(lengths), 128))
+    out, _, cu = _run_features(enc, x, lengths)
+    for s in range(len(lengths)):
+        sl = slice(int(cu[s]), int(cu[s + 1]))
+        ref = oracle.encode_fp8_features(x[sl], _w8(), K)
+        err = float(np.max(np.abs(out[sl] - ref)))
+        cos = float(np.min(row_cosines(out[sl], ref)))
+        print(f"[fp8] full depth seq{s} L={lengths[s]} max_abs={err:.3e} min_cos={cos:.6f}", flush=True)
+        assert err <= FP8_MAX_ABS and cos >= FP8_MIN_COS
+
+
+def test_fp8_ids_path_headline_batch():
+    """The phoneme-ID entry under FP8 at the full B=256, T=128 batch;
+    sampled sequences against the emulation fed by the oracle's embedding."""
+    import torch
+    enc = _enc("fp8")
+    wl = synth.make_workload(3)
+    B, T = wl.ids.shape
+    out = torch.full((B, T, 512), float("nan"), device="cuda")
+    ws = enc.new_workspace(B, B * T)
+    assert enc.encode_raw(dev(wl.ids), dev(wl.lengths), out, ws) == 0
+    got = out.cpu().numpy().astype(np.float64)
+    for b in (0, 200):
+        e = oracle.embed_ln(wl.ids[b], _w8(), K)
+        ref = oracle.encode_fp8_features(e, _w8(), K)
+        err = float(np.max(np.abs(got[b] - ref)))
+        cos = float(np.min(row_cosines(got[b], ref)))
+        print(f"[fp8] ids path seq{b} max_abs={err:.3e} min_cos={cos:.6f}", flush=True)
+        assert err <= FP8_MAX_ABS and cos >= FP8_MIN_COS
+
+
+def test_fp8_fidelity_by_the_hailo_method():
+    """16 N(0,1) inputs [128,128] at the LayerNorm output; per-sample cosine
+    of the flattened [128,512] output against full precision (float64
+    oracle, unrounded weights), as the Hailo card scores its INT8 build."""
+    enc = _enc("fp8")
+    W64 = oracle.prepare_weights(_w32(), "f32")
+    rng = np.random.default_rng(2024)
+    x = rng.normal(0, 1, (16 * 128, 128))
+    out, _, _ = _run_features(enc, x, [128] * 16)
+    cos, mse = [], []
+    for s in range(16):
+        sl = slice(128 * s, 128 * (s + 1))
+        ref = oracle.encode_features(x[sl], W64, K)
+        g = out[sl]
+        cos.append(float((g * ref).sum() / np.linalg.norm(g) / np.linalg.norm(ref)))
+        mse.append(float(np.mean((g - ref) ** 2)))
+    print(f"[fp8] hailo-method cosine mean={np.mean(cos):.5f} min={min(cos):.5f} "
+          f"max={max(cos):.5f} mse_mean={np.mean(mse):.3e}", flush=True)
+    assert min(cos) >= 0.99
+
+
+def test_bf16_features_entry():
+    """The LayerNorm-output entry on the bf16 path against the oracle's
+    encoder tail, and against the ID entry fed the same sequence."""
+    import torch
+    enc = _enc("bf16")
+    W = oracle.prepare_weights(_w32(), "bf16")
+    wl = synth.random_padded(41, B=3, T=90, lo=1, hi=90)
+    wl.lengths[:] = [90, 45, 1]
+    feats = np.concatenate([oracle.embed_ln(wl.ids[b, :L], W, K) for b, L in enumerate(wl.lengths)])
+    out, _, cu = _run_features(enc, feats, list(wl.lengths))
+    B, T = wl.ids.shape
+    ref_ids = torch.full((B, T, 512), float("nan"), device="cuda")
+    ws = enc.new_workspace(B, B * T)
+    assert enc.encode_raw(dev(wl.ids), dev(wl.lengths), ref_ids, ws) == 0
+    ref_ids = ref_ids.cpu().numpy().astype(np.float64)
+    for b, L in enumerate(wl.lengths):
+        sl = slice(int(cu[b]), int(cu[b + 1]))
+        check(out[sl], oracle.encode_features(feats[sl], W, K), "bf16", f"features entry seq{b}")
+        check(out[sl], ref_ids[b, :L], "bf16", f"features vs ids entry seq{b}")
+
+
+def test_features_entry_rejections():
+    import torch
+    import albert_transformer_amd as A
+    enc = _enc("bf16")
+    x = dev(np.zeros((10, 128), np.float32))
+    ws = enc.new_workspace(2, 10)
+    canary = torch.full((10, 512), 7.0, device="cuda")
+    bad_cu = dev(np.array([0, 0, 10], np.int32))        # an empty sequence
+    out = canary.clone()
+    assert enc.encode_features_raw(x, bad_cu, 10, out, ws) == A.E_LENGTH
+    assert torch.equal(out, canary)
+    cu = dev(np.array([0, 4, 10], np.int32))
+    assert enc.encode_features_raw(x, cu, 5, out, ws) == A.E_LENGTH   # length 6 > max_len
+    assert torch.equal(out, canary)
+    assert enc.encode_features_raw(x, cu, 513, out, ws) == A.E_ARG
+    assert enc.encode_features_raw(x, cu, 6, out, ws, ws_bytes=64) == A.E_WORKSPACE
+    assert enc.encode_features_raw(x, cu, 6, x, ws) == A.E_ALIAS
+    with pytest.raises(A.AlbertError):
+        enc.tap(2, 10, "x8")   # E4M3 copies exist only under FP8
