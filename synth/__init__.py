@@ -207,3 +207,76 @@ def random_packed(seed: int, lengths, vocab: int = 178, dtype: str = "bf16") -> 
     cu[1:] = np.cumsum(lengths)
     return Workload(f"random packed n={len(lengths)}", dtype, ids, lengths,
                     int(lengths.max()), packed=True, cu_seqlens=cu)
+
+
+# ------------------------------------------------------- text encoder ----
+# Kokoro's parallel text path: embedding -> three weight-normalized
+# convolutions -> bidirectional LSTM ("How Kokoro TTS Works and Where CKE
+# Stands", the component list; [512, T] features per "How I want CKE to
+# stitch it").  Sizes the pages leave open follow the StyleTTS 2 text
+# encoder that Kokoro inherits: 512 channels, kernel 5, 256 LSTM units per
+# direction.
+
+TEXT_WEIGHT_SEED = 20261204
+
+
+@dataclass(frozen=True)
+class TextConfig:
+    vocab: int = 178
+    channels: int = 512
+    kernel: int = 5
+    n_conv: int = 3
+    hidden: int = 256          # LSTM units per direction
+    ln_eps: float = 1e-5
+    slope: float = 0.2         # LeakyReLU negative slope
+
+    def tensor_names(self) -> tuple:
+        names = ["emb"]
+        for i in range(self.n_conv):
+            names += [f"conv{i}.v", f"conv{i}.g", f"conv{i}.b", f"conv{i}.ln.g", f"conv{i}.ln.b"]
+        for d in ("fwd", "bwd"):
+            names += [f"lstm.{d}.w_ih", f"lstm.{d}.w_hh", f"lstm.{d}.b_ih", f"lstm.{d}.b_hh"]
+        return tuple(names)
+
+    def shapes(self) -> dict:
+        C, K, Hh = self.channels, self.kernel, self.hidden
+        s = {"emb": (self.vocab, C)}
+        for i in range(self.n_conv):
+            s.update({f"conv{i}.v": (C, C, K), f"conv{i}.g": (C,), f"conv{i}.b": (C,),
+                      f"conv{i}.ln.g": (C,), f"conv{i}.ln.b": (C,)})
+        for d in ("fwd", "bwd"):
+            s.update({f"lstm.{d}.w_ih": (4 * Hh, C), f"lstm.{d}.w_hh": (4 * Hh, Hh),
+                      f"lstm.{d}.b_ih": (4 * Hh,), f"lstm.{d}.b_hh": (4 * Hh,)})
+        return s
+
+
+TEXT = TextConfig()
+TEXT_TINY = TextConfig(vocab=7, channels=6, kernel=3, n_conv=2, hidden=3)
+
+
+def make_text_weights(cfg: TextConfig = TEXT, seed: int = TEXT_WEIGHT_SEED) -> dict:
+    """Draw the text encoder's tensors in canonical order from one generator.
+
+    Embedding N(0, 1); convolution directions v ~ N(0, 0.02) with gains
+    g = 1 + N(0, 0.01) (so each output channel's effective weight has norm
+    close to 1) and biases N(0, 0.02); LayerNorm gains 1 + N(0, 0.01),
+    shifts N(0, 0.01); LSTM matrices N(0, 0.05) and biases N(0, 0.02).
+    Drawn in float64, returned as float32.
+    """
+    rng = np.random.default_rng(seed)
+    shapes = cfg.shapes()
+    out = {}
+    for name in cfg.tensor_names():
+        shp = shapes[name]
+        if name == "emb":
+            a = rng.normal(0.0, 1.0, size=shp)
+        elif name.endswith(".g"):
+            a = 1.0 + rng.normal(0.0, 0.01, size=shp)
+        elif name.endswith("ln.b"):
+            a = rng.normal(0.0, 0.01, size=shp)
+        elif name.startswith("lstm") and ".w_" in name:
+            a = rng.normal(0.0, 0.05, size=shp)
+        else:
+            a = rng.normal(0.0, 0.02, size=shp)
+        out[name] = np.ascontiguousarray(a.astype(np.float32))
+    return out
