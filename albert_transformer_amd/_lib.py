@@ -29,7 +29,13 @@ EXPORTS = ("albert_default_config", "albert_n_tensors", "albert_tensor_name",
            "albert_tensor_shape", "albert_load_weights", "albert_workspace_bytes", "albert_encode",
            "albert_encode_varlen", "albert_encode_features", "albert_read_status", "albert_tap", "albert_free",
            "albert_status_str", "albert_time_kernel", "albert_kernel_time",
-           "albert_durations", "albert_expand_workspace_bytes", "albert_expand")
+           "albert_durations", "albert_expand_workspace_bytes", "albert_expand",
+           "albert_text_default_config", "albert_text_n_tensors", "albert_text_tensor_name",
+           "albert_text_tensor_shape", "albert_text_load_weights", "albert_text_workspace_bytes",
+           "albert_text_encode", "albert_text_encode_varlen", "albert_text_tap",
+           "albert_text_time_kernel", "albert_text_kernel_time", "albert_text_free")
+TEXT_TAPS = {"status": 0, "cu": 1, "emb": 2, "conv": 3, "xg": 4}
+TEXT_KERNEL_KINDS = ("embed", "unfold", "conv", "lstm_in", "lstm")
 KERNEL_KINDS = ("embed", "proj", "qkv", "attn", "attn_out_ln", "ffn1_gelu", "ffn2_ln", "out")
 
 
@@ -40,6 +46,13 @@ class Config(ctypes.Structure):
                 ("head_dim", ctypes.c_int32), ("ffn", ctypes.c_int32),
                 ("n_iter", ctypes.c_int32), ("n_groups", ctypes.c_int32),
                 ("out_dim", ctypes.c_int32), ("ln_eps", ctypes.c_float)]
+
+
+class TextConfig(ctypes.Structure):
+    _fields_ = [("vocab", ctypes.c_int32), ("channels", ctypes.c_int32),
+                ("kernel", ctypes.c_int32), ("n_conv", ctypes.c_int32),
+                ("hidden", ctypes.c_int32), ("ln_eps", ctypes.c_float),
+                ("slope", ctypes.c_float)]
 
 
 _LIB = None
@@ -96,6 +109,33 @@ def lib():
     L.albert_expand_workspace_bytes.restype = sz
     L.albert_expand.argtypes = [vp, vp, vp, i32, i32, i32, vp, i64, vp, vp, sz, vp, ctypes.c_uint]
     L.albert_expand.restype = i32
+    tc = ctypes.POINTER(TextConfig)
+    L.albert_text_default_config.argtypes = [tc]
+    L.albert_text_default_config.restype = i32
+    L.albert_text_n_tensors.argtypes = [tc]
+    L.albert_text_n_tensors.restype = i32
+    L.albert_text_tensor_name.argtypes = [tc, i32]
+    L.albert_text_tensor_name.restype = ctypes.c_char_p
+    L.albert_text_tensor_shape.argtypes = [tc, i32, ctypes.POINTER(i64), ctypes.POINTER(i64)]
+    L.albert_text_tensor_shape.restype = i32
+    L.albert_text_load_weights.argtypes = [ctypes.POINTER(vp), tc, ctypes.POINTER(vp), vp]
+    L.albert_text_load_weights.restype = i32
+    L.albert_text_workspace_bytes.argtypes = [vp, i32, i64]
+    L.albert_text_workspace_bytes.restype = sz
+    L.albert_text_encode.argtypes = [vp, vp, vp, i32, i32, vp, vp, sz, vp, ctypes.c_uint]
+    L.albert_text_encode.restype = i32
+    L.albert_text_encode_varlen.argtypes = [vp, vp, vp, i32, i32, i32, vp, vp, sz, vp,
+                                            ctypes.c_uint]
+    L.albert_text_encode_varlen.restype = i32
+    L.albert_text_tap.argtypes = [vp, i32, i64, i32, ctypes.POINTER(sz), ctypes.POINTER(sz),
+                                  ctypes.POINTER(i64)]
+    L.albert_text_tap.restype = i32
+    L.albert_text_time_kernel.argtypes = [vp, i32, i32]
+    L.albert_text_time_kernel.restype = i32
+    L.albert_text_kernel_time.argtypes = [vp, ctypes.POINTER(i32), ctypes.POINTER(ctypes.c_double)]
+    L.albert_text_kernel_time.restype = i32
+    L.albert_text_free.argtypes = [vp]
+    L.albert_text_free.restype = None
     _LIB = L
     return L
 
@@ -317,3 +357,111 @@ def expand(feat, dur, cu_tok, max_frames, stream=None):
 
 def read_status(ws, stream=None) -> int:
     return int(lib().albert_read_status(_ptr(ws), _stream(stream)))
+
+
+def text_default_config(**overrides) -> TextConfig:
+    c = TextConfig()
+    lib().albert_text_default_config(ctypes.byref(c))
+    for k, v in overrides.items():
+        setattr(c, k, v)
+    return c
+
+
+class TextEncoder:
+    """Device copy of the parallel text encoder's weights (an albert_text_ctx).
+
+    weights: dict of canonical name -> float32 array (``synth.TextConfig``
+    names; conv<i>.v may be [C, C, K]); config overrides as keywords.
+    """
+
+    def __init__(self, weights: dict, stream=None, **cfg):
+        import torch  # noqa: F401  (HIP runtime shared with torch)
+        L = lib()
+        self.cfg = text_default_config(**cfg)
+        cf = ctypes.byref(self.cfg)
+        nt = L.albert_text_n_tensors(cf)
+        if nt < 0:
+            raise AlbertError(E_ARG, "albert_text_n_tensors")
+        host = []
+        for i in range(nt):
+            n = L.albert_text_tensor_name(cf, i).decode()
+            a = np.ascontiguousarray(np.asarray(weights[n], dtype=np.float32))
+            r, c = ctypes.c_int64(), ctypes.c_int64()
+            rc = L.albert_text_tensor_shape(cf, i, ctypes.byref(r), ctypes.byref(c))
+            if rc != OK:
+                raise AlbertError(rc, "albert_text_tensor_shape")
+            if a.size != r.value * c.value:
+                raise ValueError(f"{n}: expected {r.value}x{c.value} values, got {a.shape}")
+            host.append(a)
+        ptrs = (ctypes.c_void_p * nt)(*[a.ctypes.data for a in host])
+        h = ctypes.c_void_p()
+        rc = L.albert_text_load_weights(ctypes.byref(h), cf, ptrs, _stream(stream))
+        if rc != OK:
+            raise AlbertError(rc, "albert_text_load_weights")
+        self.handle = h
+
+    def close(self):
+        if getattr(self, "handle", None):
+            lib().albert_text_free(self.handle)
+            self.handle = None
+
+    __del__ = close
+
+    @property
+    def out_dim(self) -> int:
+        return 2 * self.cfg.hidden
+
+    def workspace_bytes(self, n_seq: int, max_rows: int) -> int:
+        return int(lib().albert_text_workspace_bytes(self.handle, n_seq, max_rows))
+
+    def new_workspace(self, n_seq: int, max_rows: int):
+        import torch
+        return torch.empty(self.workspace_bytes(n_seq, max_rows), dtype=torch.uint8,
+                           device="cuda")
+
+    def tap(self, n_seq: int, max_rows: int, name: str):
+        off, nb, st = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_int64()
+        rc = lib().albert_text_tap(self.handle, n_seq, max_rows, TEXT_TAPS[name],
+                                   ctypes.byref(off), ctypes.byref(nb), ctypes.byref(st))
+        if rc != OK:
+            raise AlbertError(rc, "albert_text_tap")
+        return off.value, nb.value, st.value
+
+    def time_kernel(self, kind: str | None, max_launches: int = 1024) -> None:
+        k = -1 if kind is None else TEXT_KERNEL_KINDS.index(kind)
+        rc = lib().albert_text_time_kernel(self.handle, k, max_launches)
+        if rc != OK:
+            raise AlbertError(rc, "albert_text_time_kernel")
+
+    def kernel_time(self) -> tuple[int, float]:
+        n, ms = ctypes.c_int(), ctypes.c_double()
+        rc = lib().albert_text_kernel_time(self.handle, ctypes.byref(n), ctypes.byref(ms))
+        if rc != OK:
+            raise AlbertError(rc, "albert_text_kernel_time")
+        return n.value, ms.value
+
+    def encode_raw(self, ids, lengths, out, ws, stream=None, flags=0, ws_bytes=None) -> int:
+        B, T = ids.shape
+        nb = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
+        return lib().albert_text_encode(self.handle, _ptr(ids), _ptr(lengths), B, T, _ptr(out),
+                                        _ptr(ws), nb, _stream(stream), flags)
+
+    def encode_varlen_raw(self, ids, cu, max_len, out, ws, stream=None, flags=0,
+                          ws_bytes=None) -> int:
+        nb = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
+        return lib().albert_text_encode_varlen(self.handle, _ptr(ids), _ptr(cu), cu.numel() - 1,
+                                               ids.numel(), max_len, _ptr(out), _ptr(ws), nb,
+                                               _stream(stream), flags)
+
+    def encode(self, ids, lengths, out=None, ws=None, stream=None):
+        """ids int32 [B, T], lengths int32 [B] (CUDA) -> fp32 [B, T, 512]."""
+        import torch
+        B, T = ids.shape
+        if out is None:
+            out = torch.empty(B, T, self.out_dim, dtype=torch.float32, device="cuda")
+        if ws is None:
+            ws = self.new_workspace(B, B * T)
+        rc = self.encode_raw(ids, lengths, out, ws, stream)
+        if rc != OK:
+            raise AlbertError(rc, "albert_text_encode")
+        return out

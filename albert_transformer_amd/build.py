@@ -11,7 +11,7 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SRC = os.path.join(HERE, "csrc", "albert.hip")
+SRCS = [os.path.join(HERE, "csrc", "albert.hip"), os.path.join(HERE, "csrc", "text.hip")]
 OUT = os.path.join(HERE, "libalbert.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -27,13 +27,13 @@ FLAGS = [
 
 def build(verbose: bool = False, extra: list[str] | None = None) -> str:
     tmp = OUT + ".tmp"
-    cmd = [HIPCC, *FLAGS, *(extra or []), SRC, "-o", tmp]
+    cmd = [HIPCC, *FLAGS, *(extra or []), *SRCS, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         sys.stderr.write(r.stdout + r.stderr)
-        raise RuntimeError(f"hipcc failed ({r.returncode}) building {SRC}")
+        raise RuntimeError(f"hipcc failed ({r.returncode}) building {' '.join(SRCS)}")
     os.replace(tmp, OUT)
     return OUT
 

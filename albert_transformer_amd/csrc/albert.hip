@@ -24,6 +24,7 @@
 #include "attention.hpp"
 #include "duration.hpp"
 #include "gemm.hpp"
+#include "launch.hpp"
 #include "prologue.hpp"
 
 using namespace albert;
@@ -183,48 +184,6 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
   if (!a || !b || !na || !nb) return false;
   const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
   return x < y + nb && y < x + na;
-}
-
-// Persistent launch: one block per CU at most (a multiple of 8, so that the
-// kernel's XCD-aware tile numbering is a bijection), each walking its tiles.
-template <typename T, bool F8, int BM, int BN, int WGM, int WGN, int RB, int STAGES, int EPI,
-          bool DEFER>
-void launch_gemm(GemmArgs g, int64_t max_rows, int grid_cap, hipStream_t s) {
-  g.n_tiles = g.N / BN;
-  const int64_t tiles = (max_rows + BM - 1) / BM * g.n_tiles;
-  const int64_t grid = std::min<int64_t>((tiles + 7) / 8 * 8, grid_cap);
-  hipLaunchKernelGGL((gemm_kernel<T, F8, BM, BN, WGM, WGN, RB, STAGES, EPI, DEFER>),
-                     dim3((unsigned)grid), dim3(WGM * WGN * 64), 0, s, g);
-}
-
-// Large tiles for plain and GELU epilogues; full-row tiles for LayerNorm.
-// bf16 bias/GELU GEMMs with at least 12 (an even number of) K slices keep
-// each tile's outputs in registers and write them during the next tile.
-// E4M3 operands stage 64-byte rows (one 64-deep MFMA step per slice).
-template <typename T, bool F8, int EPI>
-void gemm_big(GemmArgs g, int64_t max_rows, int grid_cap, hipStream_t s) {
-  constexpr bool can_defer =
-      std::is_same<T, bf16>::value && !F8 && (EPI == EPI_BIAS || EPI == EPI_GELU);
-  constexpr int RB = F8 ? 64 : 128;
-  const int slices = g.K * (F8 ? 1 : (int)sizeof(T)) / RB;
-  if (can_defer && slices >= 12 && slices % 2 == 0 && !g.Y8)
-    launch_gemm<T, F8, 256, 256, 2, 2, RB, 2, EPI, can_defer>(g, max_rows, grid_cap, s);
-  else
-    launch_gemm<T, F8, 256, 256, 2, 2, RB, 2, EPI, false>(g, max_rows, grid_cap, s);
-}
-// 128-row tiles need at least a full wave of them; smaller batches use
-// 64-row tiles (4 waves, one per SIMD) to spread over more CUs.
-// (E4M3 fragments are too wide for the 8-wave tile's register budget, so the
-// low-precision variant always uses the 4-wave one.)
-template <typename T, bool F8>
-void gemm_ln(GemmArgs g, int64_t max_rows, int grid_cap, hipStream_t s) {
-  if constexpr (!F8) {
-    if ((max_rows + 127) / 128 >= grid_cap) {
-      launch_gemm<T, F8, 128, 768, 2, 4, 64, 2, EPI_LN, false>(g, max_rows, grid_cap, s);
-      return;
-    }
-  }
-  launch_gemm<T, F8, 64, 768, 1, 4, 64, 2, EPI_LN, false>(g, max_rows, grid_cap, s);
 }
 
 // Launch `fn` on stream s, bracketed by timing events when `kind` is the

@@ -12,6 +12,8 @@
 //             residual + LayerNorm: steps 5 and 6 of "Inside One Real ALBERT
 //             Layer"); the block tile spans the whole row so the row
 //             statistics never leave the chip
+//   EPI_LN_ACT  store LeakyReLU(LN(Y) * g + beta), no residual (the text
+//             path's convolution blocks)
 //   EPI_OUT   store Y as fp32 into the caller's output, packed row m going to
 //             out row seq(m) * T + pos(m) (padded) or m (packed)
 //
@@ -58,7 +60,7 @@
 
 namespace albert {
 
-enum Epi { EPI_BIAS = 0, EPI_GELU = 1, EPI_LN = 2, EPI_OUT = 3 };
+enum Epi { EPI_BIAS = 0, EPI_GELU = 1, EPI_LN = 2, EPI_OUT = 3, EPI_LN_ACT = 4 };
 
 struct GemmArgs {
   const void* X;       // [M, K] activations, row stride ldx (elements)
@@ -72,9 +74,10 @@ struct GemmArgs {
   int64_t ldy8;
   const void* R;       // [M, N] residual (EPI_LN), stride ldr
   int64_t ldr;
-  const float* ln_g;   // [N] (EPI_LN)
+  const float* ln_g;   // [N] (EPI_LN, EPI_LN_ACT)
   const float* ln_b;
   float eps;
+  float slope;         // EPI_LN_ACT: LeakyReLU negative slope
   float* out;          // EPI_OUT: fp32 output rows of N
   const int* row_seq;  // EPI_OUT padded mapping
   const int* row_pos;
@@ -125,7 +128,8 @@ gemm_kernel(GemmArgs g) {
   constexpr int TM = WTM / 32, TN = WTN / 32;
   constexpr int KSTEPS = BK / KS;             // MFMA k-steps per slice
   constexpr int FCH = FE / CH;                // chunks per fragment (1 bf16, 2 fp32 / E4M3)
-  constexpr int NVEC = EPI == EPI_LN ? 3 : 1; // bias (+ LayerNorm gain, shift)
+  constexpr bool LNE = EPI == EPI_LN || EPI == EPI_LN_ACT;  // full-row LayerNorm epilogue
+  constexpr int NVEC = LNE ? 3 : 1;          // bias (+ LayerNorm gain, shift)
   constexpr int VPT = (BN + NT - 1) / NT;     // vector elements per thread
   static_assert(NINST % NW == 0, "DMA split");
   static_assert((BM / RPI) % NW == 0, "each DMA slot must be all-X or all-W");
@@ -155,7 +159,7 @@ gemm_kernel(GemmArgs g) {
   // Epilogue vectors, double-buffered across consecutive tiles, and the
   // LayerNorm cross-wave row reduction.
   __shared__ float vecs[2][NVEC][BN];
-  __shared__ float red[EPI == EPI_LN ? WGN * BM : 1];
+  __shared__ float red[LNE ? WGN * BM : 1];
 
   if (*g.status != 0) return;
   const int M = *g.m_ptr;
@@ -241,7 +245,7 @@ gemm_kernel(GemmArgs g) {
       const int c = tid + k * NT;
       if (c < BN) {
         vreg[0][k] = g.bias[nb0 + c];
-        if constexpr (EPI == EPI_LN) {
+        if constexpr (LNE) {
           vreg[1 % NVEC][k] = g.ln_g[nb0 + c];
           vreg[2 % NVEC][k] = g.ln_b[nb0 + c];
         }
@@ -392,7 +396,7 @@ gemm_kernel(GemmArgs g) {
   // n0 + wn*WTN + j*32 + 8q + 4hh + e.
   auto epilogue = [&](int em0, int en0, int vb) __attribute__((always_inline)) {
     const float* __restrict__ bias_s = vecs[vb][0];
-    if constexpr (EPI == EPI_LN) {
+    if constexpr (LNE) {
       const float* __restrict__ g_s = vecs[vb][1 % NVEC];
       const float* __restrict__ b_s = vecs[vb][2 % NVEC];
       const int N = g.N;
@@ -401,13 +405,18 @@ gemm_kernel(GemmArgs g) {
       for (int i = 0; i < TM; ++i) {
         const int m = em0 + wm * WTM + i * 32 + l32;
         const int mr = m < M ? m : M - 1;  // rows past M compute on a valid row, never stored
-        const T* __restrict__ rrow = R + (int64_t)mr * g.ldr + en0 + wn * WTN + 4 * hh;
+        const int64_t roff = (int64_t)mr * g.ldr + en0 + wn * WTN + 4 * hh;
         float s = 0.f;
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
           f32x4 rv[4];  // this column group's residual loads first, then one wait
 #pragma unroll
-          for (int q = 0; q < 4; ++q) rv[q] = TS::load4f(rrow + j * 32 + 8 * q);
+          for (int q = 0; q < 4; ++q) {
+            if constexpr (EPI == EPI_LN)
+              rv[q] = TS::load4f(R + roff + j * 32 + 8 * q);
+            else
+              rv[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+          }
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const int nl = wn * WTN + j * 32 + 8 * q + 4 * hh;
@@ -462,8 +471,10 @@ gemm_kernel(GemmArgs g) {
             const int nl = wn * WTN + j * 32 + 8 * q + 4 * hh;
             float o[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
+            for (int e = 0; e < 4; ++e) {
               o[e] = (acc[i][j][4 * q + e] - mean[i]) * rstd * g_s[nl + e] + b_s[nl + e];
+              if constexpr (EPI == EPI_LN_ACT) o[e] = o[e] >= 0.f ? o[e] : o[e] * g.slope;
+            }
             TS::store4(Y + (int64_t)m * g.ldy + en0 + nl, o[0], o[1], o[2], o[3]);
             if constexpr (F8)
               store4_as<T, true>(g.Y8, (int64_t)m * g.ldy8 + en0 + nl, o[0], o[1], o[2], o[3]);

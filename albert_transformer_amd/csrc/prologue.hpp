@@ -1,6 +1,9 @@
 // Request validation, packed-row bookkeeping, the three-table embedding with
 // its LayerNorm, and the zeroing of padded output rows.
 //
+// The non-template kernels have internal linkage: each translation unit of
+// the library (encoder, text path) gets its own copy.
+//
 // Every kernel reads the device status word first and does nothing when a
 // previous step has rejected the request, so that a rejected request never
 // writes the caller's output (the validate-before-write contract of the page
@@ -33,7 +36,7 @@ __device__ __forceinline__ int block_incl_scan_1024(int v, int* sh) {
 
 // Padded batch: check every length in [1, T], write cu[0..B] (prefix sums)
 // and the status word.  One block of 1024 threads.
-__global__ void __launch_bounds__(1024)
+static __global__ void __launch_bounds__(1024)
 derive_padded_kernel(const int* __restrict__ lengths, int B, int T, int* __restrict__ cu,
                      int* __restrict__ status) {
   __shared__ int sh[1024];
@@ -64,7 +67,7 @@ derive_padded_kernel(const int* __restrict__ lengths, int B, int T, int* __restr
 
 // Packed batch: cu_in[0] = 0, cu_in[n] = total, every length in
 // [1, max_len]; copy the offsets into the workspace.  One block.
-__global__ void __launch_bounds__(1024)
+static __global__ void __launch_bounds__(1024)
 derive_packed_kernel(const int* __restrict__ cu_in, int n, int total, int max_len,
                      int* __restrict__ cu, int* __restrict__ status) {
   __shared__ int bad;
@@ -82,7 +85,7 @@ derive_packed_kernel(const int* __restrict__ cu_in, int n, int total, int max_le
 // One block per sequence: write each valid row's sequence index and
 // position, and check the ID at that slot.  Pad slots are never read.
 // pad_T > 0: ids is [B, pad_T]; pad_T == 0: ids is packed [total].
-__global__ void __launch_bounds__(256)
+static __global__ void __launch_bounds__(256)
 rows_ids_kernel(const int* __restrict__ ids, const int* __restrict__ cu, int pad_T, int vocab,
                 int* __restrict__ row_seq, int* __restrict__ row_pos, int* __restrict__ status) {
   if (*status != ST_OK) return;
@@ -169,7 +172,7 @@ features_in_kernel(const float* __restrict__ x, const int* __restrict__ m_ptr,
 }
 
 // Padded output: rows t >= lengths[b] of out[B, T, n_out] are set to 0.
-__global__ void __launch_bounds__(256)
+static __global__ void __launch_bounds__(256)
 zero_pad_rows_kernel(float* __restrict__ out, const int* __restrict__ cu, int T, int n_out,
                      const int* __restrict__ status) {
   if (*status != ST_OK) return;

@@ -1,0 +1,164 @@
+// Kokoro's parallel text path on the GPU: embedding, convolution blocks,
+// bidirectional LSTM ("How Kokoro TTS Works and Where CKE Stands": a small
+// separate path of an embedding, three weight-normalized convolutions and a
+// bidirectional LSTM beside the ALBERT; [512, T] features).
+//
+// Rows are packed tokens (sequence s at rows cu[s] .. cu[s+1]-1), as in the
+// encoder.  A convolution of width K over a sequence is one GEMM over the
+// unfolded input col[m, j*C + c] = x[m + j - K/2, c] (zero where that row
+// is outside m's sequence), so zero padding happens at every sequence's own
+// ends and neighbours in the pack never mix; its LayerNorm and LeakyReLU
+// run in the GEMM's full-row epilogue.  The LSTM input projection (both
+// directions, both biases) is a second GEMM into fp32 gate pre-activations;
+// the recurrence below then only adds W_hh h_{t-1}.
+#pragma once
+
+#include "common.hpp"
+
+namespace albert {
+
+constexpr int kLstmH = 256;   // units per direction
+constexpr int kLstmSeq = 32;  // sequences per recurrence workgroup
+
+// x[m, :] = emb[id(m), :] for the M valid rows; C a multiple of 8.
+__global__ void __launch_bounds__(256)
+text_embed_kernel(const int* __restrict__ ids, int pad_T, const int* __restrict__ row_seq,
+                  const int* __restrict__ row_pos, const int* __restrict__ m_ptr,
+                  const bf16* __restrict__ emb, int C, bf16* __restrict__ out,
+                  const int* __restrict__ status) {
+  if (*status != 0) return;
+  const int cpr = C / 8;  // 16-byte chunks per row
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (int64_t)(*m_ptr) * cpr) return;
+  const int m = (int)(i / cpr), c = (int)(i % cpr);
+  const int id = pad_T ? ids[(int64_t)row_seq[m] * pad_T + row_pos[m]] : ids[m];
+  reinterpret_cast<uint4*>(out + (int64_t)m * C)[c] =
+      reinterpret_cast<const uint4*>(emb + (int64_t)id * C)[c];
+}
+
+// Unfolded convolution input: col[m, j*C + c] = x[m + j - K/2, c] when that
+// row belongs to m's sequence, else 0.  16 bytes per thread.
+__global__ void __launch_bounds__(256)
+unfold_kernel(const bf16* __restrict__ x, const int* __restrict__ row_seq,
+              const int* __restrict__ row_pos, const int* __restrict__ cu,
+              const int* __restrict__ m_ptr, int C, int K, bf16* __restrict__ col,
+              const int* __restrict__ status) {
+  if (*status != 0) return;
+  const int cpr = C / 8;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;  // over M * K * cpr
+  if (i >= (int64_t)(*m_ptr) * K * cpr) return;
+  const int c = (int)(i % cpr);
+  const int64_t mj = i / cpr;
+  const int j = (int)(mj % K), m = (int)(mj / K);
+  const int s = row_seq[m];
+  const int p = row_pos[m] + j - K / 2;
+  uint4 v = make_uint4(0, 0, 0, 0);
+  if (p >= 0 && p < cu[s + 1] - cu[s])
+    v = reinterpret_cast<const uint4*>(x + (int64_t)(cu[s] + p) * C)[c];
+  reinterpret_cast<uint4*>(col + ((int64_t)m * K + j) * C)[c] = v;
+}
+
+struct LstmArgs {
+  const float* xg;   // [M, 2*4H] fp32: W_ih x + b_ih + b_hh, direction d at column d*4H
+  const bf16* whh;   // [2][4H, H], direction-major, gates i f g o
+  float* out;        // output rows of 2H fp32, direction d at column d*H
+  int out_T;         // padded T (row = seq*T + t), or 0 for packed rows (cu[seq] + t)
+  const int* cu;     // [n_seq + 1]
+  int n_seq;
+  const int* status;
+};
+
+__device__ __forceinline__ float sigmoid_f(float x) {
+  return __builtin_amdgcn_rcpf(1.0f + fast_exp2(-x * kLog2e));
+}
+__device__ __forceinline__ float tanh_f(float x) { return 2.0f * sigmoid_f(2.0f * x) - 1.0f; }
+
+// LSTM recurrence.  Grid (ceil(n_seq / 32), 2 directions), 8 waves.  The
+// workgroup carries 32 sequences of one direction through their own
+// lengths: the forward direction visits t = 0 .. L-1, the backward one
+// t = L-1 .. 0, so padding never enters either scan (the masking that the
+// "Kokoro-82M-LiteRT" card warns about).  Each step is G^T = W_hh h^T on
+// the matrix cores: wave w owns units [32w, 32w+32) of all four gates (A
+// = those W_hh rows, streamed from L2), the B operand is h_{t-1} of the 32
+// sequences, kept in LDS as bf16; so every lane holds the i, f, g, o
+// pre-activations of the same 16 (unit, sequence) pairs and updates their
+// cell state (fp32, in registers) without any exchange.
+__global__ void __launch_bounds__(512)
+lstm_kernel(LstmArgs a) {
+  constexpr int H = kLstmH, LDH = H + 8;  // padded rows: conflict-free fragment reads
+  __shared__ __attribute__((aligned(16))) bf16 hs[2][kLstmSeq * LDH];
+  if (*a.status != 0) return;
+  const int d = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, hh = lane >> 5;
+  const int seq = blockIdx.x * kLstmSeq + l32;  // this lane's sequence (MFMA column)
+  const bool sv = seq < a.n_seq;
+  const int start = sv ? a.cu[seq] : 0;
+  const int L = sv ? a.cu[seq + 1] - start : 0;
+  int Lmax = L;
+#pragma unroll
+  for (int off = 16; off >= 1; off >>= 1) Lmax = max(Lmax, __shfl_xor(Lmax, off, 64));
+
+  for (int i = tid; i < kLstmSeq * LDH; i += 512) hs[0][i] = (bf16)0.0f;
+  float c[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) c[r] = 0.f;
+  const bf16* __restrict__ W = a.whh + (int64_t)d * 4 * H * H;
+  const int ubase = 32 * wave + 4 * hh;  // unit of register r: ubase + 8*(r/4) + r%4
+  __syncthreads();
+
+  for (int tau = 0; tau < Lmax; ++tau) {
+    const int cur = tau & 1;
+    const bool act = tau < L;
+    const int t = d == 0 ? tau : L - 1 - tau;
+    const int64_t row = (int64_t)start + t;
+    // input projection of this token (prefetched ahead of the products)
+    f32x4 xv[4][4];
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        xv[g][q] = act ? *reinterpret_cast<const f32x4*>(a.xg + row * (8 * H) + d * 4 * H + g * H +
+                                                         ubase + 8 * q)
+                       : f32x4{0.f, 0.f, 0.f, 0.f};
+    f32x16 acc[4];
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[g][r] = 0.f;
+    const bf16* hb = hs[cur] + l32 * LDH + hh * 8;
+#pragma unroll 4
+    for (int kk = 0; kk < H / 16; ++kk) {
+      const bf16x8 b = *reinterpret_cast<const bf16x8*>(hb + kk * 16);
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const bf16x8 w = *reinterpret_cast<const bf16x8*>(
+            W + (int64_t)(g * H + 32 * wave + l32) * H + kk * 16 + hh * 8);
+        acc[g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(w, b, acc[g], 0, 0, 0);
+      }
+    }
+    bf16* hn = hs[cur ^ 1] + l32 * LDH;
+    const int64_t orow = a.out_T ? (int64_t)seq * a.out_T + t : row;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      float hv[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 4 * q + e;
+        const float zi = acc[0][r] + xv[0][q][e], zf = acc[1][r] + xv[1][q][e];
+        const float zg = acc[2][r] + xv[2][q][e], zo = acc[3][r] + xv[3][q][e];
+        const float cn = sigmoid_f(zf) * c[r] + sigmoid_f(zi) * tanh_f(zg);
+        hv[e] = sigmoid_f(zo) * tanh_f(cn);
+        c[r] = cn;
+      }
+      const int u = ubase + 8 * q;
+      Tr<bf16>::store4(hn + u, hv[0], hv[1], hv[2], hv[3]);
+      if (act)
+        *reinterpret_cast<f32x4*>(a.out + orow * (2 * H) + d * H + u) =
+            f32x4{hv[0], hv[1], hv[2], hv[3]};
+    }
+    __syncthreads();  // h_t complete in hs[cur^1]; hs[cur] free for step tau+1's writes
+  }
+}
+
+}  // namespace albert

@@ -287,6 +287,101 @@ int albert_expand(const float* feat, const int32_t* dur, const int32_t* cu_tok, 
                   int total, int C, float* out, int64_t max_frames, int32_t* cu_frames,
                   void* ws, size_t ws_bytes, void* hip_stream, unsigned flags);
 
+/* ---- Kokoro's parallel text encoder ----------------------------------------
+ * The second path on the same phoneme IDs ("How Kokoro TTS Works and Where
+ * CKE Stands", the component list: embedding -> three weight-normalized
+ * convolutions -> bidirectional LSTM, beside the ALBERT; "How I want CKE to
+ * stitch it": its own [512, T] features).  Sizes and blocks the pages leave
+ * open follow the StyleTTS 2 text encoder Kokoro inherits: 512 channels,
+ * convolutions of width 5 zero-padded at each sequence's ends, each followed
+ * by a LayerNorm over the channels and a LeakyReLU; an LSTM of 256 units
+ * per direction (gates i, f, g, o; zero initial state) whose backward scan
+ * starts at each sequence's own last token (the masking the
+ * "Kokoro-82M-LiteRT" card calls for).  Storage is bf16 with fp32
+ * accumulation, gate arithmetic and cell state; output fp32, token-major
+ * [.., 512] (forward half, then backward half). */
+typedef struct albert_text_config {
+  int32_t vocab;    /* embedding rows (Kokoro: 178)                         */
+  int32_t channels; /* width C of the embedding and convolutions (512)      */
+  int32_t kernel;   /* convolution width: odd, 1..7 (5)                     */
+  int32_t n_conv;   /* convolution blocks: 1..8 (3)                         */
+  int32_t hidden;   /* LSTM units per direction (must be 256)              */
+  float ln_eps;     /* LayerNorm epsilon (1e-5)                             */
+  float slope;      /* LeakyReLU negative slope (0.2)                       */
+} albert_text_config;
+
+typedef struct albert_text_ctx albert_text_ctx; /* opaque; owns device weights */
+
+/* Fill *cfg with the configuration above. */
+int albert_text_default_config(albert_text_config* cfg);
+
+/* Weight tensors in canonical order:
+ *   emb [vocab, C];
+ *   per block i: conv<i>.v [C, C*K] (row-major [C_out][C_in][K], the
+ *     direction of the weight-normalized kernel), conv<i>.g [C] (its norm:
+ *     W = g * v / ||v|| over each output channel's C*K values), conv<i>.b
+ *     [C], conv<i>.ln.g [C], conv<i>.ln.b [C];
+ *   per direction (fwd, then bwd): lstm.<d>.w_ih [4H, C], lstm.<d>.w_hh
+ *     [4H, H], lstm.<d>.b_ih [4H], lstm.<d>.b_hh [4H].
+ * albert_text_n_tensors returns 1 + 5*n_conv + 8 (-1 for a bad config). */
+int albert_text_n_tensors(const albert_text_config* cfg);
+const char* albert_text_tensor_name(const albert_text_config* cfg, int index);
+int albert_text_tensor_shape(const albert_text_config* cfg, int index, int64_t* rows,
+                             int64_t* cols);
+
+/* One device copy of the text encoder's weights (bf16; vectors fp32).  The
+ * weight normalization is applied here, in double precision (a zero
+ * direction row is ALBERT_E_ARG); the two LSTM biases are summed.  Host
+ * tensors as albert_load_weights; allocates, and synchronises hip_stream. */
+int albert_text_load_weights(albert_text_ctx** ctx, const albert_text_config* cfg,
+                             const float* const* host_tensors, void* hip_stream);
+
+/* Workspace bytes for n_seq sequences and max_rows token rows (0 for
+ * invalid arguments). */
+size_t albert_text_workspace_bytes(const albert_text_ctx* ctx, int n_seq, int64_t max_rows);
+
+/* Padded batch: ids dev int32 [B, T], lengths dev int32 [B] in [1, T]
+ * (T >= 1, B*T < 2^31); out dev fp32 [B, T, 2*hidden], pad rows written
+ * as 0.  Validation, errors, workspace rules and flags as albert_encode. */
+int albert_text_encode(albert_text_ctx* ctx, const int32_t* ids, const int32_t* lengths, int B,
+                       int T, float* out, void* ws, size_t ws_bytes, void* hip_stream,
+                       unsigned flags);
+
+/* Packed batch: ids dev int32 [total], cu_seqlens dev int32 [n + 1], every
+ * length in [1, max_len]; out dev fp32 [total, 2*hidden].  As
+ * albert_encode_varlen. */
+int albert_text_encode_varlen(albert_text_ctx* ctx, const int32_t* ids, const int32_t* cu_seqlens,
+                              int n, int total, int max_len, float* out, void* ws,
+                              size_t ws_bytes, void* hip_stream, unsigned flags);
+
+/* Checkpoints in the workspace after a request (as albert_tap):
+ *   0 STATUS int32 [1]   1 CU int32 [n_seq + 1]
+ *   2 EMB  bf16 [rows, C]    embedding rows
+ *   3 CONV bf16 [rows, C]    the last convolution block's output
+ *   4 XG   fp32 [rows, 8H]   LSTM input projection plus both biases,
+ *                            forward gates then backward gates */
+enum albert_text_tap_kind {
+  ALBERT_TT_STATUS = 0, ALBERT_TT_CU = 1, ALBERT_TT_EMB = 2, ALBERT_TT_CONV = 3, ALBERT_TT_XG = 4
+};
+int albert_text_tap(const albert_text_ctx* ctx, int n_seq, int64_t max_rows, int tap,
+                    size_t* offset, size_t* bytes, int64_t* row_stride);
+
+/* Kernel kinds of the text path, for albert_text_time_kernel() (same
+ * contract as albert_time_kernel). */
+enum albert_text_kernel_kind {
+  ALBERT_TK_EMBED = 0,    /* embedding gather                               */
+  ALBERT_TK_UNFOLD = 1,   /* unfolded convolution input, once per block     */
+  ALBERT_TK_CONV = 2,     /* convolution GEMM + LayerNorm + LeakyReLU       */
+  ALBERT_TK_LSTM_IN = 3,  /* LSTM input projection, both directions         */
+  ALBERT_TK_LSTM = 4,     /* LSTM recurrence, both directions               */
+  ALBERT_TK_COUNT = 5
+};
+int albert_text_time_kernel(albert_text_ctx* ctx, int kind, int max_launches);
+int albert_text_kernel_time(albert_text_ctx* ctx, int* launches, double* total_ms);
+
+/* Release the text context's device memory.  NULL is accepted. */
+void albert_text_free(albert_text_ctx* ctx);
+
 /* Release the context's device memory.  NULL is accepted. */
 void albert_free(albert_ctx* ctx);
 

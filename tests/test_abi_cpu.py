@@ -8,6 +8,8 @@ import ctypes
 import os
 import re
 
+import numpy as np
+
 import pytest
 
 import synth
@@ -112,3 +114,27 @@ def test_status_strings(L):
     for code in A.STATUS_NAMES:
         assert A.status_str(code)
     assert A.status_str(99) == "unknown status"
+
+
+def test_text_encoder_tensor_table(L):
+    """The text path's tensor names and shapes follow synth.TextConfig."""
+    import albert_transformer_amd as A
+    c = A.text_default_config()
+    k = synth.TEXT
+    for f in ("vocab", "channels", "kernel", "n_conv", "hidden"):
+        assert getattr(c, f) == getattr(k, f), f
+    names = k.tensor_names()
+    assert L.albert_text_n_tensors(ctypes.byref(c)) == len(names) == 24
+    shapes = k.shapes()
+    for i, name in enumerate(names):
+        assert L.albert_text_tensor_name(ctypes.byref(c), i).decode() == name
+        r, cc = ctypes.c_int64(), ctypes.c_int64()
+        assert L.albert_text_tensor_shape(ctypes.byref(c), i, ctypes.byref(r), ctypes.byref(cc)) == 0
+        assert r.value * cc.value == int(np.prod(shapes[name])) and r.value == shapes[name][0]
+    assert L.albert_text_tensor_name(ctypes.byref(c), len(names)) is None
+    for bad in (dict(channels=256), dict(kernel=4), dict(kernel=9), dict(n_conv=0),
+                dict(n_conv=9), dict(hidden=128), dict(ln_eps=0.0)):
+        assert L.albert_text_n_tensors(ctypes.byref(A.text_default_config(**bad))) == -1
+    assert L.albert_text_workspace_bytes(None, 1, 1) == 0
+    assert L.albert_text_encode(None, None, None, 1, 8, None, None, 0, None, 0) == A.E_ARG
+    L.albert_text_free(None)
