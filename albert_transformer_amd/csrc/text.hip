@@ -33,7 +33,7 @@ struct albert_text_ctx {
   std::vector<const float*> conv_b, ln_g, ln_b;
   const bf16* w_ih;                 // [8H, C]: forward gates, then backward gates
   const float* b_gates;             // [8H]: b_ih + b_hh
-  const bf16* w_hh;                 // [2][4H, H]
+  const bf16* w_hh;                 // both directions, in the recurrence's fragment order
   int time_kind = -1;
   int n_timed = 0;
   std::vector<hipEvent_t> ev;
@@ -312,7 +312,18 @@ int albert_text_load_weights(albert_text_ctx** out_ctx, const albert_text_config
     for (int64_t e = 0; e < 4 * H * C; ++e) bf(s_wih)[d * 4 * H * C + e] = bf16_bits(wih[e]);
     for (int64_t e = 0; e < 4 * H; ++e)
       fp(s_wih + 1)[d * 4 * H + e] = (float)((double)bih[e] + bhh[e]);
-    for (int64_t e = 0; e < 4 * H * H; ++e) bf(s_wih + 2)[d * 4 * H * H + e] = bf16_bits(whh[e]);
+    // fragment order [d][wave 8][k-step H/16][gate 4][lane 64][8]: lane
+    // (l32, hh) of wave w holds row g*H + 32w + l32, columns kk*16 + hh*8 ..
+    uint16_t* wd = bf(s_wih + 2) + d * 4 * H * H;
+    for (int64_t wv = 0; wv < 8; ++wv)
+      for (int64_t kk = 0; kk < H / 16; ++kk)
+        for (int64_t g = 0; g < 4; ++g)
+          for (int64_t ln = 0; ln < 64; ++ln)
+            for (int64_t e = 0; e < 8; ++e) {
+              const int64_t r = g * H + 32 * wv + (ln & 31);
+              const int64_t k = kk * 16 + (ln >> 5) * 8 + e;
+              wd[(((wv * (H / 16) + kk) * 4 + g) * 64 + ln) * 8 + e] = bf16_bits(whh[r * H + k]);
+            }
   }
 
   albert_text_ctx* ctx = new (std::nothrow) albert_text_ctx();

@@ -60,7 +60,7 @@ unfold_kernel(const bf16* __restrict__ x, const int* __restrict__ row_seq,
 
 struct LstmArgs {
   const float* xg;   // [M, 2*4H] fp32: W_ih x + b_ih + b_hh, direction d at column d*4H
-  const bf16* whh;   // [2][4H, H], direction-major, gates i f g o
+  const bf16* whh;   // W_hh of both directions in fragment order (see lstm_kernel)
   float* out;        // output rows of 2H fp32, direction d at column d*H
   int out_T;         // padded T (row = seq*T + t), or 0 for packed rows (cu[seq] + t)
   const int* cu;     // [n_seq + 1]
@@ -83,6 +83,8 @@ __device__ __forceinline__ float tanh_f(float x) { return 2.0f * sigmoid_f(2.0f 
 // sequences, kept in LDS as bf16; so every lane holds the i, f, g, o
 // pre-activations of the same 16 (unit, sequence) pairs and updates their
 // cell state (fp32, in registers) without any exchange.
+// W_hh is stored in fragment order -- [d][wave][k-step][gate][lane][8] --
+// so that each wave-wide fragment load reads one contiguous kilobyte.
 __global__ void __launch_bounds__(512)
 lstm_kernel(LstmArgs a) {
   constexpr int H = kLstmH, LDH = H + 8;  // padded rows: conflict-free fragment reads
@@ -103,39 +105,63 @@ lstm_kernel(LstmArgs a) {
   float c[16];
 #pragma unroll
   for (int r = 0; r < 16; ++r) c[r] = 0.f;
-  const bf16* __restrict__ W = a.whh + (int64_t)d * 4 * H * H;
+  const bf16* __restrict__ W = a.whh + ((int64_t)d * 8 + wave) * (H / 16) * 4 * 64 * 8;
   const int ubase = 32 * wave + 4 * hh;  // unit of register r: ubase + 8*(r/4) + r%4
   __syncthreads();
+
+  // W_hh fragment of k-step kk for gate g (rows g*H + 32*wave + l32,
+  // columns kk*16 + hh*8 ..): one contiguous kilobyte per wave.
+  auto wload = [&](int kk, int g) __attribute__((always_inline)) {
+    return *reinterpret_cast<const bf16x8*>(W + ((kk * 4 + g) * 64 + lane) * 8);
+  };
+  constexpr int KS = H / 16;  // 16 k-steps
+  constexpr int PD = 3;       // W_hh prefetch distance (k-steps)
+  static_assert(KS % (PD + 1) == 0, "the fragment ring must wrap at a step boundary");
+
+  // Gate inputs of step tau as the accumulators' starting value (the MFMA
+  // adds into them).
+  f32x16 acc[4];
+  auto xload = [&](int tau) __attribute__((always_inline)) {
+    const bool act = tau < L;
+    const int t = d == 0 ? tau : L - 1 - tau;
+    const float* xr = a.xg + ((int64_t)start + t) * (8 * H) + d * 4 * H + ubase;
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f32x4 v = act ? *reinterpret_cast<const f32x4*>(xr + g * H + 8 * q)
+                            : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[g][4 * q + e] = v[e];
+      }
+  };
+  // W_hh streams from L2 through a ring of PD+1 k-steps, PD k-steps of
+  // loads in flight behind the matrix cores; the stream runs on across step
+  // boundaries (W_hh is the same for every step), so no step starts cold.
+  bf16x8 wr[PD + 1][4];
+  xload(0);
+#pragma unroll
+  for (int kk = 0; kk < PD; ++kk)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) wr[kk][g] = wload(kk, g);
 
   for (int tau = 0; tau < Lmax; ++tau) {
     const int cur = tau & 1;
     const bool act = tau < L;
     const int t = d == 0 ? tau : L - 1 - tau;
     const int64_t row = (int64_t)start + t;
-    // input projection of this token (prefetched ahead of the products)
-    f32x4 xv[4][4];
-#pragma unroll
-    for (int g = 0; g < 4; ++g)
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        xv[g][q] = act ? *reinterpret_cast<const f32x4*>(a.xg + row * (8 * H) + d * 4 * H + g * H +
-                                                         ubase + 8 * q)
-                       : f32x4{0.f, 0.f, 0.f, 0.f};
-    f32x16 acc[4];
-#pragma unroll
-    for (int g = 0; g < 4; ++g)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[g][r] = 0.f;
     const bf16* hb = hs[cur] + l32 * LDH + hh * 8;
-#pragma unroll 4
-    for (int kk = 0; kk < H / 16; ++kk) {
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) wr[(kk + PD) % (PD + 1)][g] = wload((kk + PD) % KS, g);
       const bf16x8 b = *reinterpret_cast<const bf16x8*>(hb + kk * 16);
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const bf16x8 w = *reinterpret_cast<const bf16x8*>(
-            W + (int64_t)(g * H + 32 * wave + l32) * H + kk * 16 + hh * 8);
-        acc[g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(w, b, acc[g], 0, 0, 0);
-      }
+      for (int g = 0; g < 4; ++g)
+        acc[g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wr[kk % (PD + 1)][g], b, acc[g], 0, 0, 0);
+      // keep each k-step's loads in place: hoisting them all would hold
+      // every W_hh fragment of the step in registers at once
+      __builtin_amdgcn_sched_barrier(0);
     }
     bf16* hn = hs[cur ^ 1] + l32 * LDH;
     const int64_t orow = a.out_T ? (int64_t)seq * a.out_T + t : row;
@@ -145,8 +171,7 @@ lstm_kernel(LstmArgs a) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = 4 * q + e;
-        const float zi = acc[0][r] + xv[0][q][e], zf = acc[1][r] + xv[1][q][e];
-        const float zg = acc[2][r] + xv[2][q][e], zo = acc[3][r] + xv[3][q][e];
+        const float zi = acc[0][r], zf = acc[1][r], zg = acc[2][r], zo = acc[3][r];
         const float cn = sigmoid_f(zf) * c[r] + sigmoid_f(zi) * tanh_f(zg);
         hv[e] = sigmoid_f(zo) * tanh_f(cn);
         c[r] = cn;
@@ -157,6 +182,7 @@ lstm_kernel(LstmArgs a) {
         *reinterpret_cast<f32x4*>(a.out + orow * (2 * H) + d * H + u) =
             f32x4{hv[0], hv[1], hv[2], hv[3]};
     }
+    xload(tau + 1);   // next step's gate inputs, in flight across the barrier
     __syncthreads();  // h_t complete in hs[cur^1]; hs[cur] free for step tau+1's writes
   }
 }

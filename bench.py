@@ -185,6 +185,113 @@ def hailo_fidelity(enc, cfg, weights, n: int = 16) -> dict:
             "mse_mean": float(np.mean(mse)), "range": [round(min(lo), 3), round(max(hi), 3)]}
 
 
+TEXT_METRIC = ("text-encoder tokens/sec at B=256,T=128 bf16 (Kokoro's parallel text path); "
+               "% of MFMA roofline")
+
+
+def text_kernel_flops(kind: str, tokens: int, tc) -> float:
+    """Algorithmic FLOP of one launch of a text-path kernel kind."""
+    C, K, H = tc.channels, tc.kernel, tc.hidden
+    return {"conv": 2.0 * tokens * C * K * C, "lstm_in": 2.0 * tokens * C * 8 * H,
+            "lstm": 2.0 * 2 * tokens * 4 * H * H}.get(kind, 0.0)
+
+
+def bench_text(args) -> int:
+    """The parallel text encoder on a workload's batch (one JSON line)."""
+    import torch
+    import albert_transformer_amd as A
+    import oracle.text_encoder as te
+    tc = synth.TEXT
+    wl = synth.make_workload(args.config)
+    weights = synth.make_text_weights(tc)
+    enc = A.TextEncoder(weights)
+    if wl.packed:
+        raise SystemExit("the text bench takes a padded workload")
+    ids = torch.from_numpy(wl.ids).cuda()
+    lens = torch.from_numpy(wl.lengths).cuda()
+    out = torch.empty((wl.n_seq, wl.T, 2 * tc.hidden), dtype=torch.float32, device="cuda")
+    ws = enc.new_workspace(wl.n_seq, wl.n_seq * wl.T)
+
+    def step():
+        return enc.encode_raw(ids, lens, out, ws, flags=A.ASYNC)
+
+    for _ in range(args.warmup):
+        assert step() == A.OK
+    torch.cuda.synchronize()
+    if A.read_status(ws) != A.OK:
+        raise SystemExit("text encoder rejected the workload")
+    per_kind = {}
+    for kind in A.TEXT_KERNEL_KINDS:
+        enc.time_kernel(kind)
+        for _ in range(3):
+            step()
+        n, ms = enc.kernel_time()
+        per_kind[kind] = {"launches_per_step": n // 3, "ms_per_step": ms / 3,
+                          "ms_per_launch": ms / max(n, 1)}
+    enc.time_kernel(None)
+    dominant = max(per_kind, key=lambda k: per_kind[k]["ms_per_step"])
+    enc.time_kernel(dominant, max_launches=max(per_kind[dominant]["launches_per_step"] * args.steps, 1))
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    n_dom, ms_dom = enc.kernel_time()
+    enc.time_kernel(None)
+    if A.read_status(ws) != A.OK:
+        raise SystemExit("text encoder failed during timing")
+    tokens = wl.tokens
+    launch_ms = ms_dom / max(n_dom, 1)
+    achieved = text_kernel_flops(dominant, tokens, tc) / (launch_ms * 1e-3) / 1e12
+    ms_step = 1e3 * elapsed / args.steps
+    flops_step = sum(text_kernel_flops(k, tokens, tc) * v["launches_per_step"]
+                     for k, v in per_kind.items())
+
+    base = None
+    if args.cpu_seconds > 0:
+        from threadpoolctl import threadpool_info
+        TW = te.prepare_text_weights(weights, tc, "bf16")
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()
+                       if i.get("user_api") == "blas"] or [1])
+        got = out.cpu().numpy()
+        done = tok = 0
+        worst = 0.0
+        t0 = time.perf_counter()
+        for b in np.random.default_rng(7).permutation(wl.n_seq):
+            L = int(wl.lengths[b])
+            ref = te.text_encode_sequence(wl.ids[b, :L], TW, tc)
+            worst = max(worst, float(np.abs(got[b, :L] - ref).max()))
+            done += 1
+            tok += L
+            if time.perf_counter() - t0 >= args.cpu_seconds:
+                break
+        dt = time.perf_counter() - t0
+        base = {"value": tok / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+                "sample": f"{done} of {wl.n_seq} sequences ({tok} tokens), float64 NumPy, "
+                          f"{dt:.1f} s", "parity_max_abs": worst}
+    line = {
+        "metric": TEXT_METRIC, "value": round(tokens * args.steps / elapsed, 1),
+        "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded text-encoder weights, uniform phoneme ids)",
+        "config": {"workload": f"text encoder, {wl.name}", "sequences": wl.n_seq, "T": wl.T,
+                   "tokens_per_step": tokens, "conv_blocks": tc.n_conv, "kernel": tc.kernel,
+                   "lstm_units": tc.hidden},
+        "tflops_end_to_end": round(flops_step / (ms_step * 1e-3) / 1e12, 2),
+        "roofline": {"kernel": dominant, "bound": "mfma", "achieved": round(achieved, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "ms_per_launch": round(launch_ms, 5), "launches_timed": n_dom},
+        "kernels_ms_per_step": {k: round(v["ms_per_step"], 4) for k, v in per_kind.items()},
+        "cpu_baseline": base, "source_sha": source_hash(),
+    }
+    print(json.dumps(line), flush=True)
+    enc.close()
+    return 0
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -195,6 +302,8 @@ def main(argv=None) -> int:
                     help="wall budget of the oracle CPU baseline (0 = skip)")
     ap.add_argument("--dtype", choices=("bf16", "fp8", "f32"), default=None,
                     help="override the workload's compute type (fp8: E4M3 operands)")
+    ap.add_argument("--model", choices=("albert", "text"), default="albert",
+                    help="albert: the phoneme encoder (default); text: the parallel text path")
     ap.add_argument("--groups", type=int, default=1,
                     help="distinct layer weight sets (1 = Kokoro's full sharing)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -210,6 +319,8 @@ def main(argv=None) -> int:
     import albert_transformer_amd as A
 
     torch.cuda.set_device(0)
+    if args.model == "text":
+        return bench_text(args)
     wl = synth.make_workload(args.config)
     dtype = wl.dtype if args.dtype is None else args.dtype
     cfg = synth.Config(n_groups=args.groups)
