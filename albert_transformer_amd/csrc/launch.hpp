@@ -25,19 +25,27 @@ void launch_gemm(GemmArgs g, int64_t max_rows, int grid_cap, hipStream_t s) {
 }
 
 // Large tiles for plain and GELU epilogues; full-row tiles for LayerNorm.
-// bf16 bias/GELU GEMMs with at least 12 (an even number of) K slices keep
-// each tile's outputs in registers and write them during the next tile.
-// E4M3 operands stage 64-byte rows (one 64-deep MFMA step per slice).
+// bf16 tiles use 8 waves (two per SIMD, so one wave's LDS waits hide
+// behind the other's matrix-core work): the bias GEMMs with at least 12
+// (an even number of) K slices as 2 x 4 waves keeping each tile's outputs
+// in registers to store them during the next tile, the GELU GEMM as 4 x 2
+// waves storing directly (the faster pair on the encoder's shapes).  E4M3
+// operands stage 64-byte rows (one 64-deep MFMA step per slice).
 template <typename T, bool F8, int EPI>
 void gemm_big(GemmArgs g, int64_t max_rows, int grid_cap, hipStream_t s) {
-  constexpr bool can_defer =
-      std::is_same<T, bf16>::value && !F8 && (EPI == EPI_BIAS || EPI == EPI_GELU);
+  constexpr bool bf = std::is_same<T, bf16>::value && !F8;
   constexpr int RB = F8 ? 64 : 128;
   const int slices = g.K * (F8 ? 1 : (int)sizeof(T)) / RB;
-  if (can_defer && slices >= 12 && slices % 2 == 0 && !g.Y8)
-    launch_gemm<T, F8, 256, 256, 2, 2, RB, 2, EPI, can_defer>(g, max_rows, grid_cap, s);
-  else
+  if constexpr (bf && EPI == EPI_GELU) {
+    launch_gemm<T, F8, 256, 256, 4, 2, RB, 2, EPI, false>(g, max_rows, grid_cap, s);
+  } else if constexpr (bf && EPI == EPI_BIAS) {
+    if (slices >= 12 && slices % 2 == 0 && !g.Y8)
+      launch_gemm<T, F8, 256, 256, 2, 4, RB, 2, EPI, true>(g, max_rows, grid_cap, s);
+    else
+      launch_gemm<T, F8, 256, 256, 2, 2, RB, 2, EPI, false>(g, max_rows, grid_cap, s);
+  } else {
     launch_gemm<T, F8, 256, 256, 2, 2, RB, 2, EPI, false>(g, max_rows, grid_cap, s);
+  }
 }
 // 128-row tiles need at least a full wave of them; smaller batches use
 // 64-row tiles (4 waves, one per SIMD) to spread over more CUs.
