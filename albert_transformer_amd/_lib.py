@@ -21,6 +21,7 @@ STATUS_NAMES = {OK: "OK", E_ARG: "E_ARG", E_WORKSPACE: "E_WORKSPACE",
 F32, BF16, FP8 = 0, 1, 2
 DTYPES = {"f32": F32, "bf16": BF16, "fp8": FP8}
 ASYNC = 1
+UNFUSED = 2
 N_TENSORS = 25
 TAPS = {"status": 0, "cu": 1, "row_seq": 2, "row_pos": 3, "emb": 4, "x": 5,
         "qkv": 6, "ctx": 7, "x1": 8, "g": 9, "x8": 10, "x1_8": 11}
@@ -36,7 +37,8 @@ EXPORTS = ("albert_default_config", "albert_n_tensors", "albert_tensor_name",
            "albert_text_time_kernel", "albert_text_kernel_time", "albert_text_free")
 TEXT_TAPS = {"status": 0, "cu": 1, "emb": 2, "conv": 3, "xg": 4}
 TEXT_KERNEL_KINDS = ("embed", "unfold", "conv", "lstm_in", "lstm")
-KERNEL_KINDS = ("embed", "proj", "qkv", "attn", "attn_out_ln", "ffn1_gelu", "ffn2_ln", "out")
+KERNEL_KINDS = ("embed", "proj", "qkv", "attn", "attn_out_ln", "ffn1_gelu", "ffn2_ln", "out",
+                "qkv_attn")
 
 
 class Config(ctypes.Structure):

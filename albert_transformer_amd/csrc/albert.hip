@@ -26,6 +26,7 @@
 #include "gemm.hpp"
 #include "launch.hpp"
 #include "prologue.hpp"
+#include "qkv_attention.hpp"
 
 using namespace albert;
 
@@ -33,6 +34,8 @@ using namespace albert;
 // plus per-row E8M0 exponents under ALBERT_FP8 -- vectors fp32).
 struct LayerW {
   const void *qkv_w, *o_w, *ffn1_w, *ffn2_w;
+  const bf16* qkv_wh;  // bf16 only: [12][192][768] per head q/8 | k | v rows
+  const float* qkv_bh; // [12][192]
   const unsigned char *qkv_e, *o_e, *ffn1_e, *ffn2_e;
   const float *qkv_b, *o_b, *ln1_g, *ln1_b, *ffn1_b, *ffn2_b, *ln2_g, *ln2_b;
 };
@@ -205,7 +208,7 @@ void timed(albert_ctx* c, int kind, hipStream_t s, Fn&& fn) {
 template <typename T, bool F8>
 int run(albert_ctx* c, const int32_t* ids, const int32_t* lens_or_cu, int n_seq, int pad_T,
         int64_t max_rows, int max_len, float* out, void* ws, hipStream_t s,
-        const float* feats = nullptr) {
+        const float* feats, unsigned flags) {
   const albert_config& cf = c->cfg;
   const Layout L = plan(c, n_seq, max_rows);
   char* w = static_cast<char*>(ws);
@@ -261,18 +264,33 @@ int run(albert_ctx* c, const int32_t* ids, const int32_t* lens_or_cu, int n_seq,
   timed(c, ALBERT_K_PROJ, s, [&] { gemm_big<T, F8, EPI_BIAS>(g, max_rows, c->grid_cap, s); });
 
   const int qtiles = (max_len + 127) / 128;
+  // Q|K|V and attention in one kernel when every sequence fits its 256-row
+  // tile (groups of S whole sequences); the unfused pair otherwise.
+  constexpr bool can_fuse = std::is_same<T, bf16>::value && !F8;
+  const bool fuse = can_fuse && !feats && max_len <= 256 && !(flags & ALBERT_UNFUSED);
+  const int S = 256 / std::max(max_len, 1);
+  const int64_t pairs = fuse ? (int64_t)((n_seq + S - 1) / S) * cf.heads : 0;
   for (int it = 0; it < cf.n_iter; ++it) {
     const LayerW& lw = c->layers[(size_t)((int64_t)it * cf.n_groups / cf.n_iter)];
-    g = base;  // fused Q|K|V projection
-    g.X = X8; g.ldx = H; g.W = lw.qkv_w; g.wexp = lw.qkv_e; g.bias = lw.qkv_b; g.Y = QKV;
-    g.ldy = 3 * H; g.N = 3 * H; g.K = H;
-    timed(c, ALBERT_K_QKV, s, [&] { gemm_big<T, F8, EPI_BIAS>(g, max_rows, c->grid_cap, s); });
+    if (fuse) {
+      QkvAttnArgs qa{static_cast<const bf16*>(X8), lw.qkv_wh, lw.qkv_bh,
+                     static_cast<bf16*>(CTX), cu, row_seq, status, n_seq, S, (int)pairs};
+      timed(c, ALBERT_K_QKV_ATTN, s, [&] {
+        hipLaunchKernelGGL(qkv_attention_kernel, dim3((unsigned)((pairs + 7) / 8 * 8)),
+                           dim3(512), 0, s, qa);
+      });
+    } else {
+      g = base;  // fused Q|K|V projection
+      g.X = X8; g.ldx = H; g.W = lw.qkv_w; g.wexp = lw.qkv_e; g.bias = lw.qkv_b; g.Y = QKV;
+      g.ldy = 3 * H; g.N = 3 * H; g.K = H;
+      timed(c, ALBERT_K_QKV, s, [&] { gemm_big<T, F8, EPI_BIAS>(g, max_rows, c->grid_cap, s); });
 
-    AttnArgs a{QKV, CTX, cu, status};
-    timed(c, ALBERT_K_ATTN, s, [&] {
-      hipLaunchKernelGGL((attention_kernel<T, F8>), dim3(n_seq, cf.heads, qtiles), dim3(256), 0,
-                         s, a);
-    });
+      AttnArgs a{QKV, CTX, cu, status};
+      timed(c, ALBERT_K_ATTN, s, [&] {
+        hipLaunchKernelGGL((attention_kernel<T, F8>), dim3(n_seq, cf.heads, qtiles), dim3(256),
+                           0, s, a);
+      });
+    }
 
     g = base;  // output projection + residual + LayerNorm
     g.X = CTX; g.ldx = H; g.W = lw.o_w; g.wexp = lw.o_e; g.bias = lw.o_b; g.R = X; g.ldr = H;
@@ -304,7 +322,7 @@ int run(albert_ctx* c, const int32_t* ids, const int32_t* lens_or_cu, int n_seq,
 
 // Dispatch on the context's dtype.
 template <typename... A>
-int run_any(albert_ctx* c, A... args) {
+int run_any(albert_ctx* c, A... args) {  // args end with (feats, flags)
   switch (c->dtype) {
     case ALBERT_BF16: return run<bf16, false>(c, args...);
     case ALBERT_FP8: return run<bf16, true>(c, args...);
@@ -377,7 +395,8 @@ int albert_load_weights(albert_ctx** out_ctx, const albert_config* cfg,
   enum { S_WORD, S_POS, S_TYPE, S_EMB_G, S_EMB_B, S_PROJ_W, S_PROJ_B, S_OUT_W, S_OUT_B,
          S_PROJ_E, S_OUT_E, S_LAYER0 };
   enum { L_QKV_W, L_QKV_B, L_O_W, L_O_B, L_LN1_G, L_LN1_B, L_F1_W, L_F1_B, L_F2_W, L_F2_B,
-         L_LN2_G, L_LN2_B, L_QKV_E, L_O_E, L_F1_E, L_F2_E, L_SEGS };
+         L_LN2_G, L_LN2_B, L_QKV_E, L_O_E, L_F1_E, L_F2_E, L_QKV_WH, L_QKV_BH, L_SEGS };
+  const bool hm = dtype == ALBERT_BF16;  // head-major Q|K|V copy for the fused kernel
   struct Seg { size_t off, bytes; };
   std::vector<Seg> seg;
   size_t off = 0;
@@ -410,6 +429,8 @@ int albert_load_weights(albert_ctx** out_ctx, const albert_config* cfg,
     add(f8 ? (size_t)H : 0);               // o exponents
     add(f8 ? (size_t)c.ffn : 0);           // ffn1 exponents
     add(f8 ? (size_t)H : 0);               // ffn2 exponents
+    add(hm ? (size_t)3 * H * H * 2 : 0);   // head-major q/8 | k | v
+    add(hm ? (size_t)3 * H * 4 : 0);       // their biases
   }
   std::vector<unsigned char> img(off, 0);
 
@@ -478,6 +499,20 @@ int albert_load_weights(albert_ctx** out_ctx, const albert_config* cfg,
     put_vec(s0 + L_F2_B, t[13], H, 1.f, 0);
     put_vec(s0 + L_LN2_G, t[14], H, 1.f, 0);
     put_vec(s0 + L_LN2_B, t[15], H, 1.f, 0);
+    if (hm) {  // head h: rows h*64.. of q (scaled), then of k, then of v
+      const int64_t D = c.head_dim, NH = c.heads;
+      uint16_t* wd = reinterpret_cast<uint16_t*>(img.data() + seg[s0 + L_QKV_WH].off);
+      float* bd = reinterpret_cast<float*>(img.data() + seg[s0 + L_QKV_BH].off);
+      for (int64_t hd = 0; hd < NH; ++hd)
+        for (int64_t part = 0; part < 3; ++part)
+          for (int64_t dd = 0; dd < D; ++dd) {
+            const int64_t src_row = hd * D + dd, dst_row = (hd * 3 + part) * D + dd;
+            const float sc = part == 0 ? qscale : 1.f;
+            for (int64_t k = 0; k < H; ++k)
+              wd[dst_row * H + k] = f32_to_bf16_bits(t[2 * part][src_row * H + k] * sc);
+            bd[dst_row] = t[2 * part + 1][src_row] * sc;
+          }
+    }
   }
 
   albert_ctx* ctx = new (std::nothrow) albert_ctx();
@@ -520,6 +555,8 @@ int albert_load_weights(albert_ctx** out_ctx, const albert_config* cfg,
     lw.ffn2_w = P(s0 + L_F2_W); lw.ffn2_b = Pf(s0 + L_F2_B);
     lw.ln2_g = Pf(s0 + L_LN2_G); lw.ln2_b = Pf(s0 + L_LN2_B);
     lw.qkv_e = Pe(s0 + L_QKV_E); lw.o_e = Pe(s0 + L_O_E);
+    lw.qkv_wh = reinterpret_cast<const bf16*>(P(s0 + L_QKV_WH));
+    lw.qkv_bh = Pf(s0 + L_QKV_BH);
     lw.ffn1_e = Pe(s0 + L_F1_E); lw.ffn2_e = Pe(s0 + L_F2_E);
   }
   *out_ctx = ctx;
@@ -545,7 +582,8 @@ int albert_encode(albert_ctx* ctx, const int32_t* ids, const int32_t* lengths, i
       overlaps(out, out_bytes, lengths, (size_t)B * 4) || overlaps(out, out_bytes, ws, need))
     return ALBERT_E_ALIAS;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const int rc = run_any(ctx, ids, lengths, B, T, rows, T, out, ws, s, (const float*)nullptr);
+  const int rc = run_any(ctx, ids, lengths, B, T, rows, T, out, ws, s, (const float*)nullptr,
+                         flags);
   return finish(rc, ws, s, flags);
 }
 
@@ -565,7 +603,7 @@ int albert_encode_varlen(albert_ctx* ctx, const int32_t* ids, const int32_t* cu_
     return ALBERT_E_ALIAS;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int rc = run_any(ctx, ids, cu_seqlens, n, 0, (int64_t)total, max_len, out, ws, s,
-                         (const float*)nullptr);
+                         (const float*)nullptr, flags);
   return finish(rc, ws, s, flags);
 }
 
@@ -586,7 +624,7 @@ int albert_encode_features(albert_ctx* ctx, const float* x, const int32_t* cu_se
     return ALBERT_E_ALIAS;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int rc = run_any(ctx, (const int32_t*)nullptr, cu_seqlens, n, 0, (int64_t)total, max_len,
-                         out, ws, s, x);
+                         out, ws, s, x, flags);
   return finish(rc, ws, s, flags);
 }
 

@@ -1,0 +1,272 @@
+// Fused Q|K|V projection and attention for one head of a group of whole
+// sequences (bf16).
+//
+// The layer's q, k, v projections ("Inside One Real ALBERT Layer", step 3)
+// and the masked-softmax attention (step 4; "How Kokoro TTS Works and Where
+// CKE Stands", "What ALBERT does here") computed in one workgroup, so q, k
+// and v of the group never leave the chip: the workgroup owns head h and a
+// group of S whole sequences of at most 256 rows in all (S = 256 / longest
+// length, chosen on the host), computes the 192 projected features of head
+// h (q/8 | k | v, the query scale folded into the weights) for those rows on
+// the matrix cores, stores them in LDS as bf16 (the same storage point as
+// the unfused path) and runs the attention of every query against the keys
+// of its own sequence.  Only the context leaves the workgroup.
+//
+// GEMM phase: 256 rows x 192 features, K = 768 in slices of 64 staged in
+// LDS by buffer_load ... lds DMA (two stages), 8 waves as 4 (rows) x 2
+// (features) of 64 x 96; weights are the MFMA A operand, tokens B (lane =
+// token), as in gemm.hpp.  Rows of the tile past the group belong to the
+// next group (or past M, where the range check reads zeros): their results
+// are never used.
+//
+// Attention phase: the stage buffers are reused for Q and K (row-major) and
+// V^T; wave w owns queries 32w .. 32w+31 of the tile, one per lane, as in
+// attention.hpp (S^T = K Q^T, online softmax per lane with the partner
+// half-wave, O^T = V^T P^T); a lane's keys are those of its own sequence,
+// so key blocks outside it are masked per lane.
+#pragma once
+
+#include "common.hpp"
+#include "gemm.hpp"
+
+namespace albert {
+
+struct QkvAttnArgs {
+  const bf16* X;        // [M, 768] layer input (row stride 768)
+  const bf16* Wh;       // [12][192][768]: per head q/8 | k | v weight rows
+  const float* bh;      // [12][192]: their biases
+  bf16* ctx;            // [M, 768] attention context
+  const int* cu;        // [n_seq + 1] packed row offsets
+  const int* row_seq;   // [M] sequence of each row
+  const int* status;
+  int n_seq;
+  int S;                // sequences per group
+  int n_pairs;          // groups * 12
+};
+
+__global__ void __launch_bounds__(512)
+qkv_attention_kernel(QkvAttnArgs a) {
+  typedef Tr<bf16> TR;
+  constexpr int H = 768, D = 64, NH = 12, BM = 256, BN = 3 * D;
+  constexpr int WGN = 2, NW = 8, NT = NW * 64;
+  constexpr int WTM = 64, WTN = 96, TM = 2, TN = 3;
+  constexpr int RB = 128, CPR = RB / 16, BK = RB / 2, RPI = 1024 / RB;
+  constexpr int NINST = (BM + BN) / RPI, IPW = NINST / NW;
+  constexpr int STAGE = (BM + BN) * RB;
+  constexpr int KSTEPS = BK / 16, KT = H / BK;
+  constexpr int LDQ = D + 8;       // Q and K rows (144 bytes)
+  constexpr int LDV = BM + 8;      // V^T rows (528 bytes)
+  static_assert(NINST % NW == 0 && (BM / RPI) % NW == 0 && NW % 2 == 0, "DMA split");
+  static_assert(KT % 2 == 0, "two stages");
+  static_assert(BM * LDQ * 2 + 32 * LDV * 2 <= STAGE, "attention buffers fit a stage");
+  __shared__ __attribute__((aligned(1024))) char lds0[STAGE];
+  __shared__ __attribute__((aligned(1024))) char lds1[STAGE];
+  __shared__ float bias_s[BN];
+
+  if (*a.status != 0) return;
+  // (group, head) pairs: consecutive pairs -- the 12 heads of a group --
+  // go to one XCD (workgroups are dealt to the 8 XCDs round-robin), so the
+  // group's rows of X are read from that XCD's L2 after the first head.
+  const int G = gridDim.x;
+  const int pair = (blockIdx.x % 8) * (G / 8) + blockIdx.x / 8;
+  if (pair >= a.n_pairs) return;
+  const int grp = pair / NH, h = pair % NH;
+  const int s0 = grp * a.S, s1 = min(s0 + a.S, a.n_seq);
+  const int r0 = a.cu[s0], nrows = a.cu[s1] - r0;  // <= 256 by the choice of S
+  const int M = a.cu[a.n_seq];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WGN, wn = wave % WGN;
+  const int l32 = lane & 31, hh = lane >> 5;
+
+  if (tid < BN) bias_s[tid] = a.bh[h * BN + tid];
+
+  // ---------------------------------------------------------- GEMM phase
+  const char* Xt = reinterpret_cast<const char*>(a.X) + (int64_t)r0 * H * 2;
+  const char* Wt = reinterpret_cast<const char*>(a.Wh) + (int64_t)h * BN * H * 2;
+  const int64_t xbytes = (int64_t)(M - r0) * H * 2;
+  const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<char*>(Xt), (short)0,
+      __builtin_amdgcn_readfirstlane((int)(xbytes > 0x7fffffff ? 0x7fffffff : xbytes)),
+      kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t wr =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(Wt), (short)0, BN * H * 2, kRsrcWord3);
+  const int lrow = lane / CPR;
+  const int lchunk = (lane % CPR) ^ swz_key<RB>(wave * RPI + lrow);
+  const int loff = lrow * H * 2 + lchunk * 16;
+  auto issue = [&](char* buf, int k0) __attribute__((always_inline)) {
+    int kb = k0 * 2;
+    asm volatile("" : "+s"(kb));
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) {
+      const int q = wave + i * NW;
+      char* dst = buf + q * RPI * RB;
+      if (i * NW * RPI < BM)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_ptr_t*)dst, 16, loff,
+                                                 kb + q * RPI * H * 2, 0, 0);
+      else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (lds_ptr_t*)dst, 16, loff,
+                                                 kb + (q * RPI - BM) * H * 2, 0, 0);
+    }
+  };
+  const int key = swz_key<RB>(l32);
+  const int xrow = (wm * WTM + l32) * RB;
+  const int wrow = (BM + wn * WTN + l32) * RB;
+  int coff[KSTEPS];
+#pragma unroll
+  for (int j = 0; j < KSTEPS; ++j) coff[j] = (((j * 16 + hh * 8) / 8) ^ key) * 16;
+
+  f32x16 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  auto compute = [&](const char* buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < KSTEPS; ++j) {
+      bf16x8 fx[TM], fw[TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+        fx[i] = TR::load(reinterpret_cast<const bf16*>(buf + xrow + i * 32 * RB + coff[j]));
+#pragma unroll
+      for (int jj = 0; jj < TN; ++jj)
+        fw[jj] = TR::load(reinterpret_cast<const bf16*>(buf + wrow + jj * 32 * RB + coff[j]));
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int jj = 0; jj < TN; ++jj) {
+          TR::mma(acc[i][jj], fw[jj], fx[i]);
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+    }
+  };
+#define ALBERT_QA_WAIT_BARRIER() asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory")
+  issue(lds0, 0);
+  for (int kt = 0; kt < KT; kt += 2) {
+    ALBERT_QA_WAIT_BARRIER();
+    issue(lds1, (kt + 1) * BK);
+    compute(lds0);
+    ALBERT_QA_WAIT_BARRIER();
+    if (kt + 2 < KT) issue(lds0, (kt + 2) * BK);
+    compute(lds1);
+  }
+#undef ALBERT_QA_WAIT_BARRIER
+  __syncthreads();  // every wave is done with the stage buffers
+
+  // Q and K rows [token][dim] at the start of lds0 / lds1, V^T [dim][token]
+  // after them, dims 0..31 in lds0 and 32..63 in lds1.
+  bf16* Qs = reinterpret_cast<bf16*>(lds0);
+  bf16* Ks = reinterpret_cast<bf16*>(lds1);
+  bf16* Vt0 = reinterpret_cast<bf16*>(lds0 + BM * LDQ * 2);
+  bf16* Vt1 = reinterpret_cast<bf16*>(lds1 + BM * LDQ * 2);
+  // acc[i][j][4q+e]: token wm*64 + 32i + l32, feature wn*96 + 32j + 8q + 4hh + e
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    const int tok = wm * WTM + i * 32 + l32;
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int f0 = wn * WTN + j * 32 + 8 * q + 4 * hh;  // 4 consecutive features
+        float o[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = acc[i][j][4 * q + e] + bias_s[f0 + e];
+        if (f0 < D) {
+          TR::store4(Qs + tok * LDQ + f0, o[0], o[1], o[2], o[3]);
+        } else if (f0 < 2 * D) {
+          TR::store4(Ks + tok * LDQ + (f0 - D), o[0], o[1], o[2], o[3]);
+        } else {
+          const int d0 = f0 - 2 * D;
+          bf16* vt = d0 < 32 ? Vt0 + d0 * LDV : Vt1 + (d0 - 32) * LDV;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) vt[e * LDV + tok] = (bf16)o[e];
+        }
+      }
+  }
+  __syncthreads();
+
+  // ----------------------------------------------------- attention phase
+  const int qr = wave * 32 + l32;  // this lane's query (tile row)
+  int ks = 0, ke = 0;              // its keys: tile rows [ks, ke)
+  if (qr < nrows) {
+    const int s = a.row_seq[r0 + qr];
+    ks = a.cu[s] - r0;
+    ke = a.cu[s + 1] - r0;
+  }
+  int kmin = qr < nrows ? ks : BM, kmax = ke;
+#pragma unroll
+  for (int off = 16; off >= 1; off >>= 1) {
+    kmin = min(kmin, __shfl_xor(kmin, off, 64));
+    kmax = max(kmax, __shfl_xor(kmax, off, 64));
+  }
+  const int kb0 = kmin / 32 * 32;  // wave-uniform key-block range
+  const int kb1 = (kmax + 31) / 32 * 32;
+
+  bf16x8 fq[4];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) fq[kk] = TR::load(Qs + qr * LDQ + kk * 16 + hh * 8);
+  f32x16 o[2];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) { o[0][r] = 0.f; o[1][r] = 0.f; }
+  float mrun = kNegInf, lrun = 0.f;
+  for (int kbase = kb0; kbase < kb1; kbase += 32) {
+    f32x16 sc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sc[r] = 0.f;
+    const bf16* kp = Ks + (kbase + l32) * LDQ + hh * 8;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) TR::mma(sc, TR::load(kp + kk * 16), fq[kk]);
+    // sc[r] = score of key kbase + 8(r/4) + 4hh + r%4 for this lane's query
+    float mx = kNegInf;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int kidx = kbase + 8 * (r >> 2) + 4 * hh + (r & 3);
+      if (kidx < ks || kidx >= ke) sc[r] = kNegInf;
+      mx = fmaxf(mx, sc[r]);
+    }
+    mx = fmaxf(mx, wave_xor(mx, 32));
+    const float mnew = fmaxf(mrun, mx);
+    // a lane may see whole blocks before its own keys: keep it at zero
+    const float alpha = mnew == kNegInf ? 1.f : fast_exp2((mrun - mnew) * kLog2e);
+    const float mb = mnew == kNegInf ? 0.f : mnew * kLog2e;
+    float p[16];
+    float psum = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      p[r] = fast_exp2(sc[r] * kLog2e - mb);
+      psum += p[r];
+    }
+    lrun = lrun * alpha + psum;
+    mrun = mnew;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) { o[0][r] *= alpha; o[1][r] *= alpha; }
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const bf16x8 fp = TR::from_f32(p + 8 * c);
+#pragma unroll
+      for (int dt = 0; dt < 2; ++dt) {
+        const bf16* vp = (dt == 0 ? Vt0 : Vt1) + l32 * LDV + kbase + 16 * c + 4 * hh;
+        TR::mma(o[dt], TR::load2x4(vp, vp + 8), fp);
+      }
+    }
+  }
+  lrun += wave_xor(lrun, 32);
+  if (qr < nrows) {
+    const float inv = 1.0f / lrun;
+    bf16* out = a.ctx + ((int64_t)r0 + qr) * H + h * D;
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int d = dt * 32 + 8 * q + 4 * hh;
+        TR::store4(out + d, o[dt][4 * q + 0] * inv, o[dt][4 * q + 1] * inv,
+                   o[dt][4 * q + 2] * inv, o[dt][4 * q + 3] * inv);
+      }
+  }
+}
+
+}  // namespace albert

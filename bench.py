@@ -59,6 +59,7 @@ def kernel_flops(kind: str, lengths: np.ndarray) -> float:
         "ffn1_gelu": 2 * M * H * F,
         "ffn2_ln": 2 * M * F * H,
         "out": 2 * M * H * O,
+        "qkv_attn": 2 * M * H * 3 * H + float(np.sum(4.0 * H * L * L)),
     }[kind]
 
 

@@ -59,6 +59,10 @@ enum albert_dtype { ALBERT_F32 = 0, ALBERT_BF16 = 1, ALBERT_FP8 = 2 };
 /* flags for albert_encode / albert_encode_varlen */
 #define ALBERT_ASYNC 1u /* return after enqueueing; read the status later
                            with albert_read_status()                        */
+#define ALBERT_UNFUSED 2u /* bf16 only: run Q|K|V and attention as separate
+                             kernels (otherwise fused when every sequence
+                             has at most 256 tokens), so that the QKV tap
+                             holds its checkpoint                           */
 
 typedef struct albert_config {
   int32_t vocab;    /* word-table rows (Kokoro: 178)                       */
@@ -210,7 +214,9 @@ int albert_read_status(const void* ws, void* hip_stream);
  *   2 ROW_SEQ int32 [rows]       3 ROW_POS int32 [rows]
  *   4 EMB  [rows, E]   embedding sum after LayerNorm
  *   5 X    [rows, H]   input projection (n_iter = 0) or last layer output
- *   6 QKV  [rows, 3H]  last execution's q/8 | k | v, head h at h*64
+ *   6 QKV  [rows, 3H]  last execution's q/8 | k | v, head h at h*64 (written
+ *                      only by the unfused sequence: ALBERT_UNFUSED, fp32,
+ *                      FP8, the features entry or sequences over 256)
  *   7 CTX  [rows, H]   last execution's attention context (token-major)
  *   8 X1   [rows, H]   last execution's post-attention LayerNorm output
  *   9 G    [rows, F]   last execution's GELU output
@@ -237,7 +243,8 @@ enum albert_kernel_kind {
   ALBERT_K_FFN1_GELU = 5,   /* 768 -> 2048 + GELU                           */
   ALBERT_K_FFN2_LN = 6,     /* 2048 -> 768 + residual + LayerNorm           */
   ALBERT_K_OUT = 7,         /* 768 -> 512 output projection                 */
-  ALBERT_K_COUNT = 8
+  ALBERT_K_QKV_ATTN = 8,    /* fused Q|K|V projection + attention (bf16)    */
+  ALBERT_K_COUNT = 9
 };
 
 /* Measurement hook for benchmarks and profilers.  After this call every
