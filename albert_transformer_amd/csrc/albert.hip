@@ -189,16 +189,16 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
   return x < y + nb && y < x + na;
 }
 
-// Launch `fn` on stream s, bracketed by timing events when `kind` is the
-// kernel kind selected with albert_time_kernel().
+// Launch `fn` on stream s; when `kind` is the kernel kind selected with
+// albert_time_kernel(), its kernel carries a pair of timing events.
 template <typename Fn>
 void timed(albert_ctx* c, int kind, hipStream_t s, Fn&& fn) {
   const bool on = c->time_kind == kind && 2 * (c->n_timed + 1) <= (int)c->ev.size();
-  if (on) (void)hipEventRecord(c->ev[2 * c->n_timed], s);
-  fn();
+  if (on) g_launch_events = LaunchEvents{c->ev[2 * c->n_timed], c->ev[2 * c->n_timed + 1]};
+  fn();  // launches exactly one kernel through launch_kernel(), which takes the events
   if (on) {
-    (void)hipEventRecord(c->ev[2 * c->n_timed + 1], s);
-    ++c->n_timed;
+    if (g_launch_events.start == nullptr) ++c->n_timed;
+    g_launch_events = LaunchEvents{};
   }
 }
 
@@ -238,18 +238,17 @@ int run(albert_ctx* c, const int32_t* ids, const int32_t* lens_or_cu, int n_seq,
                        (int)max_rows, max_len, cu, status);
   if (feats) {
     timed(c, ALBERT_K_EMBED, s, [&] {
-      hipLaunchKernelGGL((features_in_kernel<T, F8>),
-                         dim3((unsigned)((max_rows * cf.emb / 4 + 255) / 256)), dim3(256), 0, s,
-                         feats, m_ptr, emb, status);
+      launch_kernel(features_in_kernel<T, F8>,
+                    dim3((unsigned)((max_rows * cf.emb / 4 + 255) / 256)), dim3(256), s, feats,
+                    m_ptr, emb, status);
     });
   } else {
     hipLaunchKernelGGL(rows_ids_kernel, dim3(n_seq), dim3(256), 0, s, ids, cu, pad_T, cf.vocab,
                        row_seq, row_pos, status);
     timed(c, ALBERT_K_EMBED, s, [&] {
-      hipLaunchKernelGGL((embed_ln_kernel<T, F8>), dim3((unsigned)((max_rows + 15) / 16)),
-                         dim3(256), 0, s, ids, pad_T, row_seq, row_pos, m_ptr, (const T*)c->word,
-                         (const T*)c->pos, (const T*)c->type, c->emb_g, c->emb_b, cf.ln_eps, emb,
-                         status);
+      launch_kernel(embed_ln_kernel<T, F8>, dim3((unsigned)((max_rows + 15) / 16)), dim3(256),
+                    s, ids, pad_T, row_seq, row_pos, m_ptr, (const T*)c->word, (const T*)c->pos,
+                    (const T*)c->type, c->emb_g, c->emb_b, cf.ln_eps, emb, status);
     });
   }
 
@@ -276,8 +275,8 @@ int run(albert_ctx* c, const int32_t* ids, const int32_t* lens_or_cu, int n_seq,
       QkvAttnArgs qa{static_cast<const bf16*>(X8), lw.qkv_wh, lw.qkv_bh,
                      static_cast<bf16*>(CTX), cu, row_seq, status, n_seq, S, (int)pairs};
       timed(c, ALBERT_K_QKV_ATTN, s, [&] {
-        hipLaunchKernelGGL(qkv_attention_kernel, dim3((unsigned)((pairs + 7) / 8 * 8)),
-                           dim3(512), 0, s, qa);
+        launch_kernel(qkv_attention_kernel, dim3((unsigned)((pairs + 7) / 8 * 8)), dim3(512), s,
+                      qa);
       });
     } else {
       g = base;  // fused Q|K|V projection
@@ -287,8 +286,7 @@ int run(albert_ctx* c, const int32_t* ids, const int32_t* lens_or_cu, int n_seq,
 
       AttnArgs a{QKV, CTX, cu, status};
       timed(c, ALBERT_K_ATTN, s, [&] {
-        hipLaunchKernelGGL((attention_kernel<T, F8>), dim3(n_seq, cf.heads, qtiles), dim3(256),
-                           0, s, a);
+        launch_kernel(attention_kernel<T, F8>, dim3(n_seq, cf.heads, qtiles), dim3(256), s, a);
       });
     }
 

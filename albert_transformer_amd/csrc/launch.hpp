@@ -2,6 +2,7 @@
 // the text path.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -12,6 +13,23 @@
 
 namespace albert {
 
+// Kernel timing without marker packets.  A caller that wants one launch
+// timed arms a pair of events here; the next launch_kernel() hands them to
+// hipExtLaunchKernel, which stamps them from that kernel's own dispatch,
+// so a timed kernel is not separated from its neighbours by extra gaps.
+struct LaunchEvents {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+inline thread_local LaunchEvents g_launch_events;
+
+template <typename... KArgs, typename... Args>
+inline void launch_kernel(void (*kernel)(KArgs...), dim3 grid, dim3 block, hipStream_t s,
+                          Args... args) {
+  const LaunchEvents ev = g_launch_events;
+  g_launch_events = LaunchEvents{};
+  hipExtLaunchKernelGGL(kernel, grid, block, 0, s, ev.start, ev.stop, 0, args...);
+}
+
 // Persistent launch: one block per CU at most (a multiple of 8, so that the
 // kernel's XCD-aware tile numbering is a bijection), each walking its tiles.
 template <typename T, bool F8, int BM, int BN, int WGM, int WGN, int RB, int STAGES, int EPI,
@@ -20,8 +38,8 @@ void launch_gemm(GemmArgs g, int64_t max_rows, int grid_cap, hipStream_t s) {
   g.n_tiles = g.N / BN;
   const int64_t tiles = (max_rows + BM - 1) / BM * g.n_tiles;
   const int64_t grid = std::min<int64_t>((tiles + 7) / 8 * 8, grid_cap);
-  hipLaunchKernelGGL((gemm_kernel<T, F8, BM, BN, WGM, WGN, RB, STAGES, EPI, DEFER>),
-                     dim3((unsigned)grid), dim3(WGM * WGN * 64), 0, s, g);
+  launch_kernel(gemm_kernel<T, F8, BM, BN, WGM, WGN, RB, STAGES, EPI, DEFER>,
+                dim3((unsigned)grid), dim3(WGM * WGN * 64), s, g);
 }
 
 // Large tiles for plain and GELU epilogues; full-row tiles for LayerNorm.

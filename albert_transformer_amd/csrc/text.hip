@@ -129,11 +129,11 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
 template <typename Fn>
 void ttimed(albert_text_ctx* c, int kind, hipStream_t s, Fn&& fn) {
   const bool on = c->time_kind == kind && 2 * (c->n_timed + 1) <= (int)c->ev.size();
-  if (on) (void)hipEventRecord(c->ev[2 * c->n_timed], s);
-  fn();
+  if (on) g_launch_events = LaunchEvents{c->ev[2 * c->n_timed], c->ev[2 * c->n_timed + 1]};
+  fn();  // launches exactly one kernel through launch_kernel(), which takes the events
   if (on) {
-    (void)hipEventRecord(c->ev[2 * c->n_timed + 1], s);
-    ++c->n_timed;
+    if (g_launch_events.start == nullptr) ++c->n_timed;
+    g_launch_events = LaunchEvents{};
   }
 }
 
@@ -163,9 +163,8 @@ int text_run(albert_text_ctx* c, const int32_t* ids, const int32_t* lens_or_cu, 
   hipLaunchKernelGGL(rows_ids_kernel, dim3(n_seq), dim3(256), 0, s, ids, cu, pad_T, cf.vocab,
                      row_seq, row_pos, status);
   ttimed(c, ALBERT_TK_EMBED, s, [&] {
-    hipLaunchKernelGGL(text_embed_kernel, dim3((unsigned)((max_rows * (C / 8) + 255) / 256)),
-                       dim3(256), 0, s, ids, pad_T, row_seq, row_pos, m_ptr, c->emb, C, X[0],
-                       status);
+    launch_kernel(text_embed_kernel, dim3((unsigned)((max_rows * (C / 8) + 255) / 256)),
+                  dim3(256), s, ids, pad_T, row_seq, row_pos, m_ptr, c->emb, C, X[0], status);
   });
 
   GemmArgs base{};
@@ -175,8 +174,8 @@ int text_run(albert_text_ctx* c, const int32_t* ids, const int32_t* lens_or_cu, 
   for (int i = 0; i < cf.n_conv; ++i) {
     const int nxt = cur == 1 ? 2 : 1;
     ttimed(c, ALBERT_TK_UNFOLD, s, [&] {
-      hipLaunchKernelGGL(unfold_kernel, dim3((unsigned)((max_rows * K * (C / 8) + 255) / 256)),
-                         dim3(256), 0, s, X[cur], row_seq, row_pos, cu, m_ptr, C, K, col, status);
+      launch_kernel(unfold_kernel, dim3((unsigned)((max_rows * K * (C / 8) + 255) / 256)),
+                    dim3(256), s, X[cur], row_seq, row_pos, cu, m_ptr, C, K, col, status);
     });
     GemmArgs g = base;  // convolution as one GEMM over the unfolded input
     g.X = col; g.ldx = (int64_t)K * C; g.W = c->conv_w[i]; g.bias = c->conv_b[i];
@@ -197,8 +196,8 @@ int text_run(albert_text_ctx* c, const int32_t* ids, const int32_t* lens_or_cu, 
 
   LstmArgs la{XG, c->w_hh, out, pad_T, cu, n_seq, status};
   ttimed(c, ALBERT_TK_LSTM, s, [&] {
-    hipLaunchKernelGGL(lstm_kernel, dim3((unsigned)((n_seq + kLstmSeq - 1) / kLstmSeq), 2),
-                       dim3(512), 0, s, la);
+    launch_kernel(lstm_kernel, dim3((unsigned)((n_seq + kLstmSeq - 1) / kLstmSeq), 2),
+                  dim3(512), s, la);
   });
   if (pad_T)
     hipLaunchKernelGGL(zero_pad_rows_kernel, dim3(n_seq), dim3(256), 0, s, out, cu, pad_T, 2 * H,
