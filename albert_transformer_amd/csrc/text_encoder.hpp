@@ -115,7 +115,10 @@ lstm_kernel(LstmArgs a) {
     return *reinterpret_cast<const bf16x8*>(W + ((kk * 4 + g) * 64 + lane) * 8);
   };
   constexpr int KS = H / 16;  // 16 k-steps
-  constexpr int PD = 3;       // W_hh prefetch distance (k-steps)
+  // W_hh prefetch distance (k-steps).  One k-step ahead keeps the kernel
+  // within its 256 registers; three ahead spilled in the step loop and ran
+  // 16 % slower on MI355X.
+  constexpr int PD = 1;
   static_assert(KS % (PD + 1) == 0, "the fragment ring must wrap at a step boundary");
 
   // Gate inputs of step tau as the accumulators' starting value (the MFMA
