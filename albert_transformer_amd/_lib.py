@@ -15,9 +15,10 @@ import numpy as np
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libalbert.so")
 
-OK, E_ARG, E_WORKSPACE, E_LENGTH, E_ID, E_ALIAS, E_HIP = range(7)
+OK, E_ARG, E_WORKSPACE, E_LENGTH, E_ID, E_ALIAS, E_HIP, E_SYNC = range(8)
 STATUS_NAMES = {OK: "OK", E_ARG: "E_ARG", E_WORKSPACE: "E_WORKSPACE",
-                E_LENGTH: "E_LENGTH", E_ID: "E_ID", E_ALIAS: "E_ALIAS", E_HIP: "E_HIP"}
+                E_LENGTH: "E_LENGTH", E_ID: "E_ID", E_ALIAS: "E_ALIAS", E_HIP: "E_HIP",
+                E_SYNC: "E_SYNC"}
 F32, BF16, FP8 = 0, 1, 2
 DTYPES = {"f32": F32, "bf16": BF16, "fp8": FP8}
 ASYNC = 1

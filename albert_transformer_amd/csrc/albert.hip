@@ -783,6 +783,7 @@ const char* albert_status_str(int status) {
     case ALBERT_E_ID: return "phoneme id outside the vocabulary";
     case ALBERT_E_ALIAS: return "output overlaps an input or the workspace";
     case ALBERT_E_HIP: return "HIP runtime error";
+    case ALBERT_E_SYNC: return "LSTM workgroups did not meet (not co-resident)";
     default: return "unknown status";
   }
 }

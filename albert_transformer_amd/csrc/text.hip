@@ -8,6 +8,7 @@
 //   -> zeroing of padded rows.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -34,6 +35,8 @@ struct albert_text_ctx {
   const bf16* w_ih;                 // [8H, C]: forward gates, then backward gates
   const float* b_gates;             // [8H]: b_ih + b_hh
   const bf16* w_hh;                 // both directions, in the recurrence's fragment order
+  const bf16* w_hh_mc;              // the same, in the four-workgroup recurrence's order
+  int mc_groups = 0;                // groups of 32 sequences per cooperative launch (0: none)
   int time_kind = -1;
   int n_timed = 0;
   std::vector<hipEvent_t> ev;
@@ -99,7 +102,8 @@ uint16_t bf16_bits(double v) {
 }
 
 struct TextLayout {
-  size_t status, cu, row_seq, row_pos, emb, x1, x2, col, xg, total;
+  size_t status, cu, row_seq, row_pos, emb, x1, x2, col, xg, hx, flags, total;
+  int mc_groups;  // groups of 32 sequences per launch of the four-workgroup recurrence
 };
 
 TextLayout text_plan(const albert_text_ctx* c, int n_seq, int64_t max_rows) {
@@ -116,6 +120,11 @@ TextLayout text_plan(const albert_text_ctx* c, int n_seq, int64_t max_rows) {
   L.x2 = off; off += align_up(rows * C * 2, kAlign);
   L.col = off; off += align_up(rows * K * C * 2, kAlign);
   L.xg = off; off += align_up(rows * 8 * H * 4, kAlign);
+  // exchange buffers of the four-workgroup recurrence: per launch up to
+  // mc_groups groups x 2 directions, each h_t twice (parity) as bf16
+  L.mc_groups = std::min((n_seq + kLstmSeq - 1) / kLstmSeq, c->mc_groups);
+  L.hx = off; off += align_up((size_t)L.mc_groups * 2 * 2 * kLstmSeq * H * 2, kAlign);
+  L.flags = off; off += align_up((size_t)L.mc_groups * 2 * kMcMembers * 4, kAlign);
   L.total = off;
   return L;
 }
@@ -138,7 +147,8 @@ void ttimed(albert_text_ctx* c, int kind, hipStream_t s, Fn&& fn) {
 }
 
 int text_run(albert_text_ctx* c, const int32_t* ids, const int32_t* lens_or_cu, int n_seq,
-             int pad_T, int64_t max_rows, int max_len, float* out, void* ws, hipStream_t s) {
+             int pad_T, int64_t max_rows, int max_len, float* out, void* ws, hipStream_t s,
+             unsigned flags) {
   const albert_text_config& cf = c->cfg;
   const TextLayout L = text_plan(c, n_seq, max_rows);
   char* w = static_cast<char*>(ws);
@@ -194,15 +204,43 @@ int text_run(albert_text_ctx* c, const int32_t* ids, const int32_t* lens_or_cu, 
     gemm_big<bf16, false, EPI_OUT>(g, max_rows, c->grid_cap, s);
   });
 
-  LstmArgs la{XG, c->w_hh, out, pad_T, cu, n_seq, status};
-  ttimed(c, ALBERT_TK_LSTM, s, [&] {
-    launch_kernel(lstm_kernel, dim3((unsigned)((n_seq + kLstmSeq - 1) / kLstmSeq), 2),
-                  dim3(512), s, la);
-  });
+  bool launch_failed = false;
+  if (L.mc_groups > 0 && !(flags & ALBERT_UNFUSED)) {
+    // four cooperating workgroups per direction and group of 32 sequences,
+    // at most mc_groups groups per launch (all resident together)
+    ttimed(c, ALBERT_TK_LSTM, s, [&] {
+      const LaunchEvents ev = g_launch_events;
+      g_launch_events = LaunchEvents{};
+      if (ev.start) (void)hipEventRecord(ev.start, s);
+      for (int seq0 = 0; seq0 < n_seq; seq0 += L.mc_groups * kLstmSeq) {
+        const int groups = std::min(L.mc_groups, (n_seq - seq0 + kLstmSeq - 1) / kLstmSeq);
+        const int quads = 2 * groups;
+        int* fl = reinterpret_cast<int*>(w + L.flags);
+        hipLaunchKernelGGL(zero_ints_kernel, dim3((quads * kMcMembers + 255) / 256), dim3(256),
+                           0, s, fl, quads * kMcMembers);
+        LstmMcArgs ma{XG, c->w_hh_mc, out, pad_T, cu, n_seq, seq0, quads,
+                      reinterpret_cast<bf16*>(w + L.hx), fl, status};
+        void* args[] = {&ma};
+        // quads padded to a multiple of 8, 4 workgroups each (see the kernel)
+        const unsigned grid = (unsigned)((quads + 7) / 8 * 32);
+        if (hipLaunchCooperativeKernel(reinterpret_cast<const void*>(lstm_mc_kernel), dim3(grid),
+                                       dim3(512), args, 0, s) != hipSuccess)
+          launch_failed = true;
+      }
+      if (ev.stop) (void)hipEventRecord(ev.stop, s);
+      g_launch_events = LaunchEvents{};  // consumed
+    });
+  } else {
+    LstmArgs la{XG, c->w_hh, out, pad_T, cu, n_seq, status};
+    ttimed(c, ALBERT_TK_LSTM, s, [&] {
+      launch_kernel(lstm_kernel, dim3((unsigned)((n_seq + kLstmSeq - 1) / kLstmSeq), 2),
+                    dim3(512), s, la);
+    });
+  }
   if (pad_T)
     hipLaunchKernelGGL(zero_pad_rows_kernel, dim3(n_seq), dim3(256), 0, s, out, cu, pad_T, 2 * H,
                        status);
-  return hipGetLastError() == hipSuccess ? ALBERT_OK : ALBERT_E_HIP;
+  return hipGetLastError() == hipSuccess && !launch_failed ? ALBERT_OK : ALBERT_E_HIP;
 }
 
 int text_finish(int rc, const void* ws, hipStream_t s, unsigned flags) {
@@ -280,6 +318,7 @@ int albert_text_load_weights(albert_text_ctx** out_ctx, const albert_text_config
   add((size_t)8 * H * C * 2);                   // w_ih, both directions
   add((size_t)8 * H * 4);                       // b_ih + b_hh
   add((size_t)2 * 4 * H * H * 2);               // w_hh, both directions
+  add((size_t)2 * 4 * H * H * 2);               // w_hh again, four-workgroup order
   std::vector<unsigned char> img(off, 0);
   auto bf = [&](int s) { return reinterpret_cast<uint16_t*>(img.data() + seg[s].off); };
   auto fp = [&](int s) { return reinterpret_cast<float*>(img.data() + seg[s].off); };
@@ -323,6 +362,22 @@ int albert_text_load_weights(albert_text_ctx** out_ctx, const albert_text_config
               const int64_t k = kk * 16 + (ln >> 5) * 8 + e;
               wd[(((wv * (H / 16) + kk) * 4 + g) * 64 + ln) * 8 + e] = bf16_bits(whh[r * H + k]);
             }
+    // four-workgroup order [d][member 4][wave 8][k-step H/16][lane 64][8]:
+    // row l32 of wave w's tile in member m is gate l32 % 4 of unit
+    // 64m + 8w + u/2 + 4(u%2), u = l32 / 4, so that MFMA lane (l32, hh)
+    // ends up with the four gates of units 64m + 8w + 4hh .. +3
+    uint16_t* wm = bf(s_wih + 3) + d * 4 * H * H;
+    for (int64_t mb = 0; mb < kMcMembers; ++mb)
+      for (int64_t wv = 0; wv < 8; ++wv)
+        for (int64_t kk = 0; kk < H / 16; ++kk)
+          for (int64_t ln = 0; ln < 64; ++ln)
+            for (int64_t e = 0; e < 8; ++e) {
+              const int64_t tr = ln & 31, u = tr / 4, g = tr % 4;
+              const int64_t unit = 64 * mb + 8 * wv + u / 2 + 4 * (u % 2);
+              const int64_t k = kk * 16 + (ln >> 5) * 8 + e;
+              wm[((((mb * 8 + wv) * (H / 16) + kk) * 64) + ln) * 8 + e] =
+                  bf16_bits(whh[(g * H + unit) * H + k]);
+            }
   }
 
   albert_text_ctx* ctx = new (std::nothrow) albert_text_ctx();
@@ -355,6 +410,18 @@ int albert_text_load_weights(albert_text_ctx** out_ctx, const albert_text_config
   ctx->w_ih = reinterpret_cast<const bf16*>(m + seg[s_wih].off);
   ctx->b_gates = reinterpret_cast<const float*>(m + seg[s_wih + 1].off);
   ctx->w_hh = reinterpret_cast<const bf16*>(m + seg[s_wih + 2].off);
+  ctx->w_hh_mc = reinterpret_cast<const bf16*>(m + seg[s_wih + 3].off);
+  // the four-workgroup recurrence needs a cooperative launch: all of its
+  // workgroups resident at once; groups per launch in multiples of 4 (a
+  // launch is a multiple of 32 workgroups)
+  int coop = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, ctx->device) ==
+          hipSuccess &&
+      coop &&
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, lstm_mc_kernel, 512, 0) ==
+          hipSuccess &&
+      per_cu >= 1)
+    ctx->mc_groups = std::min(64, (per_cu * n_cu) / 32 * 4);
   *out_ctx = ctx;
   return ALBERT_OK;
 }
@@ -379,7 +446,7 @@ int albert_text_encode(albert_text_ctx* ctx, const int32_t* ids, const int32_t* 
       overlaps(out, out_bytes, lengths, (size_t)B * 4) || overlaps(out, out_bytes, ws, need))
     return ALBERT_E_ALIAS;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  return text_finish(text_run(ctx, ids, lengths, B, T, rows, T, out, ws, s), ws, s, flags);
+  return text_finish(text_run(ctx, ids, lengths, B, T, rows, T, out, ws, s, flags), ws, s, flags);
 }
 
 int albert_text_encode_varlen(albert_text_ctx* ctx, const int32_t* ids, const int32_t* cu_seqlens,
@@ -397,8 +464,8 @@ int albert_text_encode_varlen(albert_text_ctx* ctx, const int32_t* ids, const in
       overlaps(out, out_bytes, ws, need))
     return ALBERT_E_ALIAS;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  return text_finish(text_run(ctx, ids, cu_seqlens, n, 0, total, max_len, out, ws, s), ws, s,
-                     flags);
+  return text_finish(text_run(ctx, ids, cu_seqlens, n, 0, total, max_len, out, ws, s, flags), ws,
+                     s, flags);
 }
 
 int albert_text_tap(const albert_text_ctx* ctx, int n_seq, int64_t max_rows, int tap,

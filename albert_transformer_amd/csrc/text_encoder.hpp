@@ -71,7 +71,17 @@ struct LstmArgs {
 __device__ __forceinline__ float sigmoid_f(float x) {
   return __builtin_amdgcn_rcpf(1.0f + fast_exp2(-x * kLog2e));
 }
-__device__ __forceinline__ float tanh_f(float x) { return 2.0f * sigmoid_f(2.0f * x) - 1.0f; }
+__device__ __forceinline__ float tanh_f(float x) {
+  return __builtin_fmaf(2.0f, sigmoid_f(2.0f * x), -1.0f);
+}
+// One cell update: c <- sigmoid(f) c + sigmoid(i) tanh(g); returns
+// sigmoid(o) tanh(c).  The multiply-adds are explicit so that both
+// recurrence kernels round every step alike.
+__device__ __forceinline__ float lstm_cell(float zi, float zf, float zg, float zo, float& c) {
+  const float cn = __builtin_fmaf(sigmoid_f(zf), c, sigmoid_f(zi) * tanh_f(zg));
+  c = cn;
+  return sigmoid_f(zo) * tanh_f(cn);
+}
 
 // LSTM recurrence.  Grid (ceil(n_seq / 32), 2 directions), 8 waves.  The
 // workgroup carries 32 sequences of one direction through their own
@@ -174,10 +184,7 @@ lstm_kernel(LstmArgs a) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = 4 * q + e;
-        const float zi = acc[0][r], zf = acc[1][r], zg = acc[2][r], zo = acc[3][r];
-        const float cn = sigmoid_f(zf) * c[r] + sigmoid_f(zi) * tanh_f(zg);
-        hv[e] = sigmoid_f(zo) * tanh_f(cn);
-        c[r] = cn;
+        hv[e] = lstm_cell(acc[0][r], acc[1][r], acc[2][r], acc[3][r], c[r]);
       }
       const int u = ubase + 8 * q;
       Tr<bf16>::store4(hn + u, hv[0], hv[1], hv[2], hv[3]);
@@ -187,6 +194,151 @@ lstm_kernel(LstmArgs a) {
     }
     xload(tau + 1);   // next step's gate inputs, in flight across the barrier
     __syncthreads();  // h_t complete in hs[cur^1]; hs[cur] free for step tau+1's writes
+  }
+}
+
+// Multi-workgroup recurrence.  Each direction of a group of 32 sequences
+// is carried by a quad of workgroups; member m owns units [64m, 64m+64) and
+// keeps their W_hh rows (4 gates x 64 units x 256 inputs, 128 KB) in
+// registers for the whole scan, so no weight bytes move per step.  Wave w
+// of member m owns the 32 gate rows of units 64m + 8w .. +7 as one MFMA
+// tile, rows ordered so that lane (l32, hh) receives the four gates of
+// units 64m + 8w + 4hh + j (j = 0..3) for sequence l32: acc[4j + g] is gate
+// g of unit j.  After each step a member publishes its 64 units of h_t
+// (bf16) and a step flag; once all four flags reach the step, every member
+// reads the full h_t into LDS for the next step.  The quad must be resident
+// at once (the host uses a cooperative launch); every wait is bounded, and a
+// wait that runs out sets the status word to ALBERT_E_SYNC and ends the
+// workgroup, after which its partners' waits run out too.
+constexpr int kMcMembers = 4;
+constexpr int kMcSpin = 1 << 20;  // polls (each after a short sleep) before giving up
+constexpr int kStatusSync = 7;    // ALBERT_E_SYNC
+
+__global__ void zero_ints_kernel(int* __restrict__ p, int n) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = 0;
+}
+
+struct LstmMcArgs {
+  const float* xg;   // as LstmArgs
+  const bf16* whh;   // [d][member][wave][k-step 16][lane 64][8], rows permuted as above
+  float* out;
+  int out_T;
+  const int* cu;
+  int n_seq;
+  int seq0;          // first sequence of this launch
+  int n_quads;       // (groups of 32 sequences in this launch) x 2 directions
+  bf16* hx;          // exchange, [quad][parity 2][32 sequences][256 units]
+  int* flags;        // [quad][member], zero before the launch
+  int* status;
+};
+
+__global__ void __launch_bounds__(512)
+lstm_mc_kernel(LstmMcArgs a) {
+  constexpr int H = kLstmH, LDH = H + 8, KS = H / 16;
+  __shared__ __attribute__((aligned(16))) bf16 hs[kLstmSeq * LDH];
+  __shared__ int ok_s;
+  // workgroup b -> quad q, member m: the four members of a quad are b, b+8,
+  // b+16, b+24 (workgroups are dealt to the 8 XCDs round-robin, so a quad
+  // shares one XCD)
+  const int b = blockIdx.x;
+  const int q = (b / 32) * 8 + b % 8, m = (b / 8) % kMcMembers;
+  if (q >= a.n_quads || *a.status != 0) return;
+  const int d = q % 2, grp = q / 2;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, hh = lane >> 5;
+  const int seq = a.seq0 + grp * kLstmSeq + l32;
+  const bool sv = seq < a.n_seq;
+  const int start = sv ? a.cu[seq] : 0;
+  const int L = sv ? a.cu[seq + 1] - start : 0;
+  int Lmax = L;
+#pragma unroll
+  for (int off = 16; off >= 1; off >>= 1) Lmax = max(Lmax, __shfl_xor(Lmax, off, 64));
+  const int ub = 64 * m + 8 * wave + 4 * hh;  // this lane's units ub .. ub+3
+
+  bf16x8 wf[KS];
+  const bf16* __restrict__ W = a.whh + ((((int64_t)d * kMcMembers + m) * 8 + wave) * KS) * 64 * 8;
+#pragma unroll
+  for (int kk = 0; kk < KS; ++kk) wf[kk] = *reinterpret_cast<const bf16x8*>(W + (kk * 64 + lane) * 8);
+  for (int i = tid; i < kLstmSeq * LDH; i += 512) hs[i] = (bf16)0.0f;
+  float c[4] = {0.f, 0.f, 0.f, 0.f};
+
+  // gate inputs of step tau for this lane's 4 units: one 16-byte load per gate
+  f32x4 xv[4];
+  auto xload = [&](int tau) __attribute__((always_inline)) {
+    const bool act = tau < L;
+    const int t = d == 0 ? tau : L - 1 - tau;
+    const float* xr = a.xg + ((int64_t)start + t) * (8 * H) + d * 4 * H + ub;
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+      xv[g] = act ? *reinterpret_cast<const f32x4*>(xr + g * H) : f32x4{0.f, 0.f, 0.f, 0.f};
+  };
+  xload(0);
+  bf16* const hxq = a.hx + (int64_t)q * 2 * kLstmSeq * H;
+  int* const fq = a.flags + q * kMcMembers;
+  // the weight registers have arrived before the step loop (otherwise the
+  // loop's waits for them would also wait for each step's gate-input loads)
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  __syncthreads();
+
+  for (int tau = 0; tau < Lmax; ++tau) {
+    f32x16 acc;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) acc[4 * j + g] = xv[g][j];
+    xload(tau + 1);  // in flight across the step
+    const bf16* hb = hs + l32 * LDH + hh * 8;
+    bf16x8 hf[KS];
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) hf[kk] = *reinterpret_cast<const bf16x8*>(hb + kk * 16);
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk)
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[kk], hf[kk], acc, 0, 0, 0);
+    float hv[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      hv[j] = lstm_cell(acc[4 * j], acc[4 * j + 1], acc[4 * j + 2], acc[4 * j + 3], c[j]);
+    }
+    if (tau < L) {
+      const int t = d == 0 ? tau : L - 1 - tau;
+      const int64_t orow = a.out_T ? (int64_t)seq * a.out_T + t : (int64_t)start + t;
+      *reinterpret_cast<f32x4*>(a.out + orow * (2 * H) + d * H + ub) = f32x4{hv[0], hv[1], hv[2], hv[3]};
+    }
+    if (tau + 1 == Lmax) break;
+    // publish this member's h_t, then meet the other members
+    bf16* const hxp = hxq + (tau & 1) * kLstmSeq * H;
+    Tr<bf16>::store4(hxp + l32 * H + ub, hv[0], hv[1], hv[2], hv[3]);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's stores have reached L2
+    __syncthreads();                                   // every wave is done with hs
+    if (tid == 0) {
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+      __hip_atomic_store(fq + m, tau + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      bool ok = true;
+      for (int mm = 0; mm < kMcMembers && ok; ++mm) {
+        int polls = 0;
+        while (__hip_atomic_load(fq + mm, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < tau + 1) {
+          if (++polls > kMcSpin) {
+            ok = false;
+            break;
+          }
+          __builtin_amdgcn_s_sleep(1);
+        }
+      }
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      if (!ok) __hip_atomic_store(a.status, kStatusSync, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      ok_s = ok;
+    }
+    __syncthreads();
+    if (!ok_s) return;
+    {  // h_t of all 256 units -> LDS: 32 bytes per thread
+      const int sq = tid / 16, ch = tid % 16;
+      const uint4* src = reinterpret_cast<const uint4*>(hxp + sq * H + ch * 16);
+      uint4* dst = reinterpret_cast<uint4*>(hs + sq * LDH + ch * 16);
+      dst[0] = src[0];
+      dst[1] = src[1];
+    }
+    __syncthreads();
   }
 }
 

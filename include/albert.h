@@ -41,7 +41,10 @@ enum albert_status {
   ALBERT_E_LENGTH = 3,    /* a length outside [1, T] / bad cu_seqlens        */
   ALBERT_E_ID = 4,        /* an ID at a valid slot outside [0, vocab-1]      */
   ALBERT_E_ALIAS = 5,     /* `out` overlaps an input or the workspace        */
-  ALBERT_E_HIP = 6        /* a HIP runtime call failed                       */
+  ALBERT_E_HIP = 6,       /* a HIP runtime call failed                       */
+  ALBERT_E_SYNC = 7       /* the text path's multi-workgroup LSTM recurrence:
+                             a workgroup waited too long for its partners
+                             (they were not resident together)            */
 };
 
 /* Compute/storage type of tables, weight matrices and activations.
@@ -62,7 +65,9 @@ enum albert_dtype { ALBERT_F32 = 0, ALBERT_BF16 = 1, ALBERT_FP8 = 2 };
 #define ALBERT_UNFUSED 2u /* bf16 only: run Q|K|V and attention as separate
                              kernels (otherwise fused when every sequence
                              has at most 256 tokens), so that the QKV tap
-                             holds its checkpoint                           */
+                             holds its checkpoint.  Text path: run the LSTM
+                             recurrence as one workgroup per direction and
+                             32 sequences instead of four cooperating ones */
 
 typedef struct albert_config {
   int32_t vocab;    /* word-table rows (Kokoro: 178)                       */

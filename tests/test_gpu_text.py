@@ -153,3 +153,55 @@ def test_text_rejections_leave_output_untouched():
     assert enc.encode_raw(dev(bad), dev(np.array([8, 5], np.int32)), out, ws) == A.OK
     assert enc.encode_raw(dev(ids), dev(np.array([8, 8], np.int32)), out, ws, ws_bytes=16) == \
         A.E_WORKSPACE
+
+
+def test_text_recurrence_variants_agree_bitwise():
+    """The four-workgroup recurrence (default) and the one-workgroup one
+    (ALBERT_UNFUSED) add the same products in the same order: identical
+    outputs, on a ragged batch of three groups of 32 sequences."""
+    import torch
+    import albert_transformer_amd as A
+    enc = _enc()
+    TW = _tw()
+    rng = np.random.default_rng(54)
+    lengths = rng.integers(1, 97, 70).astype(np.int32)
+    lengths[:2] = [96, 1]
+    ids = rng.integers(0, 178, (70, 96)).astype(np.int32)
+    outs = []
+    for flags in (0, A.UNFUSED):
+        out = torch.full((70, 96, 512), float("nan"), device="cuda")
+        ws = enc.new_workspace(70, 70 * 96)
+        assert enc.encode_raw(dev(ids), dev(lengths), out, ws, flags=flags) == A.OK
+        outs.append(out.cpu().numpy())
+    assert np.array_equal(outs[0], outs[1])
+    for b in (0, 1, 69):
+        L = int(lengths[b])
+        check(outs[0][b, :L].astype(np.float64), te.text_encode_sequence(ids[b, :L], TW, TC),
+              "bf16", f"text recurrence L={L}")
+
+
+def test_text_many_short_sequences():
+    """More sequences than one cooperative launch of the recurrence holds
+    (several launches, the last one partial); packed rows; sampled
+    sequences against the oracle and the whole output against the
+    one-workgroup recurrence."""
+    import torch
+    import albert_transformer_amd as A
+    enc = _enc()
+    TW = _tw()
+    rng = np.random.default_rng(55)
+    n = 64 * 32 * 2 + 37
+    lengths = rng.integers(1, 7, n).astype(np.int32)
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    total = int(cu[-1])
+    flat = rng.integers(0, 178, total).astype(np.int32)
+    outs = []
+    for flags in (0, A.UNFUSED):
+        out = torch.full((total, 512), float("nan"), device="cuda")
+        ws = enc.new_workspace(n, total)
+        assert enc.encode_varlen_raw(dev(flat), dev(cu), 6, out, ws, flags=flags) == A.OK
+        outs.append(out.cpu().numpy())
+    assert np.array_equal(outs[0], outs[1])
+    for b in (0, 2047, 2048, 4095, n - 1):
+        check(outs[0][cu[b]:cu[b + 1]].astype(np.float64),
+              te.text_encode_sequence(flat[cu[b]:cu[b + 1]], TW, TC), "bf16", f"text short seq{b}")
