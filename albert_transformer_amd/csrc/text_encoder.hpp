@@ -311,23 +311,28 @@ lstm_mc_kernel(LstmMcArgs a) {
     Tr<bf16>::store4(hxp + l32 * H + ub, hv[0], hv[1], hv[2], hv[3]);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's stores have reached L2
     __syncthreads();                                   // every wave is done with hs
-    if (tid == 0) {
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-      __hip_atomic_store(fq + m, tau + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (wave == 0) {  // lane 0 publishes; lanes 0..3 watch one member each
+      if (lane == 0) {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        __hip_atomic_store(fq + m, tau + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
       bool ok = true;
-      for (int mm = 0; mm < kMcMembers && ok; ++mm) {
-        int polls = 0;
-        while (__hip_atomic_load(fq + mm, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < tau + 1) {
-          if (++polls > kMcSpin) {
-            ok = false;
-            break;
-          }
-          __builtin_amdgcn_s_sleep(1);
+      for (int polls = 0;; ++polls) {
+        const int v = lane < kMcMembers
+                          ? __hip_atomic_load(fq + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                          : tau + 1;
+        if (__all(v >= tau + 1)) break;
+        if (polls >= kMcSpin) {
+          ok = false;
+          break;
         }
+        __builtin_amdgcn_s_sleep(1);
       }
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-      if (!ok) __hip_atomic_store(a.status, kStatusSync, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      ok_s = ok;
+      if (lane == 0) {
+        if (!ok) __hip_atomic_store(a.status, kStatusSync, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        ok_s = ok;
+      }
     }
     __syncthreads();
     if (!ok_s) return;
