@@ -237,6 +237,9 @@ int run(albert_ctx* c, const int32_t* ids, const int32_t* lens_or_cu, int n_seq,
     hipLaunchKernelGGL(derive_packed_kernel, dim3(1), dim3(1024), 0, s, lens_or_cu, n_seq,
                        (int)max_rows, max_len, cu, status);
   if (feats) {
+    // row -> sequence map for the attention's packed query blocks
+    hipLaunchKernelGGL(rows_ids_kernel, dim3(n_seq), dim3(256), 0, s, nullptr, cu, 0, cf.vocab,
+                       row_seq, row_pos, status);
     timed(c, ALBERT_K_EMBED, s, [&] {
       launch_kernel(features_in_kernel<T, F8>,
                     dim3((unsigned)((max_rows * cf.emb / 4 + 255) / 256)), dim3(256), s, feats,
@@ -262,7 +265,6 @@ int run(albert_ctx* c, const int32_t* ids, const int32_t* lens_or_cu, int n_seq,
   g.Y = X; g.ldy = H; g.Y8 = Y8; g.ldy8 = H; g.N = H; g.K = cf.emb;
   timed(c, ALBERT_K_PROJ, s, [&] { gemm_big<T, F8, EPI_BIAS>(g, max_rows, c->grid_cap, s); });
 
-  const int qtiles = (max_len + 127) / 128;
   // Q|K|V and attention in one kernel when every sequence fits its 256-row
   // tile (groups of S whole sequences); the unfused pair otherwise.
   constexpr bool can_fuse = std::is_same<T, bf16>::value && !F8;
@@ -284,10 +286,13 @@ int run(albert_ctx* c, const int32_t* ids, const int32_t* lens_or_cu, int n_seq,
       g.ldy = 3 * H; g.N = 3 * H; g.K = H;
       timed(c, ALBERT_K_QKV, s, [&] { gemm_big<T, F8, EPI_BIAS>(g, max_rows, c->grid_cap, s); });
 
-      AttnArgs a{QKV, CTX, cu, status};
-      timed(c, ALBERT_K_ATTN, s, [&] {
-        launch_kernel(attention_kernel<T, F8>, dim3(n_seq, cf.heads, qtiles), dim3(256), s, a);
-      });
+      // short sequences on average (many per 128 rows): packed query blocks;
+      // otherwise query tiles aligned to each sequence
+      const bool packed = max_rows < (int64_t)n_seq * 128;
+      AttnArgs a{QKV, CTX, cu, row_seq, m_ptr, status, packed ? 1 : 0};
+      const dim3 grid = packed ? dim3((unsigned)((max_rows + 127) / 128), cf.heads)
+                               : dim3(n_seq, cf.heads, (max_len + 127) / 128);
+      timed(c, ALBERT_K_ATTN, s, [&] { launch_kernel(attention_kernel<T, F8>, grid, dim3(256), s, a); });
     }
 
     g = base;  // output projection + residual + LayerNorm

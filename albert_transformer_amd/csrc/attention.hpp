@@ -6,10 +6,17 @@
 // CKE Stands", section "What ALBERT does here": keys beyond the length get no
 // weight).  The 1/8 scale is already folded into the stored query weights.
 //
-// Grid: (sequences, 12 heads, query tiles of 128).  Each wave owns 32
-// queries.  Keys and values of the (sequence, head) are staged in LDS in
-// chunks of 128 keys (K row-major, V transposed), zero-filled past the
-// length, so one workgroup walks the whole sequence (<= 512 keys).
+// Two grids.  Per sequence (long sequences): (sequences, 12 heads, query
+// tiles of 128 from the sequence's start).  Packed blocks (many short
+// sequences): (blocks of 128 packed query rows, 12 heads); a block may hold
+// the tail of one sequence, several whole short ones and the head of
+// another.  Each wave owns 32 queries.  The workgroup walks the sequences
+// of its queries in order, staging each one's keys and values in LDS in
+// chunks of 128 keys (K row-major, V transposed), zero-filled past its
+// length, and a lane takes only the chunks of its own sequence (for the
+// others its scores are masked, which leaves its running softmax exactly
+// unchanged).  Every lane therefore sees its sequence's keys in the same
+// blocks, from the sequence's start, whichever grid and packing.
 // Scores are computed transposed, S^T = K Q^T, so each lane owns one query
 // and 16 keys of every 32-key block: the running max and sum of the online
 // softmax need only the partner half-wave, and the probabilities feed the
@@ -26,7 +33,10 @@ struct AttnArgs {
   const void* qkv;    // [M, 3H]: q*(1/8) | k | v, head h at h*64
   void* ctx;          // [M, H] (T, or E4M3 codes)
   const int* cu;      // [n_seq + 1]
+  const int* row_seq; // [M] sequence of each packed row
+  const int* m_ptr;   // device: M
   const int* status;
+  int packed;         // 1: packed-block grid, 0: per-sequence grid
 };
 
 template <typename T, bool F8>
@@ -42,108 +52,126 @@ attention_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) T Vt[D * LDVT];
 
   if (*a.status != 0) return;
-  const int b = blockIdx.x, h = blockIdx.y;
-  const int start = a.cu[b], L = a.cu[b + 1] - start;
-  const int q0 = blockIdx.z * 128;
-  if (q0 >= L) return;
+  const int h = blockIdx.y;
+  int q0, q1, s_first, s_last;  // query rows [q0, q1), their sequences
+  if (a.packed) {
+    const int M = *a.m_ptr;
+    q0 = blockIdx.x * 128;
+    if (q0 >= M) return;
+    q1 = min(q0 + 128, M);
+    s_first = a.row_seq[q0];
+    s_last = a.row_seq[q1 - 1];
+  } else {
+    const int sq = blockIdx.x, start = a.cu[sq];
+    q0 = start + blockIdx.z * 128;
+    q1 = min(q0 + 128, a.cu[sq + 1]);
+    if (q0 >= q1) return;
+    s_first = s_last = sq;
+  }
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hh = lane >> 5;
-  const int qi = q0 + wave * 32 + l32;  // this lane's query (column of S^T)
+  const int qi = q0 + wave * 32 + l32;  // this lane's query row (column of S^T)
+  const bool qv = qi < q1;
+  const int my_seq = qv ? a.row_seq[qi] : -1;
 
   const T* __restrict__ qkv = static_cast<const T*>(a.qkv);
-  const T* __restrict__ base = qkv + (int64_t)start * LDQKV;
-
   typename TR::frag fq[4];
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk)
-    fq[kk] = (qi < L) ? TR::load(base + (int64_t)qi * LDQKV + h * D + kk * 16 + hh * 8)
-                      : TR::zero();
+    fq[kk] = qv ? TR::load(qkv + (int64_t)qi * LDQKV + h * D + kk * 16 + hh * 8) : TR::zero();
 
   f32x16 o[2];
 #pragma unroll
   for (int r = 0; r < 16; ++r) { o[0][r] = 0.f; o[1][r] = 0.f; }
   float mrun = kNegInf, lrun = 0.f;
 
-  for (int c0 = 0; c0 < L; c0 += KC) {
-    const int nk = min(KC, L - c0);
-    __syncthreads();  // the previous chunk is fully consumed
-    // K chunk, row-major [key][dim]
-    for (int idx = tid; idx < KC * (D / VEC); idx += 256) {
-      const int j = idx / (D / VEC), cc = idx % (D / VEC);
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (j < nk) v = *reinterpret_cast<const uint4*>(base + (int64_t)(c0 + j) * LDQKV + H + h * D + cc * VEC);
-      *reinterpret_cast<uint4*>(Ks + j * LDKS + cc * VEC) = v;
-    }
-    // V chunk, transposed [dim][key]: a task reads one 16-byte chunk of two
-    // consecutive key rows (coalesced along the rows) and writes words that
-    // each hold one dim for both keys.
-    for (int idx = tid; idx < (KC / 2) * (D / VEC); idx += 256) {
-      const int cc = idx % (D / VEC), p = idx / (D / VEC);
-      const int j = 2 * p;
-      T t0[VEC], t1[VEC];
-      uint4 u0 = make_uint4(0, 0, 0, 0), u1 = make_uint4(0, 0, 0, 0);
-      if (j < nk) u0 = *reinterpret_cast<const uint4*>(base + (int64_t)(c0 + j) * LDQKV + 2 * H + h * D + cc * VEC);
-      if (j + 1 < nk) u1 = *reinterpret_cast<const uint4*>(base + (int64_t)(c0 + j + 1) * LDQKV + 2 * H + h * D + cc * VEC);
-      *reinterpret_cast<uint4*>(t0) = u0;
-      *reinterpret_cast<uint4*>(t1) = u1;
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) {
-        T* dst = Vt + (cc * VEC + e) * LDVT + j;
-        dst[0] = t0[e];
-        dst[1] = t1[e];
+  for (int sq = s_first; sq <= s_last; ++sq) {
+    const int start = a.cu[sq], L = a.cu[sq + 1] - start;
+    const bool mine = my_seq == sq;
+    const T* __restrict__ base = qkv + (int64_t)start * LDQKV;
+    for (int c0 = 0; c0 < L; c0 += KC) {
+      const int nk = min(KC, L - c0);
+      const int nk32 = (nk + 31) / 32 * 32;  // rows the 32-key blocks below read
+      __syncthreads();  // the previous chunk is fully consumed
+      // K chunk, row-major [key][dim]
+      for (int idx = tid; idx < nk32 * (D / VEC); idx += 256) {
+        const int j = idx / (D / VEC), cc = idx % (D / VEC);
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (j < nk) v = *reinterpret_cast<const uint4*>(base + (int64_t)(c0 + j) * LDQKV + H + h * D + cc * VEC);
+        *reinterpret_cast<uint4*>(Ks + j * LDKS + cc * VEC) = v;
       }
-    }
-    __syncthreads();
+      // V chunk, transposed [dim][key]: a task reads one 16-byte chunk of two
+      // consecutive key rows (coalesced along the rows) and writes words that
+      // each hold one dim for both keys.
+      for (int idx = tid; idx < (nk32 / 2) * (D / VEC); idx += 256) {
+        const int cc = idx % (D / VEC), p = idx / (D / VEC);
+        const int j = 2 * p;
+        T t0[VEC], t1[VEC];
+        uint4 u0 = make_uint4(0, 0, 0, 0), u1 = make_uint4(0, 0, 0, 0);
+        if (j < nk) u0 = *reinterpret_cast<const uint4*>(base + (int64_t)(c0 + j) * LDQKV + 2 * H + h * D + cc * VEC);
+        if (j + 1 < nk) u1 = *reinterpret_cast<const uint4*>(base + (int64_t)(c0 + j + 1) * LDQKV + 2 * H + h * D + cc * VEC);
+        *reinterpret_cast<uint4*>(t0) = u0;
+        *reinterpret_cast<uint4*>(t1) = u1;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          T* dst = Vt + (cc * VEC + e) * LDVT + j;
+          dst[0] = t0[e];
+          dst[1] = t1[e];
+        }
+      }
+      __syncthreads();
 
-    const int nkb = (nk + 31) / 32;
-    for (int kb = 0; kb < nkb; ++kb) {
-      f32x16 s;
+      const int nkb = (nk + 31) / 32;
+      for (int kb = 0; kb < nkb; ++kb) {
+        f32x16 s;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[r] = 0.f;
-      const T* kp = Ks + (kb * 32 + l32) * LDKS + hh * 8;
+        for (int r = 0; r < 16; ++r) s[r] = 0.f;
+        const T* kp = Ks + (kb * 32 + l32) * LDKS + hh * 8;
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) TR::mma(s, TR::load(kp + kk * 16), fq[kk]);
-      // s[r] = score of key c0 + kb*32 + 8(r/4) + 4hh + r%4 for query qi
-      const int kbase = c0 + kb * 32 + 4 * hh;
-      float mx = kNegInf;
+        for (int kk = 0; kk < 4; ++kk) TR::mma(s, TR::load(kp + kk * 16), fq[kk]);
+        // s[r] = score of key c0 + kb*32 + 8(r/4) + 4hh + r%4 for query qi
+        const int kbase = c0 + kb * 32 + 4 * hh;
+        float mx = kNegInf;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = kbase + 8 * (r >> 2) + (r & 3);
-        if (key >= L) s[r] = kNegInf;
-        mx = fmaxf(mx, s[r]);
-      }
-      mx = fmaxf(mx, wave_xor(mx, 32));
-      const float mnew = fmaxf(mrun, mx);
-      const float alpha = fast_exp2((mrun - mnew) * kLog2e);
-      const float mb = mnew * kLog2e;
-      float p[16];
-      float psum = 0.f;
+        for (int r = 0; r < 16; ++r) {
+          const int key = kbase + 8 * (r >> 2) + (r & 3);
+          if (key >= L || !mine) s[r] = kNegInf;
+          mx = fmaxf(mx, s[r]);
+        }
+        mx = fmaxf(mx, wave_xor(mx, 32));
+        const float mnew = fmaxf(mrun, mx);
+        // a lane that has not met its own sequence yet keeps a zero state
+        const float alpha = mnew == kNegInf ? 1.f : fast_exp2((mrun - mnew) * kLog2e);
+        const float mb = mnew == kNegInf ? 0.f : mnew * kLog2e;
+        float p[16];
+        float psum = 0.f;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        p[r] = fast_exp2(s[r] * kLog2e - mb);
-        psum += p[r];
-      }
-      lrun = lrun * alpha + psum;
-      mrun = mnew;
+        for (int r = 0; r < 16; ++r) {
+          p[r] = fast_exp2(s[r] * kLog2e - mb);
+          psum += p[r];
+        }
+        lrun = lrun * alpha + psum;
+        mrun = mnew;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) { o[0][r] *= alpha; o[1][r] *= alpha; }
+        for (int r = 0; r < 16; ++r) { o[0][r] *= alpha; o[1][r] *= alpha; }
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        // element e of this lane <-> key 16c + 4hh + e (e < 4), 16c + 8 + 4hh + e - 4
-        const typename TR::frag fp = TR::from_f32(p + 8 * c);
+        for (int c = 0; c < 2; ++c) {
+          // element e of this lane <-> key 16c + 4hh + e (e < 4), 16c + 8 + 4hh + e - 4
+          const typename TR::frag fp = TR::from_f32(p + 8 * c);
 #pragma unroll
-        for (int dt = 0; dt < 2; ++dt) {
-          const T* vp = Vt + (dt * 32 + l32) * LDVT + kb * 32 + 16 * c + 4 * hh;
-          TR::mma(o[dt], TR::load2x4(vp, vp + 8), fp);
+          for (int dt = 0; dt < 2; ++dt) {
+            const T* vp = Vt + (dt * 32 + l32) * LDVT + kb * 32 + 16 * c + 4 * hh;
+            TR::mma(o[dt], TR::load2x4(vp, vp + 8), fp);
+          }
         }
       }
     }
   }
   lrun += wave_xor(lrun, 32);
-  if (qi >= L) return;
+  if (!qv) return;
   const float inv = 1.0f / lrun;
-  const int64_t orow = ((int64_t)start + qi) * H + h * D;
+  const int64_t orow = (int64_t)qi * H + h * D;
 #pragma unroll
   for (int dt = 0; dt < 2; ++dt)
 #pragma unroll

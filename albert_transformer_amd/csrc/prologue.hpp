@@ -96,8 +96,10 @@ rows_ids_kernel(const int* __restrict__ ids, const int* __restrict__ cu, int pad
     const int r = start + t;
     row_seq[r] = b;
     row_pos[r] = t;
-    const int id = pad_T ? ids[(int64_t)b * pad_T + t] : ids[r];
-    bad |= (id < 0 || id >= vocab);
+    if (ids) {  // null for the LayerNorm-output entry, which has no IDs
+      const int id = pad_T ? ids[(int64_t)b * pad_T + t] : ids[r];
+      bad |= (id < 0 || id >= vocab);
+    }
   }
   if (bad) atomicOr(status, (int)ST_ID);
 }
