@@ -355,3 +355,39 @@ def test_fused_packed_short_sequences(max_len, n):
     for s in (0, 1, n // 2, n - 1):
         a, b = int(cu[s]), int(cu[s + 1])
         check(got[a:b], oracle.encode_sequence(ids[a:b], W, K), "bf16", f"fused packed L<={max_len} seq{s}")
+
+
+def test_attention_grids_agree_bitwise():
+    """The unfused attention runs on packed 128-row query blocks when the
+    mean length is under 128 and on per-sequence query tiles otherwise.
+    A lane sees its own sequence's keys in the same 32-key blocks either
+    way, so the same sequences give the same bits: packed (mean < 128, a
+    block may hold several whole sequences and parts of two more) against
+    padded to T=256 (256 rows per sequence: per-sequence tiles).  Sampled
+    sequences also against the oracle."""
+    import torch
+    import albert_transformer_amd as A
+    enc = encoder("bf16")
+    W = oracle_weights("bf16")
+    rng = np.random.default_rng(68)
+    lengths = rng.integers(1, 200, 45).astype(np.int32)
+    lengths[:6] = [1, 256, 2, 129, 128, 255]
+    n = len(lengths)
+    assert lengths.sum() < n * 128
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    ids = rng.integers(0, 178, int(cu[-1])).astype(np.int32)
+    out = torch.full((int(cu[-1]), 512), float("nan"), device="cuda")
+    ws = enc.new_workspace(n, int(cu[-1]))
+    assert enc.encode_varlen_raw(dev(ids), dev(cu), 256, out, ws, flags=A.UNFUSED) == 0
+    got = out.cpu().numpy()
+    padded = np.zeros((n, 256), np.int32)
+    for s in range(n):
+        padded[s, :lengths[s]] = ids[cu[s]:cu[s + 1]]
+    wl = synth.Workload("grids", "bf16", padded, lengths, 256)
+    out_pad, _ = _run_padded(enc, wl, flags=A.UNFUSED)
+    for s in range(n):
+        assert np.array_equal(got[cu[s]:cu[s + 1]], out_pad[s, :lengths[s]].astype(np.float32)), s
+    for s in (0, 1, 3, n - 1):
+        a, b = int(cu[s]), int(cu[s + 1])
+        check(got[a:b].astype(np.float64), oracle.encode_sequence(ids[a:b], W, K), "bf16",
+              f"packed attention blocks seq{s}")
