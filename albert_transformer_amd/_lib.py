@@ -23,6 +23,7 @@ F32, BF16, FP8 = 0, 1, 2
 DTYPES = {"f32": F32, "bf16": BF16, "fp8": FP8}
 ASYNC = 1
 UNFUSED = 2
+LN_HANDOFF = 4
 N_TENSORS = 25
 TAPS = {"status": 0, "cu": 1, "row_seq": 2, "row_pos": 3, "emb": 4, "x": 5,
         "qkv": 6, "ctx": 7, "x1": 8, "g": 9, "x8": 10, "x1_8": 11}

@@ -45,6 +45,7 @@ struct albert_ctx {
   int dtype;
   int device;
   int grid_cap;  // persistent GEMM grid: CUs rounded down to a multiple of 8
+  bool ln_pair = false;  // bf16 LayerNorm GEMMs on block pairs (cooperative launch)
   void* mem;
   // device pointers (tables/matrices in dtype, vectors fp32)
   const void *word, *pos, *type, *proj_w, *out_w;
@@ -150,8 +151,13 @@ int e4m3_row_exp(const float* row, int64_t n, float scale) {
   return std::min(k, 127);
 }
 
+__global__ void clear_u64_kernel(unsigned long long* __restrict__ p, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = 0ull;
+}
+
 struct Layout {
-  size_t status, cu, row_seq, row_pos, emb, x, x1, x8, x18, qkv, ctx, g, total;
+  size_t status, cu, row_seq, row_pos, emb, x, x1, x8, x18, qkv, ctx, g, xch, total;
   int64_t rows_cap;
 };
 
@@ -179,6 +185,8 @@ Layout plan(const albert_ctx* c, int n_seq, int64_t max_rows) {
   L.qkv = off; off += align_up((size_t)rows * 3 * H * es, kAlign);
   L.ctx = off; off += align_up((size_t)rows * H * eo, kAlign);
   L.g = off; off += align_up((size_t)rows * c->cfg.ffn * eo, kAlign);
+  // row statistics swapped by the paired LayerNorm GEMMs (bf16)
+  L.xch = off; off += c->dtype == ALBERT_BF16 ? align_up(ln_pair_words(rows) * 8, kAlign) : 0;
   L.total = off;
   return L;
 }
@@ -265,6 +273,37 @@ int run(albert_ctx* c, const int32_t* ids, const int32_t* lens_or_cu, int n_seq,
   g.Y = X; g.ldy = H; g.Y8 = Y8; g.ldy8 = H; g.N = H; g.K = cf.emb;
   timed(c, ALBERT_K_PROJ, s, [&] { gemm_big<T, F8, EPI_BIAS>(g, max_rows, c->grid_cap, s); });
 
+  // LayerNorm GEMMs: bf16 rows split over two blocks that swap row
+  // statistics (full rows in one block otherwise).  Their exchange words
+  // are cleared once per request and whenever the launch tags wrap.
+  constexpr bool can_pair = std::is_same<T, bf16>::value && !F8;
+  const bool pair = can_pair && c->ln_pair;
+  unsigned long long* xch = reinterpret_cast<unsigned long long*>(w + L.xch);
+  const int64_t xwords = (int64_t)ln_pair_words(max_rows);
+  int xtag = 0;
+  bool launch_failed = false;
+  auto clear_xch = [&] {
+    hipLaunchKernelGGL(clear_u64_kernel, dim3((unsigned)((xwords + 255) / 256)), dim3(256), 0, s,
+                       xch, xwords);
+  };
+  if (pair) clear_xch();
+  auto gemm_layernorm = [&](GemmArgs& ga, int kind) {
+    if (pair) {
+      if (++xtag > 4095) {
+        clear_xch();
+        xtag = 1;
+      }
+      ga.xch = xch;
+      ga.xtag = xtag;
+      ga.pair_spin = (flags & ALBERT_LN_HANDOFF) ? 0 : kPairPolls;
+      timed(c, kind, s, [&] {
+        if (gemm_ln_pair(ga, max_rows, c->grid_cap, s) != hipSuccess) launch_failed = true;
+      });
+    } else {
+      timed(c, kind, s, [&] { gemm_ln<T, F8>(ga, max_rows, c->grid_cap, s); });
+    }
+  };
+
   // Q|K|V and attention in one kernel when every sequence fits its 256-row
   // tile (groups of S whole sequences); the unfused pair otherwise.
   constexpr bool can_fuse = std::is_same<T, bf16>::value && !F8;
@@ -299,7 +338,7 @@ int run(albert_ctx* c, const int32_t* ids, const int32_t* lens_or_cu, int n_seq,
     g.X = CTX; g.ldx = H; g.W = lw.o_w; g.wexp = lw.o_e; g.bias = lw.o_b; g.R = X; g.ldr = H;
     g.ln_g = lw.ln1_g; g.ln_b = lw.ln1_b; g.Y = X1; g.ldy = H; g.Y8 = Y18; g.ldy8 = H;
     g.N = H; g.K = H;
-    timed(c, ALBERT_K_ATTN_OUT_LN, s, [&] { gemm_ln<T, F8>(g, max_rows, c->grid_cap, s); });
+    gemm_layernorm(g, ALBERT_K_ATTN_OUT_LN);
 
     g = base;  // FFN 768 -> 2048 + GELU
     g.X = X18; g.ldx = H; g.W = lw.ffn1_w; g.wexp = lw.ffn1_e; g.bias = lw.ffn1_b; g.Y = G;
@@ -310,7 +349,7 @@ int run(albert_ctx* c, const int32_t* ids, const int32_t* lens_or_cu, int n_seq,
     g.X = G; g.ldx = F; g.W = lw.ffn2_w; g.wexp = lw.ffn2_e; g.bias = lw.ffn2_b; g.R = X1;
     g.ldr = H; g.ln_g = lw.ln2_g; g.ln_b = lw.ln2_b; g.Y = X; g.ldy = H; g.Y8 = Y8; g.ldy8 = H;
     g.N = H; g.K = F;
-    timed(c, ALBERT_K_FFN2_LN, s, [&] { gemm_ln<T, F8>(g, max_rows, c->grid_cap, s); });
+    gemm_layernorm(g, ALBERT_K_FFN2_LN);
   }
 
   g = base;  // output projection H -> 512, fp32, into the caller's rows
@@ -320,7 +359,7 @@ int run(albert_ctx* c, const int32_t* ids, const int32_t* lens_or_cu, int n_seq,
   if (pad_T)
     hipLaunchKernelGGL(zero_pad_rows_kernel, dim3(n_seq), dim3(256), 0, s, out, cu, pad_T,
                        cf.out_dim, status);
-  return hipGetLastError() == hipSuccess ? ALBERT_OK : ALBERT_E_HIP;
+  return hipGetLastError() == hipSuccess && !launch_failed ? ALBERT_OK : ALBERT_E_HIP;
 }
 
 // Dispatch on the context's dtype.
@@ -531,6 +570,17 @@ int albert_load_weights(albert_ctx** out_ctx, const albert_config* cfg,
     return ALBERT_E_HIP;
   }
   ctx->grid_cap = std::max(8, n_cu / 8 * 8);
+  {  // paired LayerNorm blocks: shapes they take, and one block per CU fits
+    bool ok = dtype == ALBERT_BF16 && ctx->grid_cap >= 16 && c.hidden == 768 &&
+              ln_pair_k_ok(c.hidden) && ln_pair_k_ok(c.ffn);
+    for (int kr = 0; kr < 3 && ok; ++kr)
+      for (const void* k : {ln_pair_pick<256>(kr), ln_pair_pick<128>(kr)}) {
+        int per_cu = 0;
+        ok = ok && hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, 512, 0) == hipSuccess &&
+             per_cu >= 1;
+      }
+    ctx->ln_pair = ok;
+  }
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (hipMemcpyAsync(ctx->mem, img.data(), off, hipMemcpyHostToDevice, s) != hipSuccess ||
       hipStreamSynchronize(s) != hipSuccess) {

@@ -38,6 +38,7 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegInf = -__builtin_inff();
+constexpr int kStatusSync = 7;  // ALBERT_E_SYNC: cooperating workgroups never met
 
 template <typename T> struct Tr;
 

@@ -14,6 +14,12 @@
 //             statistics never leave the chip
 //   EPI_LN_ACT  store LeakyReLU(LN(Y) * g + beta), no residual (the text
 //             path's convolution blocks)
+//   EPI_LN_PAIR as EPI_LN, with the row split over two blocks of BN = N/2
+//             features that run at the same time: each reduces its half of
+//             every row to a mean and a sum of squared deviations, the two
+//             blocks swap these through device memory, and both combine
+//             them the same way (Chan, Golub and LeVeque's pairwise update),
+//             so the row statistics are identical in both halves
 //   EPI_OUT   store Y as fp32 into the caller's output, packed row m going to
 //             out row seq(m) * T + pos(m) (padded) or m (packed)
 //
@@ -60,7 +66,7 @@
 
 namespace albert {
 
-enum Epi { EPI_BIAS = 0, EPI_GELU = 1, EPI_LN = 2, EPI_OUT = 3, EPI_LN_ACT = 4 };
+enum Epi { EPI_BIAS = 0, EPI_GELU = 1, EPI_LN = 2, EPI_OUT = 3, EPI_LN_ACT = 4, EPI_LN_PAIR = 5 };
 
 struct GemmArgs {
   const void* X;       // [M, K] activations, row stride ldx (elements)
@@ -86,7 +92,19 @@ struct GemmArgs {
   const int* m_ptr;    // device: number of valid rows M
   int N, K;
   int n_tiles;         // N / BN
+  // EPI_LN_PAIR: per row tile 4*BM + 8 words (see the epilogue), cleared
+  // before the first launch that uses them; this launch's tag (1..4095,
+  // distinct among the launches since the clear); polls of the partner's
+  // statistics before handing this half over
+  unsigned long long* xch;
+  int xtag;
+  int pair_spin;
 };
+
+// Polls (each after a short sleep) of a block that is known to be running
+// before giving up and reporting ALBERT_E_SYNC.
+constexpr int kPairSpin = 1 << 20;
+
 
 typedef __attribute__((address_space(3))) void lds_ptr_t;
 
@@ -104,7 +122,7 @@ __device__ __forceinline__ int swz_key(int row) {
 #define ALBERT_WAIT_BARRIER(N) asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory")
 
 template <typename T, bool F8, int BM, int BN, int WGM, int WGN, int RB, int STAGES, int EPI,
-          bool DEFER>
+          bool DEFER, int KR = 0>
 __global__ void __launch_bounds__(WGM * WGN * 64)
 gemm_kernel(GemmArgs g) {
   typedef typename std::conditional<F8, fp8, T>::type TO;  // operand codes
@@ -128,7 +146,9 @@ gemm_kernel(GemmArgs g) {
   constexpr int TM = WTM / 32, TN = WTN / 32;
   constexpr int KSTEPS = BK / KS;             // MFMA k-steps per slice
   constexpr int FCH = FE / CH;                // chunks per fragment (1 bf16, 2 fp32 / E4M3)
-  constexpr bool LNE = EPI == EPI_LN || EPI == EPI_LN_ACT;  // full-row LayerNorm epilogue
+  constexpr bool PAIR = EPI == EPI_LN_PAIR;                // LayerNorm row split over two blocks
+  constexpr bool LNE = EPI == EPI_LN || EPI == EPI_LN_ACT || PAIR;  // LayerNorm epilogue
+  constexpr bool RES = EPI == EPI_LN || PAIR;              // with a residual
   constexpr int NVEC = LNE ? 3 : 1;          // bias (+ LayerNorm gain, shift)
   constexpr int VPT = (BN + NT - 1) / NT;     // vector elements per thread
   static_assert(NINST % NW == 0, "DMA split");
@@ -137,6 +157,7 @@ gemm_kernel(GemmArgs g) {
   static_assert(RB == 64 || RB == 128, "row bytes");
   static_assert(KSTEPS >= 1, "slice shorter than one MFMA step");
   static_assert(STAGES >= 2 && STAGES <= 4, "stages");
+  static_assert(KR >= 0 && KR < STAGES, "K slices past the last whole round");
   static_assert(IPW * (STAGES - 2) <= 63, "vmcnt range");
   static_assert(CPR == 8 ? (NW % 2 == 0) : true, "swizzle key must not depend on i");
   // Deferred stores: bf16 (or E4M3) outputs of tile i are kept in registers
@@ -159,14 +180,21 @@ gemm_kernel(GemmArgs g) {
   // Epilogue vectors, double-buffered across consecutive tiles, and the
   // LayerNorm cross-wave row reduction.
   __shared__ float vecs[2][NVEC][BN];
-  __shared__ float red[LNE ? WGN * BM : 1];
+  __shared__ float red[LNE ? (PAIR ? 2 : 1) * WGN * BM : 1];
+  // EPI_LN_PAIR: per row, mean and squared deviations of the first half of
+  // the features, then of the second
+  __shared__ float pst[PAIR ? 4 * BM : 1];
+  __shared__ int pflag;
 
   if (*g.status != 0) return;
   const int M = *g.m_ptr;
   const int ntiles = ((M + BM - 1) / BM) * g.n_tiles;
-  const int G = gridDim.x;  // the host launches a multiple of 8 blocks
+  const int G = gridDim.x;  // the host launches a multiple of 8 blocks (EPI_LN_PAIR: of 16)
   int tile = (blockIdx.x % 8) * (G / 8) + blockIdx.x / 8;
   if (tile >= ntiles) return;
+  // EPI_LN_PAIR: n_tiles = 2 and G / 8 is even, so the block 8 away (on
+  // the same XCD) holds tile ^ 1, the other half of the same rows, in the
+  // same round
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -394,7 +422,7 @@ gemm_kernel(GemmArgs g) {
   // ------------------------------------------------------------ epilogue
   // acc[i][j][4q+e] holds token m0 + wm*WTM + i*32 + l32 and feature
   // n0 + wn*WTN + j*32 + 8q + 4hh + e.
-  auto epilogue = [&](int em0, int en0, int vb) __attribute__((always_inline)) {
+  auto epilogue = [&](int em0, int en0, int vb) __attribute__((always_inline)) -> bool {
     const float* __restrict__ bias_s = vecs[vb][0];
     if constexpr (LNE) {
       const float* __restrict__ g_s = vecs[vb][1 % NVEC];
@@ -412,7 +440,7 @@ gemm_kernel(GemmArgs g) {
           f32x4 rv[4];  // this column group's residual loads first, then one wait
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            if constexpr (EPI == EPI_LN)
+            if constexpr (RES)
               rv[q] = TS::load4f(R + roff + j * 32 + 8 * q);
             else
               rv[q] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -432,15 +460,17 @@ gemm_kernel(GemmArgs g) {
         if (hh == 0) red[wn * BM + wm * WTM + i * 32 + l32] = s;
       }
       asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-      float mean[TM];
+      constexpr float inv_cols = 1.0f / (PAIR ? BN : 1);  // the block's share of the row (PAIR)
+      constexpr int R2 = PAIR ? WGN * BM : 0;             // where the squared deviations go
+      float mean[TM], rstd[TM];
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
         float s = 0.f;
 #pragma unroll
         for (int w = 0; w < WGN; ++w) s += red[w * BM + wm * WTM + i * 32 + l32];
-        mean[i] = s * (1.0f / N);
+        mean[i] = PAIR ? s * inv_cols : s * (1.0f / N);
       }
-      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      if constexpr (!PAIR) asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
         float s = 0.f;
@@ -452,35 +482,178 @@ gemm_kernel(GemmArgs g) {
             s += d * d;
           }
         s += wave_xor(s, 32);
-        if (hh == 0) red[wn * BM + wm * WTM + i * 32 + l32] = s;
+        if (hh == 0) red[R2 + wn * BM + wm * WTM + i * 32 + l32] = s;
       }
       asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
       T* __restrict__ Y = static_cast<T*>(g.Y);
+      // This block's columns: normalised from registers, or (raw, EPI_LN_PAIR
+      // handing its half over) the values before normalisation.
+      auto store_own = [&](bool raw) __attribute__((always_inline)) {
 #pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        float s = 0.f;
+        for (int i = 0; i < TM; ++i) {
+          const int m = em0 + wm * WTM + i * 32 + l32;
+          if (m >= M) continue;
 #pragma unroll
-        for (int w = 0; w < WGN; ++w) s += red[w * BM + wm * WTM + i * 32 + l32];
-        const float rstd = 1.0f / sqrtf(s * (1.0f / N) + g.eps);
-        const int m = em0 + wm * WTM + i * 32 + l32;
-        if (m >= M) continue;
+          for (int j = 0; j < TN; ++j)
 #pragma unroll
-        for (int j = 0; j < TN; ++j)
+            for (int q = 0; q < 4; ++q) {
+              const int nl = wn * WTN + j * 32 + 8 * q + 4 * hh;
+              float o[4];
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int nl = wn * WTN + j * 32 + 8 * q + 4 * hh;
-            float o[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              o[e] = (acc[i][j][4 * q + e] - mean[i]) * rstd * g_s[nl + e] + b_s[nl + e];
-              if constexpr (EPI == EPI_LN_ACT) o[e] = o[e] >= 0.f ? o[e] : o[e] * g.slope;
+              for (int e = 0; e < 4; ++e) {
+                o[e] = raw ? acc[i][j][4 * q + e]
+                           : (acc[i][j][4 * q + e] - mean[i]) * rstd[i] * g_s[nl + e] + b_s[nl + e];
+                if constexpr (EPI == EPI_LN_ACT) o[e] = o[e] >= 0.f ? o[e] : o[e] * g.slope;
+              }
+              TS::store4(Y + (int64_t)m * g.ldy + en0 + nl, o[0], o[1], o[2], o[3]);
+              if constexpr (F8)
+                store4_as<T, true>(g.Y8, (int64_t)m * g.ldy8 + en0 + nl, o[0], o[1], o[2], o[3]);
             }
-            TS::store4(Y + (int64_t)m * g.ldy + en0 + nl, o[0], o[1], o[2], o[3]);
-            if constexpr (F8)
-              store4_as<T, true>(g.Y8, (int64_t)m * g.ldy8 + en0 + nl, o[0], o[1], o[2], o[3]);
+        }
+      };
+      // EPI_LN_PAIR.  Per row tile the exchange holds each half's 2*BM
+      // statistic words, one word per half saying that the half normalises
+      // itself, and one handoff word; every word carries the launch's tag
+      // in its upper 32 bits (tags start at 1, so cleared words never match).
+      // A block publishes its statistics and polls the partner's for a short
+      // while.  If they all came, it normalises its own half and then learns
+      // whether the partner does the same or handed its half over.  If not
+      // (the partner is late, or not resident), it leaves its values before
+      // normalisation in Y and claims the handoff word: the partner, whenever
+      // it runs, normalises both halves.  If the partner claimed first, this
+      // block normalises both.  Each remaining wait is for a block that has
+      // already published its statistics, so it is running and ends.
+      const int half = en0 / BN;
+      const size_t xbase = (size_t)(em0 / BM) * (4 * BM + 8);
+      // word i of this row tile: statistics [half][2*BM], decisions at 4*BM
+      // + half, the handoff word at 4*BM + 2
+      auto xw = [&](int i) __attribute__((always_inline)) { return g.xch + xbase + i; };
+      const unsigned long long tag = (unsigned long long)(unsigned)g.xtag << 32;
+      constexpr unsigned long long kTagMask = ~0xFFFFFFFFull;
+      // poll word p up to `spin` times for this launch's tag; its value to *dst
+      auto poll = [&](unsigned long long* p, int spin, float* dst) __attribute__((always_inline)) {
+        unsigned long long u = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        for (int polls = 0; (u & kTagMask) != tag; ++polls) {
+          if (polls >= spin) return false;
+          __builtin_amdgcn_s_sleep(1);
+          u = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        *dst = __uint_as_float((unsigned)u);
+        return true;
+      };
+      bool help = false;  // this block also normalises the partner's half
+      if constexpr (PAIR) {
+        // thread t < 2*BM: statistic t / BM (0: mean, 1: squared
+        // deviations) of row t % BM
+        unsigned long long* const theirs = xw((half ^ 1) * 2 * BM + tid);
+        float* const pdst = pst + (half ^ 1) * 2 * BM + tid;
+        bool found = true;
+        if (tid < 2 * BM) {
+          const int kind = tid / BM, row = tid % BM;
+          float v = 0.f;
+#pragma unroll
+          for (int w = 0; w < WGN; ++w) v += red[kind * R2 + w * BM + row];
+          if (kind == 0) v *= inv_cols;
+          __hip_atomic_store(xw(half * 2 * BM + tid), tag | __float_as_uint(v), __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+          pst[half * 2 * BM + tid] = v;
+          found = poll(theirs, g.pair_spin, pdst);
+        }
+        if (__syncthreads_and(found)) {
+          if (tid == 0)
+            __hip_atomic_store(xw(4 * BM + half), tag | 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        } else {
+          store_own(true);
+          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's rows have left
+          __syncthreads();
+          if (tid == 0) {
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+            unsigned long long cur = __hip_atomic_load(xw(4 * BM + 2), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            bool won = false;
+            if ((cur & kTagMask) != tag)  // not claimed in this launch yet
+              won = __hip_atomic_compare_exchange_strong(xw(4 * BM + 2), &cur, tag | (unsigned)(half + 1),
+                                                         __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                                         __HIP_MEMORY_SCOPE_AGENT);
+            pflag = won ? 1 : 0;
           }
+          __syncthreads();
+          if (pflag) return true;  // the partner normalises both halves
+          // the partner handed over first, after publishing its statistics
+          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+          bool ok = true;
+          if (tid < 2 * BM) ok = poll(theirs, kPairSpin, pdst);
+          if (!__syncthreads_and(ok)) return false;
+          help = true;
+        }
+        // both halves combine the same four numbers in the same order
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+          const int row = wm * WTM + i * 32 + l32;
+          const float ma = pst[row], qa = pst[BM + row], mb = pst[2 * BM + row], qb = pst[3 * BM + row];
+          const float d = ma - mb;
+          mean[i] = (ma + mb) * 0.5f;
+          const float m2 = (qa + qb) + d * d * (0.5f * BN);
+          rstd[i] = 1.0f / sqrtf(m2 * (1.0f / N) + g.eps);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+          float s = 0.f;
+#pragma unroll
+          for (int w = 0; w < WGN; ++w) s += red[w * BM + wm * WTM + i * 32 + l32];
+          rstd[i] = 1.0f / sqrtf(s * (1.0f / N) + g.eps);
+        }
       }
-      // the next tile's epilogue reuses `red`: everyone has read it
+      store_own(false);
+      if constexpr (PAIR) {
+        if (!help) {  // does the partner normalise its own half?
+          if (tid == 0) {
+            int r = 2;  // 0: yes, 1: handed over, 2: no answer
+            const unsigned long long handed = tag | (unsigned)((half ^ 1) + 1);
+            for (int polls = 0;; ++polls) {
+              const unsigned long long d =
+                  __hip_atomic_load(xw(4 * BM + (half ^ 1)), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+              if ((d & kTagMask) == tag) { r = 0; break; }
+              if (__hip_atomic_load(xw(4 * BM + 2), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == handed) {
+                r = 1;
+                break;
+              }
+              if (polls >= kPairSpin) break;
+              __builtin_amdgcn_s_sleep(1);
+            }
+            pflag = r;
+          }
+          __syncthreads();
+          const int r = pflag;
+          if (r == 2) return false;
+          if (r == 1) {
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+            help = true;
+          }
+        }
+        if (help) {  // the partner's values before normalisation are in Y
+          const int n0p = (half ^ 1) * BN;
+#pragma unroll
+          for (int i = 0; i < TM; ++i) {
+            const int m = em0 + wm * WTM + i * 32 + l32;
+            if (m >= M) continue;
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                const int c = n0p + wn * WTN + j * 32 + 8 * q + 4 * hh;
+                T* const y = Y + (int64_t)m * g.ldy + c;
+                const f32x4 pv = TS::load4f(y);
+                float o[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                  o[e] = (pv[e] - mean[i]) * rstd[i] * g.ln_g[c + e] + g.ln_b[c + e];
+                TS::store4(y, o[0], o[1], o[2], o[3]);
+              }
+          }
+        }
+      }
+      // the next tile's epilogue reuses `red` and `pst`: everyone has read them
       asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     } else if constexpr (DEFER) {
       // pack into registers; stored during the next tile's K loop
@@ -544,6 +717,7 @@ gemm_kernel(GemmArgs g) {
           }
       }
     }
+    return true;
   };
 
   // --------------------------------------------------------- tile loop
@@ -552,7 +726,7 @@ gemm_kernel(GemmArgs g) {
   vstore(0);
   prologue();
   int vb = 0;
-  const int KT = g.K / BK;  // a multiple of STAGES (checked by the host)
+  const int KT = g.K / BK;  // KR more than a multiple of STAGES, at least STAGES + KR (host)
   for (;;) {
 #pragma unroll
     for (int i = 0; i < TM; ++i)
@@ -600,30 +774,37 @@ gemm_kernel(GemmArgs g) {
       // only for its own DMA of slice t (later slices may still be in flight);
       // the barrier then makes every wave's part visible and frees the buffer
       // consumed at t-1, which receives slice t+STAGES-1.  The main loop is
-      // branch-free and the last STAGES slices are peeled with static waits.
-      for (int kt = 0; kt < KT - STAGES; kt += STAGES) {
-  #pragma unroll
+      // branch-free; the last STAGES + KR slices (KR = KT mod STAGES, fixed
+      // per instantiation) are peeled with static buffers and waits.
+      for (int kt = 0; kt < KT - STAGES - KR; kt += STAGES) {
+#pragma unroll
         for (int s = 0; s < STAGES; ++s) {
           ALBERT_WAIT_BARRIER(IPW * (STAGES - 2));
           issue(ALBERT_BUF((s + STAGES - 1) % STAGES), (kt + s + STAGES - 1) * BK);
           compute(ALBERT_BUF(s));
         }
       }
-      {
-        const int kt = KT - STAGES;
-  #pragma unroll
-        for (int s = 0; s < STAGES; ++s) {
-          // slices issued after slice kt+s: min(STAGES-2, STAGES-1-s)
-          if (s + 1 < STAGES - 1 || s == 0)
-            ALBERT_WAIT_BARRIER(IPW * (STAGES - 2));
-          else if (s == STAGES - 2)
-            ALBERT_WAIT_BARRIER(IPW * (STAGES > 2 ? 1 : 0));
+      // kt0 is a multiple of STAGES, so slice kt0 + s sits in buffer
+      // s % STAGES; after slice kt0 + s, min(STAGES-2, NS-1-s) younger
+      // slices are in flight
+      auto tail = [&](auto rc) __attribute__((always_inline)) {
+        constexpr int NS = STAGES + decltype(rc)::value;
+        const int kt0 = KT - NS;
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+          const int pend = STAGES - 2 < NS - 1 - s ? STAGES - 2 : NS - 1 - s;
+          if (pend >= 2)
+            ALBERT_WAIT_BARRIER(2 * IPW);
+          else if (pend == 1)
+            ALBERT_WAIT_BARRIER(IPW);
           else
             ALBERT_WAIT_BARRIER(0);
-          if (s == 0) issue(ALBERT_BUF(STAGES - 1), (kt + STAGES - 1) * BK);
-          compute(ALBERT_BUF(s));
+          if (s + STAGES - 1 < NS)
+            issue(ALBERT_BUF((s + STAGES - 1) % STAGES), (kt0 + s + STAGES - 1) * BK);
+          compute(ALBERT_BUF(s % STAGES));
         }
-      }
+      };
+      tail(std::integral_constant<int, KR>{});
     }
 
     const int next = tile + G;
@@ -637,7 +818,13 @@ gemm_kernel(GemmArgs g) {
     // the MFMAs above), so the next tile's first slices may land there
     asm volatile("s_barrier" ::: "memory");
     if (more) prologue();
-    epilogue(em0, en0, vb);
+    if (!epilogue(em0, en0, vb)) {
+      // EPI_LN_PAIR: the partner never delivered its statistics; report it
+      // and stop (nothing of this tile is stored)
+      if (tid == 0) __hip_atomic_store(const_cast<int*>(g.status), kStatusSync, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the next tile's DMA has landed
+      return;
+    }
     if (!more) {
 #pragma unroll
       for (int bt = 0; bt < NB; ++bt) store_batch(bt);  // last tile: write everything now

@@ -212,7 +212,6 @@ lstm_kernel(LstmArgs a) {
 // workgroup, after which its partners' waits run out too.
 constexpr int kMcMembers = 4;
 constexpr int kMcSpin = 1 << 20;  // polls (each after a short sleep) before giving up
-constexpr int kStatusSync = 7;    // ALBERT_E_SYNC
 
 __global__ void zero_ints_kernel(int* __restrict__ p, int n) {
   const int i = blockIdx.x * 256 + threadIdx.x;

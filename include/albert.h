@@ -68,6 +68,12 @@ enum albert_dtype { ALBERT_F32 = 0, ALBERT_BF16 = 1, ALBERT_FP8 = 2 };
                              holds its checkpoint.  Text path: run the LSTM
                              recurrence as one workgroup per direction and
                              32 sequences instead of four cooperating ones */
+#define ALBERT_LN_HANDOFF 4u /* testing aid, bf16: the two workgroups that
+                             share each LayerNorm row tile do not wait for
+                             each other's row statistics, so the fallback in
+                             which one hands its rows to the other runs
+                             (results equal to the default within bf16
+                             rounding) */
 
 typedef struct albert_config {
   int32_t vocab;    /* word-table rows (Kokoro: 178)                       */

@@ -391,3 +391,30 @@ def test_attention_grids_agree_bitwise():
         a, b = int(cu[s]), int(cu[s + 1])
         check(got[a:b].astype(np.float64), oracle.encode_sequence(ids[a:b], W, K), "bf16",
               f"packed attention blocks seq{s}")
+
+
+@pytest.mark.parametrize("B,T,seed", [(6, 200, 71), (256, 128, 72)])
+def test_layernorm_pair_handoff(B, T, seed):
+    """bf16 LayerNorm products split each 768-wide row tile between two
+    workgroups that swap row statistics.  ALBERT_LN_HANDOFF stops them from
+    waiting for each other, so in every row tile one half hands its rows
+    over (before normalisation, as bf16) and the other normalises both:
+    the fallback for a partner that is late or not resident.  Outputs agree
+    with the default run and, on sampled sequences, with the oracle, to the
+    bf16 tolerance.  B=6 runs 128-row tiles, B=256 x T=128 256-row tiles."""
+    import albert_transformer_amd as A
+    enc = encoder("bf16")
+    W = oracle_weights("bf16")
+    wl = synth.random_padded(seed, B=B, T=T, lo=1, hi=T)
+    wl.lengths[0] = T
+    a, _ = _run_padded(enc, wl)
+    for rep in range(2):  # which half hands over varies from run to run
+        b, _ = _run_padded(enc, wl, flags=A.LN_HANDOFF)
+        for s in range(B):
+            L = int(wl.lengths[s])
+            check(b[s, :L], a[s, :L], "bf16", f"handoff vs default seq{s} run{rep}")
+        pad = np.arange(T)[None, :] >= wl.lengths[:, None]
+        assert np.all(b[pad] == 0.0)
+    for s in (0, B - 1):
+        L = int(wl.lengths[s])
+        check(b[s, :L], oracle.encode_sequence(wl.ids[s, :L], W, K), "bf16", f"handoff seq{s}")
