@@ -25,6 +25,7 @@
 // codes (its one consumer is the output projection's matrix product).
 #pragma once
 
+#include "attend.hpp"
 #include "common.hpp"
 
 namespace albert {
@@ -40,7 +41,9 @@ struct AttnArgs {
 };
 
 template <typename T, bool F8>
-__global__ void __launch_bounds__(256)
+// At least three waves per SIMD (168 VGPRs): the staging of each chunk is
+// latency-bound, and with two the kernel ran 28 % slower; four spill.
+__global__ void __launch_bounds__(256, 3)
 attention_kernel(AttnArgs a) {
   typedef Tr<T> TR;
   constexpr int H = 768, D = 64, LDQKV = 3 * H;
@@ -122,50 +125,15 @@ attention_kernel(AttnArgs a) {
       }
       __syncthreads();
 
+      // this lane's keys in the chunk: all of it up to the sequence's end,
+      // or none when the lane's query belongs to another sequence
       const int nkb = (nk + 31) / 32;
-      for (int kb = 0; kb < nkb; ++kb) {
-        f32x16 s;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[r] = 0.f;
-        const T* kp = Ks + (kb * 32 + l32) * LDKS + hh * 8;
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) TR::mma(s, TR::load(kp + kk * 16), fq[kk]);
-        // s[r] = score of key c0 + kb*32 + 8(r/4) + 4hh + r%4 for query qi
-        const int kbase = c0 + kb * 32 + 4 * hh;
-        float mx = kNegInf;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = kbase + 8 * (r >> 2) + (r & 3);
-          if (key >= L || !mine) s[r] = kNegInf;
-          mx = fmaxf(mx, s[r]);
-        }
-        mx = fmaxf(mx, wave_xor(mx, 32));
-        const float mnew = fmaxf(mrun, mx);
-        // a lane that has not met its own sequence yet keeps a zero state
-        const float alpha = mnew == kNegInf ? 1.f : fast_exp2((mrun - mnew) * kLog2e);
-        const float mb = mnew == kNegInf ? 0.f : mnew * kLog2e;
-        float p[16];
-        float psum = 0.f;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          p[r] = fast_exp2(s[r] * kLog2e - mb);
-          psum += p[r];
-        }
-        lrun = lrun * alpha + psum;
-        mrun = mnew;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) { o[0][r] *= alpha; o[1][r] *= alpha; }
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          // element e of this lane <-> key 16c + 4hh + e (e < 4), 16c + 8 + 4hh + e - 4
-          const typename TR::frag fp = TR::from_f32(p + 8 * c);
-#pragma unroll
-          for (int dt = 0; dt < 2; ++dt) {
-            const T* vp = Vt + (dt * 32 + l32) * LDVT + kb * 32 + 16 * c + 4 * hh;
-            TR::mma(o[dt], TR::load2x4(vp, vp + 8), fp);
-          }
-        }
-      }
+      attend_pass<T>(o, mrun, lrun, fq, nkb, 0, mine ? L - c0 : 0, hh,
+                     [&](int b, int kk) { return TR::load(Ks + (b * 32 + l32) * LDKS + hh * 8 + kk * 16); },
+                     [&](int b, int c, int dt) {
+                       const T* vp = Vt + (dt * 32 + l32) * LDVT + b * 32 + 16 * c + 4 * hh;
+                       return TR::load2x4(vp, vp + 8);
+                     });
     }
   }
   lrun += wave_xor(lrun, 32);

@@ -26,6 +26,7 @@
 // so key blocks outside it are masked per lane.
 #pragma once
 
+#include "attend.hpp"
 #include "common.hpp"
 #include "gemm.hpp"
 
@@ -213,46 +214,15 @@ qkv_attention_kernel(QkvAttnArgs a) {
 #pragma unroll
   for (int r = 0; r < 16; ++r) { o[0][r] = 0.f; o[1][r] = 0.f; }
   float mrun = kNegInf, lrun = 0.f;
-  for (int kbase = kb0; kbase < kb1; kbase += 32) {
-    f32x16 sc;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) sc[r] = 0.f;
-    const bf16* kp = Ks + (kbase + l32) * LDQ + hh * 8;
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) TR::mma(sc, TR::load(kp + kk * 16), fq[kk]);
-    // sc[r] = score of key kbase + 8(r/4) + 4hh + r%4 for this lane's query
-    float mx = kNegInf;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int kidx = kbase + 8 * (r >> 2) + 4 * hh + (r & 3);
-      if (kidx < ks || kidx >= ke) sc[r] = kNegInf;
-      mx = fmaxf(mx, sc[r]);
-    }
-    mx = fmaxf(mx, wave_xor(mx, 32));
-    const float mnew = fmaxf(mrun, mx);
-    // a lane may see whole blocks before its own keys: keep it at zero
-    const float alpha = mnew == kNegInf ? 1.f : fast_exp2((mrun - mnew) * kLog2e);
-    const float mb = mnew == kNegInf ? 0.f : mnew * kLog2e;
-    float p[16];
-    float psum = 0.f;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      p[r] = fast_exp2(sc[r] * kLog2e - mb);
-      psum += p[r];
-    }
-    lrun = lrun * alpha + psum;
-    mrun = mnew;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) { o[0][r] *= alpha; o[1][r] *= alpha; }
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const bf16x8 fp = TR::from_f32(p + 8 * c);
-#pragma unroll
-      for (int dt = 0; dt < 2; ++dt) {
-        const bf16* vp = (dt == 0 ? Vt0 : Vt1) + l32 * LDV + kbase + 16 * c + 4 * hh;
-        TR::mma(o[dt], TR::load2x4(vp, vp + 8), fp);
-      }
-    }
+  // passes of up to 128 keys from the wave's first key block (for a wave
+  // whose queries share one sequence, its start, as in the separate kernel)
+  for (int kc = kb0; kc < kb1; kc += 128) {
+    attend_pass<bf16>(o, mrun, lrun, fq, min(4, (kb1 - kc) / 32), ks - kc, ke - kc, hh,
+                      [&](int b, int kk) { return TR::load(Ks + (kc + b * 32 + l32) * LDQ + hh * 8 + kk * 16); },
+                      [&](int b, int c, int dt) {
+                        const bf16* vp = (dt == 0 ? Vt0 : Vt1) + l32 * LDV + kc + b * 32 + 16 * c + 4 * hh;
+                        return TR::load2x4(vp, vp + 8);
+                      });
   }
   lrun += wave_xor(lrun, 32);
   if (qr < nrows) {
