@@ -45,7 +45,7 @@ struct albert_ctx {
   int dtype;
   int device;
   int grid_cap;  // persistent GEMM grid: CUs rounded down to a multiple of 8
-  bool ln_pair = false;  // bf16 LayerNorm GEMMs on block pairs (cooperative launch)
+  bool ln_pair = false;  // LayerNorm GEMMs on block pairs (bf16 storage)
   void* mem;
   // device pointers (tables/matrices in dtype, vectors fp32)
   const void *word, *pos, *type, *proj_w, *out_w;
@@ -186,7 +186,7 @@ Layout plan(const albert_ctx* c, int n_seq, int64_t max_rows) {
   L.ctx = off; off += align_up((size_t)rows * H * eo, kAlign);
   L.g = off; off += align_up((size_t)rows * c->cfg.ffn * eo, kAlign);
   // row statistics swapped by the paired LayerNorm GEMMs (bf16)
-  L.xch = off; off += c->dtype == ALBERT_BF16 ? align_up(ln_pair_words(rows) * 8, kAlign) : 0;
+  L.xch = off; off += c->dtype != ALBERT_F32 ? align_up(ln_pair_words(rows) * 8, kAlign) : 0;
   L.total = off;
   return L;
 }
@@ -273,10 +273,11 @@ int run(albert_ctx* c, const int32_t* ids, const int32_t* lens_or_cu, int n_seq,
   g.Y = X; g.ldy = H; g.Y8 = Y8; g.ldy8 = H; g.N = H; g.K = cf.emb;
   timed(c, ALBERT_K_PROJ, s, [&] { gemm_big<T, F8, EPI_BIAS>(g, max_rows, c->grid_cap, s); });
 
-  // LayerNorm GEMMs: bf16 rows split over two blocks that swap row
-  // statistics (full rows in one block otherwise).  Their exchange words
-  // are cleared once per request and whenever the launch tags wrap.
-  constexpr bool can_pair = std::is_same<T, bf16>::value && !F8;
+  // LayerNorm GEMMs: bf16 rows (bf16 or E4M3 operands) split over two
+  // blocks that swap row statistics (full rows in one block otherwise).
+  // Their exchange words are cleared once per request and whenever the
+  // launch tags wrap.
+  constexpr bool can_pair = std::is_same<T, bf16>::value;
   const bool pair = can_pair && c->ln_pair;
   unsigned long long* xch = reinterpret_cast<unsigned long long*>(w + L.xch);
   const int64_t xwords = (int64_t)ln_pair_words(max_rows);
@@ -297,7 +298,7 @@ int run(albert_ctx* c, const int32_t* ids, const int32_t* lens_or_cu, int n_seq,
       ga.xtag = xtag;
       ga.pair_spin = (flags & ALBERT_LN_HANDOFF) ? 0 : kPairPolls;
       timed(c, kind, s, [&] {
-        if (gemm_ln_pair(ga, max_rows, c->grid_cap, s) != hipSuccess) launch_failed = true;
+        if (gemm_ln_pair<F8>(ga, max_rows, c->grid_cap, s) != hipSuccess) launch_failed = true;
       });
     } else {
       timed(c, kind, s, [&] { gemm_ln<T, F8>(ga, max_rows, c->grid_cap, s); });
@@ -571,14 +572,22 @@ int albert_load_weights(albert_ctx** out_ctx, const albert_config* cfg,
   }
   ctx->grid_cap = std::max(8, n_cu / 8 * 8);
   {  // paired LayerNorm blocks: shapes they take, and one block per CU fits
-    bool ok = dtype == ALBERT_BF16 && ctx->grid_cap >= 16 && c.hidden == 768 &&
-              ln_pair_k_ok(c.hidden) && ln_pair_k_ok(c.ffn);
-    for (int kr = 0; kr < 3 && ok; ++kr)
-      for (const void* k : {ln_pair_pick<256>(kr), ln_pair_pick<128>(kr)}) {
-        int per_cu = 0;
-        ok = ok && hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, 512, 0) == hipSuccess &&
-             per_cu >= 1;
+    const bool f8 = dtype == ALBERT_FP8;
+    bool ok = dtype != ALBERT_F32 && ctx->grid_cap >= 16 && c.hidden == 768 &&
+              ln_pair_k_ok(c.hidden, f8) && ln_pair_k_ok(c.ffn, f8);
+    std::vector<const void*> ks;
+    if (f8) ks.push_back(reinterpret_cast<const void*>(ln_pair_kernel_f8));
+    else
+      for (int kr = 0; kr < 3; ++kr) {
+        ks.push_back(ln_pair_pick<256>(kr));
+        ks.push_back(ln_pair_pick<128>(kr));
       }
+    for (const void* k : ks) {
+      int per_cu = 0;
+      ok = ok && hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, f8 ? 256 : 512, 0) ==
+                     hipSuccess &&
+           per_cu >= 1;
+    }
     ctx->ln_pair = ok;
   }
   hipStream_t s = static_cast<hipStream_t>(stream);

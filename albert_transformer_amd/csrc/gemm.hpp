@@ -158,6 +158,7 @@ gemm_kernel(GemmArgs g) {
   static_assert(KSTEPS >= 1, "slice shorter than one MFMA step");
   static_assert(STAGES >= 2 && STAGES <= 4, "stages");
   static_assert(KR >= 0 && KR < STAGES, "K slices past the last whole round");
+  static_assert(EPI != EPI_LN_PAIR || 2 * BM <= NT, "one thread per row statistic");
   static_assert(IPW * (STAGES - 2) <= 63, "vmcnt range");
   static_assert(CPR == 8 ? (NW % 2 == 0) : true, "swizzle key must not depend on i");
   // Deferred stores: bf16 (or E4M3) outputs of tile i are kept in registers
@@ -506,8 +507,9 @@ gemm_kernel(GemmArgs g) {
                 if constexpr (EPI == EPI_LN_ACT) o[e] = o[e] >= 0.f ? o[e] : o[e] * g.slope;
               }
               TS::store4(Y + (int64_t)m * g.ldy + en0 + nl, o[0], o[1], o[2], o[3]);
-              if constexpr (F8)
-                store4_as<T, true>(g.Y8, (int64_t)m * g.ldy8 + en0 + nl, o[0], o[1], o[2], o[3]);
+              if constexpr (F8) {
+                if (!raw) store4_as<T, true>(g.Y8, (int64_t)m * g.ldy8 + en0 + nl, o[0], o[1], o[2], o[3]);
+              }
             }
         }
       };
@@ -649,6 +651,8 @@ gemm_kernel(GemmArgs g) {
                 for (int e = 0; e < 4; ++e)
                   o[e] = (pv[e] - mean[i]) * rstd[i] * g.ln_g[c + e] + g.ln_b[c + e];
                 TS::store4(y, o[0], o[1], o[2], o[3]);
+                if constexpr (F8)
+                  store4_as<T, true>(g.Y8, (int64_t)m * g.ldy8 + c, o[0], o[1], o[2], o[3]);
               }
           }
         }

@@ -93,17 +93,21 @@ void gemm_ln(GemmArgs g, int64_t max_rows, int grid_cap, hipStream_t s) {
 }
 
 // LayerNorm over rows of 768 split between two blocks of 384 features
-// (EPI_LN_PAIR, bf16): 256-row tiles (4 x 2 waves of 64 x 192) when they
-// fill the chip, else 128-row tiles (2 x 4 waves of 64 x 96); three
-// stages of 32-deep K slices, the kernel instantiated per K slices mod 3.
-// At most grid_cap blocks rounded down to a multiple of 16, so that the
-// two halves of a row tile normally run at the same time on one XCD (a
-// half whose partner is late hands its rows over instead of waiting).  The
-// caller clears g.xch before the first launch and gives each launch since
-// then its own g.xtag.
+// (EPI_LN_PAIR, bf16 storage).  bf16 operands: 256-row tiles (4 x 2 waves
+// of 64 x 192) when they fill the chip, else 128-row tiles (2 x 4 waves of
+// 64 x 96), three stages of 32-deep K slices, the kernel instantiated per
+// K slices mod 3.  E4M3 operands: 128-row tiles of 2 x 2 waves of 64 x 192
+// (one wave per SIMD: each wave may hold 512 registers), two stages of
+// 64-deep slices; with eight waves, or three stages, they spill.  At most
+// grid_cap blocks rounded down to a multiple of 16, so that the two halves
+// of a row tile normally run at the same time on one XCD (a half whose
+// partner is late hands its rows over instead of waiting).  The caller
+// clears g.xch before the first launch and gives each launch since then
+// its own g.xtag.
 template <int BM, int KR>
 constexpr auto ln_pair_kernel =
     gemm_kernel<bf16, false, BM, 384, BM / 64, 8 / (BM / 64), 64, 3, EPI_LN_PAIR, false, KR>;
+constexpr auto ln_pair_kernel_f8 = gemm_kernel<bf16, true, 128, 384, 2, 2, 64, 2, EPI_LN_PAIR, false, 0>;
 template <int BM>
 inline const void* ln_pair_pick(int kr) {
   return kr == 0   ? reinterpret_cast<const void*>(ln_pair_kernel<BM, 0>)
@@ -114,29 +118,34 @@ inline const void* ln_pair_pick(int kr) {
 // (each poll is a device-scope load plus a short sleep, about a
 // microsecond: the halves of a tile normally finish within a few).
 constexpr int kPairPolls = 64;
-inline int ln_pair_rows(int64_t max_rows, int grid_cap) {
-  return (max_rows + 255) / 256 * 2 >= grid_cap ? 256 : 128;
+inline int ln_pair_rows(int64_t max_rows, int grid_cap, bool f8) {
+  return !f8 && (max_rows + 255) / 256 * 2 >= grid_cap ? 256 : 128;
 }
-// K the pair kernels accept: whole 32-deep slices, at least 3 + 2 of them
-inline bool ln_pair_k_ok(int K) { return K % 32 == 0 && K / 32 >= 5; }
+// K the pair kernels accept: bf16, whole 32-deep slices, at least 3 + 2 of
+// them; E4M3, an even number of 64-deep slices
+inline bool ln_pair_k_ok(int K, bool f8) {
+  return f8 ? K % 128 == 0 && K > 0 : K % 32 == 0 && K / 32 >= 5;
+}
 // exchange words the pair launches need for up to max_rows rows: 4*BM + 8
 // per row tile, for either tile height
 inline size_t ln_pair_words(int64_t max_rows) {
   return (size_t)std::max((max_rows + 127) / 128 * (4 * 128 + 8), (max_rows + 255) / 256 * (4 * 256 + 8));
 }
+template <bool F8>
 inline hipError_t gemm_ln_pair(GemmArgs g, int64_t max_rows, int grid_cap, hipStream_t s) {
-  if (!ln_pair_k_ok(g.K) || g.N != 768) return hipErrorInvalidValue;
-  const int BM = ln_pair_rows(max_rows, grid_cap);
+  if (!ln_pair_k_ok(g.K, F8) || g.N != 768) return hipErrorInvalidValue;
+  const int BM = ln_pair_rows(max_rows, grid_cap, F8);
   g.n_tiles = 2;
   const int64_t tiles = (max_rows + BM - 1) / BM * 2;
   const int64_t grid = std::min<int64_t>((tiles + 15) / 16 * 16, grid_cap / 16 * 16);
-  const int kr = (g.K / 32) % 3;
-  const void* k = BM == 256 ? ln_pair_pick<256>(kr) : ln_pair_pick<128>(kr);
+  const void* k = F8 ? reinterpret_cast<const void*>(ln_pair_kernel_f8)
+                     : BM == 256 ? ln_pair_pick<256>((g.K / 32) % 3) : ln_pair_pick<128>((g.K / 32) % 3);
+  const unsigned threads = F8 ? 256 : 512;
   const LaunchEvents ev = g_launch_events;
   g_launch_events = LaunchEvents{};
   void* args[] = {&g};
-  const hipError_t e = hipExtLaunchKernel(k, dim3((unsigned)grid), dim3(512), args, 0, s, ev.start,
-                                          ev.stop, 0);
+  const hipError_t e = hipExtLaunchKernel(k, dim3((unsigned)grid), dim3(threads), args, 0, s,
+                                          ev.start, ev.stop, 0);
   return e;
 }
 

@@ -63,14 +63,14 @@ def _tap(enc, ws, n_seq, rows_cap, name, rows, codes):
     return t.view(-1, stride)[:rows].double().numpy()
 
 
-def _run_features(enc, x, lengths):
+def _run_features(enc, x, lengths, flags=0):
     import torch
     cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
     total = int(cu[-1])
     out = torch.full((total, 512), float("nan"), device="cuda")
     ws = enc.new_workspace(len(lengths), total)
     rc = enc.encode_features_raw(dev(np.ascontiguousarray(x, np.float32)), dev(cu),
-                                 int(max(lengths)), out, ws)
+                                 int(max(lengths)), out, ws, flags=flags)
     assert rc == 0, rc
     return out.cpu().numpy().astype(np.float64), ws, cu
 
@@ -230,6 +230,34 @@ def test_fp8_full_depth_parity():
         err = float(np.max(np.abs(out[sl] - ref)))
         cos = float(np.min(row_cosines(out[sl], ref)))
         print(f"[fp8] full depth seq{s} L={lengths[s]} max_abs={err:.3e} min_cos={cos:.6f}", flush=True)
+        assert err <= FP8_MAX_ABS and cos >= FP8_MIN_COS
+
+
+def test_fp8_layernorm_pair_handoff():
+    """E4M3 LayerNorm products split each row tile between two workgroups
+    that swap row statistics; ALBERT_LN_HANDOFF makes one half of every
+    tile hand its rows over (before normalisation, as bf16) instead of
+    waiting.  Both runs meet the full-depth bar against the emulation, and
+    agree with each other to it (E4M3 codes decided from the bf16 hand-over
+    may flip)."""
+    import albert_transformer_amd as A
+    enc = _enc("fp8")
+    rng = np.random.default_rng(10)
+    lengths = [128, 300, 5, 97]
+    x = rng.normal(0, 1, (sum(lengths), 128))
+    a, _, cu = _run_features(enc, x, lengths)
+    for rep in range(2):
+        b, _, _ = _run_features(enc, x, lengths, flags=A.LN_HANDOFF)
+        err = float(np.max(np.abs(a - b)))
+        cos = float(np.min(row_cosines(a, b)))
+        print(f"[fp8] handoff vs default run{rep} max_abs={err:.3e} min_cos={cos:.6f}", flush=True)
+        assert err <= FP8_MAX_ABS and cos >= FP8_MIN_COS
+    for s in (0, 1):
+        sl = slice(int(cu[s]), int(cu[s + 1]))
+        ref = oracle.encode_fp8_features(x[sl], _w8(), K)
+        err = float(np.max(np.abs(b[sl] - ref)))
+        cos = float(np.min(row_cosines(b[sl], ref)))
+        print(f"[fp8] handoff seq{s} max_abs={err:.3e} min_cos={cos:.6f}", flush=True)
         assert err <= FP8_MAX_ABS and cos >= FP8_MIN_COS
 
 
