@@ -34,7 +34,8 @@ using namespace albert;
 // plus per-row E8M0 exponents under ALBERT_FP8 -- vectors fp32).
 struct LayerW {
   const void *qkv_w, *o_w, *ffn1_w, *ffn2_w;
-  const bf16* qkv_wh;  // bf16 only: [12][192][768] per head q/8 | k | v rows
+  const void* qkv_wh;  // bf16 / E4M3: [12][192][768] per head q/8 | k | v rows
+  const unsigned char* qkv_eh;  // E4M3: their E8M0 exponents [12][192]
   const float* qkv_bh; // [12][192]
   const unsigned char *qkv_e, *o_e, *ffn1_e, *ffn2_e;
   const float *qkv_b, *o_b, *ln1_g, *ln1_b, *ffn1_b, *ffn2_b, *ln2_g, *ln2_b;
@@ -307,18 +308,19 @@ int run(albert_ctx* c, const int32_t* ids, const int32_t* lens_or_cu, int n_seq,
 
   // Q|K|V and attention in one kernel when every sequence fits its 256-row
   // tile (groups of S whole sequences); the unfused pair otherwise.
-  constexpr bool can_fuse = std::is_same<T, bf16>::value && !F8;
-  const bool fuse = can_fuse && !feats && max_len <= 256 && !(flags & ALBERT_UNFUSED);
+  constexpr bool can_fuse = std::is_same<T, bf16>::value;
+  const bool fuse = can_fuse && max_len <= 256 && !(flags & ALBERT_UNFUSED);
   const int S = 256 / std::max(max_len, 1);
   const int64_t pairs = fuse ? (int64_t)((n_seq + S - 1) / S) * cf.heads : 0;
   for (int it = 0; it < cf.n_iter; ++it) {
     const LayerW& lw = c->layers[(size_t)((int64_t)it * cf.n_groups / cf.n_iter)];
     if (fuse) {
-      QkvAttnArgs qa{static_cast<const bf16*>(X8), lw.qkv_wh, lw.qkv_bh,
-                     static_cast<bf16*>(CTX), cu, row_seq, status, n_seq, S, (int)pairs};
+      QkvAttnArgs qa{X8, lw.qkv_wh, lw.qkv_eh, lw.qkv_bh, CTX, cu, row_seq, status, n_seq, S,
+                     (int)pairs};
       timed(c, ALBERT_K_QKV_ATTN, s, [&] {
-        launch_kernel(qkv_attention_kernel, dim3((unsigned)((pairs + 7) / 8 * 8)), dim3(512), s,
-                      qa);
+        if constexpr (can_fuse)
+          launch_kernel(qkv_attention_kernel<F8>, dim3((unsigned)((pairs + 7) / 8 * 8)), dim3(512),
+                        s, qa);
       });
     } else {
       g = base;  // fused Q|K|V projection
@@ -438,8 +440,8 @@ int albert_load_weights(albert_ctx** out_ctx, const albert_config* cfg,
   enum { S_WORD, S_POS, S_TYPE, S_EMB_G, S_EMB_B, S_PROJ_W, S_PROJ_B, S_OUT_W, S_OUT_B,
          S_PROJ_E, S_OUT_E, S_LAYER0 };
   enum { L_QKV_W, L_QKV_B, L_O_W, L_O_B, L_LN1_G, L_LN1_B, L_F1_W, L_F1_B, L_F2_W, L_F2_B,
-         L_LN2_G, L_LN2_B, L_QKV_E, L_O_E, L_F1_E, L_F2_E, L_QKV_WH, L_QKV_BH, L_SEGS };
-  const bool hm = dtype == ALBERT_BF16;  // head-major Q|K|V copy for the fused kernel
+         L_LN2_G, L_LN2_B, L_QKV_E, L_O_E, L_F1_E, L_F2_E, L_QKV_WH, L_QKV_BH, L_QKV_EH, L_SEGS };
+  const bool hm = dtype != ALBERT_F32;  // head-major Q|K|V copy for the fused kernel
   struct Seg { size_t off, bytes; };
   std::vector<Seg> seg;
   size_t off = 0;
@@ -472,8 +474,9 @@ int albert_load_weights(albert_ctx** out_ctx, const albert_config* cfg,
     add(f8 ? (size_t)H : 0);               // o exponents
     add(f8 ? (size_t)c.ffn : 0);           // ffn1 exponents
     add(f8 ? (size_t)H : 0);               // ffn2 exponents
-    add(hm ? (size_t)3 * H * H * 2 : 0);   // head-major q/8 | k | v
+    add(hm ? (size_t)3 * H * H * em : 0);  // head-major q/8 | k | v
     add(hm ? (size_t)3 * H * 4 : 0);       // their biases
+    add(hm && f8 ? (size_t)3 * H : 0);     // their exponents
   }
   std::vector<unsigned char> img(off, 0);
 
@@ -544,15 +547,19 @@ int albert_load_weights(albert_ctx** out_ctx, const albert_config* cfg,
     put_vec(s0 + L_LN2_B, t[15], H, 1.f, 0);
     if (hm) {  // head h: rows h*64.. of q (scaled), then of k, then of v
       const int64_t D = c.head_dim, NH = c.heads;
-      uint16_t* wd = reinterpret_cast<uint16_t*>(img.data() + seg[s0 + L_QKV_WH].off);
+      unsigned char* wd = img.data() + seg[s0 + L_QKV_WH].off;
       float* bd = reinterpret_cast<float*>(img.data() + seg[s0 + L_QKV_BH].off);
+      const unsigned char* wq = img.data() + seg[s0 + L_QKV_W].off;  // packed rows, as stored
+      const unsigned char* eq = img.data() + seg[s0 + L_QKV_E].off;
+      unsigned char* ed = img.data() + seg[s0 + L_QKV_EH].off;
       for (int64_t hd = 0; hd < NH; ++hd)
         for (int64_t part = 0; part < 3; ++part)
           for (int64_t dd = 0; dd < D; ++dd) {
             const int64_t src_row = hd * D + dd, dst_row = (hd * 3 + part) * D + dd;
             const float sc = part == 0 ? qscale : 1.f;
-            for (int64_t k = 0; k < H; ++k)
-              wd[dst_row * H + k] = f32_to_bf16_bits(t[2 * part][src_row * H + k] * sc);
+            // the same stored row (bf16 values or E4M3 codes), moved
+            std::memcpy(wd + dst_row * H * em, wq + (part * H + src_row) * H * em, (size_t)(H * em));
+            if (f8) ed[dst_row] = eq[part * H + src_row];
             bd[dst_row] = t[2 * part + 1][src_row] * sc;
           }
     }
@@ -617,7 +624,8 @@ int albert_load_weights(albert_ctx** out_ctx, const albert_config* cfg,
     lw.ffn2_w = P(s0 + L_F2_W); lw.ffn2_b = Pf(s0 + L_F2_B);
     lw.ln2_g = Pf(s0 + L_LN2_G); lw.ln2_b = Pf(s0 + L_LN2_B);
     lw.qkv_e = Pe(s0 + L_QKV_E); lw.o_e = Pe(s0 + L_O_E);
-    lw.qkv_wh = reinterpret_cast<const bf16*>(P(s0 + L_QKV_WH));
+    lw.qkv_wh = P(s0 + L_QKV_WH);
+    lw.qkv_eh = Pe(s0 + L_QKV_EH);
     lw.qkv_bh = Pf(s0 + L_QKV_BH);
     lw.ffn1_e = Pe(s0 + L_F1_E); lw.ffn2_e = Pe(s0 + L_F2_E);
   }

@@ -1,5 +1,5 @@
 // Fused Q|K|V projection and attention for one head of a group of whole
-// sequences (bf16).
+// sequences (bf16 storage; bf16 or E4M3 matrix-product operands).
 //
 // The layer's q, k, v projections ("Inside One Real ALBERT Layer", step 3)
 // and the masked-softmax attention (step 4; "How Kokoro TTS Works and Where
@@ -12,10 +12,12 @@
 // the unfused path) and runs the attention of every query against the keys
 // of its own sequence.  Only the context leaves the workgroup.
 //
-// GEMM phase: 256 rows x 192 features, K = 768 in slices of 64 staged in
-// LDS by buffer_load ... lds DMA (two stages), 8 waves as 4 (rows) x 2
-// (features) of 64 x 96; weights are the MFMA A operand, tokens B (lane =
-// token), as in gemm.hpp.  Rows of the tile past the group belong to the
+// GEMM phase: 256 rows x 192 features, K = 768 in slices of 128 bytes per
+// row (64 bf16 or 128 E4M3 elements) staged in LDS by buffer_load ... lds
+// DMA (two stages), 8 waves as 4 (rows) x 2 (features) of 64 x 96; weights
+// are the MFMA A operand, tokens B (lane = token), as in gemm.hpp.  E4M3
+// weight rows carry an E8M0 exponent that the matrix core applies as A's
+// scale; Q, K and V are stored as bf16 either way.  Rows of the tile past the group belong to the
 // next group (or past M, where the range check reads zeros): their results
 // are never used.
 //
@@ -23,8 +25,12 @@
 // V^T; wave w owns queries 32w .. 32w+31 of the tile, one per lane, as in
 // attention.hpp (S^T = K Q^T, online softmax per lane with the partner
 // half-wave, O^T = V^T P^T); a lane's keys are those of its own sequence,
-// so key blocks outside it are masked per lane.
+// so key blocks outside it are masked per lane.  With E4M3 operands the
+// context is written as E4M3 codes (its one consumer is the output
+// projection's matrix product).
 #pragma once
+
+#include <type_traits>
 
 #include "attend.hpp"
 #include "common.hpp"
@@ -33,10 +39,11 @@
 namespace albert {
 
 struct QkvAttnArgs {
-  const bf16* X;        // [M, 768] layer input (row stride 768)
-  const bf16* Wh;       // [12][192][768]: per head q/8 | k | v weight rows
+  const void* X;        // [M, 768] layer input (row stride 768), bf16 or E4M3 codes
+  const void* Wh;       // [12][192][768]: per head q/8 | k | v weight rows, bf16 or E4M3 codes
+  const unsigned char* Eh;  // E4M3: [12][192] E8M0 exponents of those rows
   const float* bh;      // [12][192]: their biases
-  bf16* ctx;            // [M, 768] attention context
+  void* ctx;            // [M, 768] attention context, bf16 or E4M3 codes
   const int* cu;        // [n_seq + 1] packed row offsets
   const int* row_seq;   // [M] sequence of each row
   const int* status;
@@ -45,20 +52,27 @@ struct QkvAttnArgs {
   int n_pairs;          // groups * 12
 };
 
+template <bool F8>
 __global__ void __launch_bounds__(512)
 qkv_attention_kernel(QkvAttnArgs a) {
-  typedef Tr<bf16> TR;
+  typedef typename std::conditional<F8, fp8, bf16>::type TO;  // operand codes
+  typedef Tr<TO> TRO;                                         // operand fragments
+  typedef Tr<bf16> TR;                                        // attention
+  constexpr int ES = sizeof(TO);
   constexpr int H = 768, D = 64, NH = 12, BM = 256, BN = 3 * D;
   constexpr int WGN = 2, NW = 8, NT = NW * 64;
   constexpr int WTM = 64, WTN = 96, TM = 2, TN = 3;
-  constexpr int RB = 128, CPR = RB / 16, BK = RB / 2, RPI = 1024 / RB;
+  constexpr int RB = 128, CPR = RB / 16, BK = RB / ES, RPI = 1024 / RB;
+  constexpr int KS = F8 ? 64 : 16;         // K per MFMA step
+  constexpr int FE = F8 ? 32 : 8;          // elements per lane per step
+  constexpr int CH = 16 / ES, FCH = FE / CH;  // chunks per fragment
   constexpr int NINST = (BM + BN) / RPI, IPW = NINST / NW;
   constexpr int STAGE = (BM + BN) * RB;
-  constexpr int KSTEPS = BK / 16, KT = H / BK;
+  constexpr int KSTEPS = BK / KS, KT = H / BK;
   constexpr int LDQ = D + 8;       // Q and K rows (144 bytes)
   constexpr int LDV = BM + 8;      // V^T rows (528 bytes)
   static_assert(NINST % NW == 0 && (BM / RPI) % NW == 0 && NW % 2 == 0, "DMA split");
-  static_assert(KT % 2 == 0, "two stages");
+  static_assert(KT % 2 == 0 && KSTEPS >= 1, "two stages of whole MFMA steps");
   static_assert(BM * LDQ * 2 + 32 * LDV * 2 <= STAGE, "attention buffers fit a stage");
   __shared__ __attribute__((aligned(1024))) char lds0[STAGE];
   __shared__ __attribute__((aligned(1024))) char lds1[STAGE];
@@ -84,20 +98,20 @@ qkv_attention_kernel(QkvAttnArgs a) {
   if (tid < BN) bias_s[tid] = a.bh[h * BN + tid];
 
   // ---------------------------------------------------------- GEMM phase
-  const char* Xt = reinterpret_cast<const char*>(a.X) + (int64_t)r0 * H * 2;
-  const char* Wt = reinterpret_cast<const char*>(a.Wh) + (int64_t)h * BN * H * 2;
-  const int64_t xbytes = (int64_t)(M - r0) * H * 2;
+  const char* Xt = static_cast<const char*>(a.X) + (int64_t)r0 * H * ES;
+  const char* Wt = static_cast<const char*>(a.Wh) + (int64_t)h * BN * H * ES;
+  const int64_t xbytes = (int64_t)(M - r0) * H * ES;
   const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<char*>(Xt), (short)0,
       __builtin_amdgcn_readfirstlane((int)(xbytes > 0x7fffffff ? 0x7fffffff : xbytes)),
       kRsrcWord3);
   const __amdgpu_buffer_rsrc_t wr =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(Wt), (short)0, BN * H * 2, kRsrcWord3);
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(Wt), (short)0, BN * H * ES, kRsrcWord3);
   const int lrow = lane / CPR;
   const int lchunk = (lane % CPR) ^ swz_key<RB>(wave * RPI + lrow);
-  const int loff = lrow * H * 2 + lchunk * 16;
+  const int loff = lrow * H * ES + lchunk * 16;
   auto issue = [&](char* buf, int k0) __attribute__((always_inline)) {
-    int kb = k0 * 2;
+    int kb = k0 * ES;
     asm volatile("" : "+s"(kb));
 #pragma unroll
     for (int i = 0; i < IPW; ++i) {
@@ -105,18 +119,23 @@ qkv_attention_kernel(QkvAttnArgs a) {
       char* dst = buf + q * RPI * RB;
       if (i * NW * RPI < BM)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_ptr_t*)dst, 16, loff,
-                                                 kb + q * RPI * H * 2, 0, 0);
+                                                 kb + q * RPI * H * ES, 0, 0);
       else
         __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (lds_ptr_t*)dst, 16, loff,
-                                                 kb + (q * RPI - BM) * H * 2, 0, 0);
+                                                 kb + (q * RPI - BM) * H * ES, 0, 0);
     }
   };
   const int key = swz_key<RB>(l32);
   const int xrow = (wm * WTM + l32) * RB;
   const int wrow = (BM + wn * WTN + l32) * RB;
-  int coff[KSTEPS];
+  int coff[KSTEPS][FCH];
 #pragma unroll
-  for (int j = 0; j < KSTEPS; ++j) coff[j] = (((j * 16 + hh * 8) / 8) ^ key) * 16;
+  for (int j = 0; j < KSTEPS; ++j)
+#pragma unroll
+    for (int f = 0; f < FCH; ++f) coff[j][f] = (((j * KS + hh * FE) / CH + f) ^ key) * 16;
+  int sc[TN];  // E4M3: E8M0 exponents of this lane's weight rows
+#pragma unroll
+  for (int jj = 0; jj < TN; ++jj) sc[jj] = F8 ? a.Eh[h * BN + wn * WTN + jj * 32 + l32] : 127;
 
   f32x16 acc[TM][TN];
 #pragma unroll
@@ -128,18 +147,27 @@ qkv_attention_kernel(QkvAttnArgs a) {
   auto compute = [&](const char* buf) __attribute__((always_inline)) {
 #pragma unroll
     for (int j = 0; j < KSTEPS; ++j) {
-      bf16x8 fx[TM], fw[TN];
+      typename TRO::frag fx[TM], fw[TN];
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
-        fx[i] = TR::load(reinterpret_cast<const bf16*>(buf + xrow + i * 32 * RB + coff[j]));
+      for (int i = 0; i < TM; ++i) {
+        const char* p = buf + xrow + i * 32 * RB;
+        fx[i] = TRO::load2(reinterpret_cast<const TO*>(p + coff[j][0]),
+                           reinterpret_cast<const TO*>(p + coff[j][FCH - 1]));
+      }
 #pragma unroll
-      for (int jj = 0; jj < TN; ++jj)
-        fw[jj] = TR::load(reinterpret_cast<const bf16*>(buf + wrow + jj * 32 * RB + coff[j]));
+      for (int jj = 0; jj < TN; ++jj) {
+        const char* p = buf + wrow + jj * 32 * RB;
+        fw[jj] = TRO::load2(reinterpret_cast<const TO*>(p + coff[j][0]),
+                            reinterpret_cast<const TO*>(p + coff[j][FCH - 1]));
+      }
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int jj = 0; jj < TN; ++jj) {
-          TR::mma(acc[i][jj], fw[jj], fx[i]);
+          if constexpr (F8)
+            TRO::mma_s(acc[i][jj], fw[jj], fx[i], sc[jj]);
+          else
+            TRO::mma(acc[i][jj], fw[jj], fx[i]);
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
           __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
@@ -147,6 +175,9 @@ qkv_attention_kernel(QkvAttnArgs a) {
   };
 #define ALBERT_QA_WAIT_BARRIER() asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory")
   issue(lds0, 0);
+  // kept as a loop: unrolled (six E4M3 slices), loads hoisted across
+  // iterations spill
+#pragma unroll 1
   for (int kt = 0; kt < KT; kt += 2) {
     ALBERT_QA_WAIT_BARRIER();
     issue(lds1, (kt + 1) * BK);
@@ -227,14 +258,14 @@ qkv_attention_kernel(QkvAttnArgs a) {
   lrun += wave_xor(lrun, 32);
   if (qr < nrows) {
     const float inv = 1.0f / lrun;
-    bf16* out = a.ctx + ((int64_t)r0 + qr) * H + h * D;
+    const int64_t orow = ((int64_t)r0 + qr) * H + h * D;
 #pragma unroll
     for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int d = dt * 32 + 8 * q + 4 * hh;
-        TR::store4(out + d, o[dt][4 * q + 0] * inv, o[dt][4 * q + 1] * inv,
-                   o[dt][4 * q + 2] * inv, o[dt][4 * q + 3] * inv);
+        store4_as<bf16, F8>(a.ctx, orow + d, o[dt][4 * q + 0] * inv, o[dt][4 * q + 1] * inv,
+                            o[dt][4 * q + 2] * inv, o[dt][4 * q + 3] * inv);
       }
   }
 }
