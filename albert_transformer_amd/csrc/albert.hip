@@ -158,7 +158,7 @@ __global__ void clear_u64_kernel(unsigned long long* __restrict__ p, int64_t n) 
 }
 
 struct Layout {
-  size_t status, cu, row_seq, row_pos, emb, x, x1, x8, x18, qkv, ctx, g, xch, total;
+  size_t status, cu, groups, row_seq, row_pos, emb, x, x1, x8, x18, qkv, ctx, g, xch, total;
   int64_t rows_cap;
 };
 
@@ -188,6 +188,9 @@ Layout plan(const albert_ctx* c, int n_seq, int64_t max_rows) {
   L.g = off; off += align_up((size_t)rows * c->cfg.ffn * eo, kAlign);
   // row statistics swapped by the paired LayerNorm GEMMs (bf16)
   L.xch = off; off += c->dtype != ALBERT_F32 ? align_up(ln_pair_words(rows) * 8, kAlign) : 0;
+  // the fused kernel's sequence groups (last: the activations keep the
+  // offsets they have without it)
+  L.groups = off; off += align_up((size_t)(n_seq + 2) * 4, kAlign);
   L.total = off;
   return L;
 }
@@ -239,12 +242,20 @@ int run(albert_ctx* c, const int32_t* ids, const int32_t* lens_or_cu, int n_seq,
   const int H = cf.hidden, F = cf.ffn;
   const int* m_ptr = cu + n_seq;
 
+  // Q|K|V and attention in one kernel when every sequence fits a 256-row
+  // tile: groups of consecutive whole sequences, packed greedily on the
+  // device (up to kGreedyMaxSeqs sequences), else S = 256 / longest per
+  // group, chosen on the host; the separate kernels otherwise.
+  constexpr bool can_fuse = std::is_same<T, bf16>::value;
+  const bool fuse = can_fuse && max_len <= 256 && !(flags & ALBERT_UNFUSED);
+  const bool greedy = fuse && n_seq <= kGreedyMaxSeqs;
+  int* groups = greedy ? reinterpret_cast<int*>(w + L.groups) : nullptr;
   if (pad_T)
     hipLaunchKernelGGL(derive_padded_kernel, dim3(1), dim3(1024), 0, s, lens_or_cu, n_seq, pad_T,
-                       cu, status);
+                       cu, status, groups);
   else
     hipLaunchKernelGGL(derive_packed_kernel, dim3(1), dim3(1024), 0, s, lens_or_cu, n_seq,
-                       (int)max_rows, max_len, cu, status);
+                       (int)max_rows, max_len, cu, status, groups);
   if (feats) {
     // row -> sequence map for the attention's packed query blocks
     hipLaunchKernelGGL(rows_ids_kernel, dim3(n_seq), dim3(256), 0, s, nullptr, cu, 0, cf.vocab,
@@ -306,21 +317,20 @@ int run(albert_ctx* c, const int32_t* ids, const int32_t* lens_or_cu, int n_seq,
     }
   };
 
-  // Q|K|V and attention in one kernel when every sequence fits its 256-row
-  // tile (groups of S whole sequences); the unfused pair otherwise.
-  constexpr bool can_fuse = std::is_same<T, bf16>::value;
-  const bool fuse = can_fuse && max_len <= 256 && !(flags & ALBERT_UNFUSED);
-  const int S = 256 / std::max(max_len, 1);
+  // Any S consecutive sequences fit 256 rows, so greedy groups take at
+  // least S sequences each (the last one aside): there are never more of
+  // them than S-groups, whose count sizes the grid.
+  const int S = fuse ? 256 / max_len : 0;  // >= 1 when fused
   const int64_t pairs = fuse ? (int64_t)((n_seq + S - 1) / S) * cf.heads : 0;
   for (int it = 0; it < cf.n_iter; ++it) {
     const LayerW& lw = c->layers[(size_t)((int64_t)it * cf.n_groups / cf.n_iter)];
     if (fuse) {
-      QkvAttnArgs qa{X8, lw.qkv_wh, lw.qkv_eh, lw.qkv_bh, CTX, cu, row_seq, status, n_seq, S,
-                     (int)pairs};
+      QkvAttnArgs qa{X8, lw.qkv_wh, lw.qkv_eh, lw.qkv_bh, CTX, cu, row_seq, status, groups, n_seq,
+                     S, (int)pairs};
       timed(c, ALBERT_K_QKV_ATTN, s, [&] {
         if constexpr (can_fuse)
-          launch_kernel(qkv_attention_kernel<F8>, dim3((unsigned)((pairs + 7) / 8 * 8)), dim3(512),
-                        s, qa);
+          launch_kernel(qkv_attention_kernel<F8>, dim3((unsigned)((pairs + 7) / 8 * 8)),
+                        dim3(512), s, qa);
       });
     } else {
       g = base;  // fused Q|K|V projection

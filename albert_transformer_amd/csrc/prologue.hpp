@@ -34,11 +34,65 @@ __device__ __forceinline__ int block_incl_scan_1024(int v, int* sh) {
   return r;
 }
 
+// Greedy grouping of consecutive sequences for the fused Q|K|V + attention
+// kernel: each group takes sequences in order while their rows fit 256.
+// groups[0] = number of groups g, groups[1 + i] = first row of group i
+// (the row offset of its first sequence), groups[1 + g] = the rows in all.  Called by the whole block after this block has
+// written cu[0..n]; `bad` is the block's rejection flag in LDS.  Every
+// sequence has at most 256 rows (checked on the host), n <=
+// kGreedyMaxSeqs.  The offsets go to LDS, each thread finds by binary
+// search where a group starting at its sequences must end (nxt) and where
+// the group after it ends (nxt2), and one thread walks that chain from
+// sequence 0 two groups per dependent LDS load.  cu is written by this same block, so
+// it must not be declared __restrict__ (nor the caller's copy be read
+// through one): the compiler could then move its loads above the barrier.
+constexpr int kGreedyMaxSeqs = 8192;
+__device__ void greedy_groups(const int* cu, int n, int* groups, const int* bad) {
+  __shared__ int scu[kGreedyMaxSeqs + 1];
+  __shared__ short nxt[kGreedyMaxSeqs + 1];
+  __shared__ short nxt2[kGreedyMaxSeqs];
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's cu[] stores are done
+  __syncthreads();                     // every wave's cu[] and the flag are written
+  if (*bad) {
+    if (threadIdx.x == 0) groups[0] = 0;
+    return;
+  }
+  for (int i = threadIdx.x; i <= n; i += blockDim.x) scu[i] = cu[i];
+  __syncthreads();
+  for (int s = threadIdx.x; s < n; s += blockDim.x) {
+    // largest t in (s, n] with scu[t] - scu[s] <= 256
+    int lo = s + 1, hi = n;
+    const int lim = scu[s] + 256;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (scu[mid] <= lim) lo = mid;
+      else hi = mid - 1;
+    }
+    nxt[s] = (short)lo;
+  }
+  if (threadIdx.x == 0) nxt[n] = (short)n;
+  __syncthreads();
+  for (int s = threadIdx.x; s < n; s += blockDim.x) nxt2[s] = nxt[nxt[s]];
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int g = 0, s = 0;
+    while (s < n) {
+      const int t = nxt[s], u = nxt2[s];  // independent loads
+      groups[1 + g++] = scu[s];
+      if (t < n) groups[1 + g++] = scu[t];
+      s = u;
+    }
+    groups[1 + g] = scu[n];
+    groups[0] = g;
+  }
+}
+
 // Padded batch: check every length in [1, T], write cu[0..B] (prefix sums)
-// and the status word.  One block of 1024 threads.
+// and the status word (and, with groups, the greedy groups).  One block of
+// 1024 threads.
 static __global__ void __launch_bounds__(1024)
-derive_padded_kernel(const int* __restrict__ lengths, int B, int T, int* __restrict__ cu,
-                     int* __restrict__ status) {
+derive_padded_kernel(const int* __restrict__ lengths, int B, int T, int* cu,
+                     int* __restrict__ status, int* __restrict__ groups) {
   __shared__ int sh[1024];
   __shared__ int bad;
   if (threadIdx.x == 0) bad = 0;
@@ -63,13 +117,15 @@ derive_padded_kernel(const int* __restrict__ lengths, int B, int T, int* __restr
     cu[0] = 0;
     *status = bad ? ST_LENGTH : ST_OK;
   }
+  if (groups) greedy_groups(cu, B, groups, &bad);
 }
 
 // Packed batch: cu_in[0] = 0, cu_in[n] = total, every length in
-// [1, max_len]; copy the offsets into the workspace.  One block.
+// [1, max_len]; copy the offsets into the workspace (and, with groups, the
+// greedy groups).  One block.
 static __global__ void __launch_bounds__(1024)
 derive_packed_kernel(const int* __restrict__ cu_in, int n, int total, int max_len,
-                     int* __restrict__ cu, int* __restrict__ status) {
+                     int* cu, int* __restrict__ status, int* __restrict__ groups) {
   __shared__ int bad;
   if (threadIdx.x == 0) bad = (cu_in[0] != 0 || cu_in[n] != total) ? 1 : 0;
   __syncthreads();
@@ -80,6 +136,7 @@ derive_packed_kernel(const int* __restrict__ cu_in, int n, int total, int max_le
   for (int i = threadIdx.x; i <= n; i += 1024) cu[i] = cu_in[i];
   __syncthreads();
   if (threadIdx.x == 0) *status = bad ? ST_LENGTH : ST_OK;
+  if (groups) greedy_groups(cu, n, groups, &bad);
 }
 
 // One block per sequence: write each valid row's sequence index and

@@ -5,8 +5,9 @@
 // and the masked-softmax attention (step 4; "How Kokoro TTS Works and Where
 // CKE Stands", "What ALBERT does here") computed in one workgroup, so q, k
 // and v of the group never leave the chip: the workgroup owns head h and a
-// group of S whole sequences of at most 256 rows in all (S = 256 / longest
-// length, chosen on the host), computes the 192 projected features of head
+// group of consecutive whole sequences of at most 256 rows in all (packed
+// greedily on the device, or S = 256 / longest per group, chosen on the
+// host, for very large batches), computes the 192 projected features of head
 // h (q/8 | k | v, the query scale folded into the weights) for those rows on
 // the matrix cores, stores them in LDS as bf16 (the same storage point as
 // the unfused path) and runs the attention of every query against the keys
@@ -47,9 +48,10 @@ struct QkvAttnArgs {
   const int* cu;        // [n_seq + 1] packed row offsets
   const int* row_seq;   // [M] sequence of each row
   const int* status;
+  const int* groups;    // greedy groups (count, first rows, rows in all), or null:
   int n_seq;
-  int S;                // sequences per group
-  int n_pairs;          // groups * 12
+  int S;                //   then groups of S consecutive sequences
+  int n_pairs;          // groups (an upper bound with greedy groups) * 12
 };
 
 template <bool F8>
@@ -79,195 +81,216 @@ qkv_attention_kernel(QkvAttnArgs a) {
   __shared__ float bias_s[BN];
 
   if (*a.status != 0) return;
-  // (group, head) pairs: consecutive pairs -- the 12 heads of a group --
-  // go to one XCD (workgroups are dealt to the 8 XCDs round-robin), so the
-  // group's rows of X are read from that XCD's L2 after the first head.
-  const int G = gridDim.x;
-  const int pair = (blockIdx.x % 8) * (G / 8) + blockIdx.x / 8;
-  if (pair >= a.n_pairs) return;
-  const int grp = pair / NH, h = pair % NH;
-  const int s0 = grp * a.S, s1 = min(s0 + a.S, a.n_seq);
-  const int r0 = a.cu[s0], nrows = a.cu[s1] - r0;  // <= 256 by the choice of S
-  const int M = a.cu[a.n_seq];
-
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WGN, wn = wave % WGN;
   const int l32 = lane & 31, hh = lane >> 5;
+  const int M = a.cu[a.n_seq];
 
-  if (tid < BN) bias_s[tid] = a.bh[h * BN + tid];
-
-  // ---------------------------------------------------------- GEMM phase
-  const char* Xt = static_cast<const char*>(a.X) + (int64_t)r0 * H * ES;
-  const char* Wt = static_cast<const char*>(a.Wh) + (int64_t)h * BN * H * ES;
-  const int64_t xbytes = (int64_t)(M - r0) * H * ES;
-  const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<char*>(Xt), (short)0,
-      __builtin_amdgcn_readfirstlane((int)(xbytes > 0x7fffffff ? 0x7fffffff : xbytes)),
-      kRsrcWord3);
-  const __amdgpu_buffer_rsrc_t wr =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(Wt), (short)0, BN * H * ES, kRsrcWord3);
-  const int lrow = lane / CPR;
-  const int lchunk = (lane % CPR) ^ swz_key<RB>(wave * RPI + lrow);
-  const int loff = lrow * H * ES + lchunk * 16;
-  auto issue = [&](char* buf, int k0) __attribute__((always_inline)) {
-    int kb = k0 * ES;
-    asm volatile("" : "+s"(kb));
-#pragma unroll
-    for (int i = 0; i < IPW; ++i) {
-      const int q = wave + i * NW;
-      char* dst = buf + q * RPI * RB;
-      if (i * NW * RPI < BM)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_ptr_t*)dst, 16, loff,
-                                                 kb + q * RPI * H * ES, 0, 0);
-      else
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (lds_ptr_t*)dst, 16, loff,
-                                                 kb + (q * RPI - BM) * H * ES, 0, 0);
+  // One (group, head) pair: the GEMM phase, then the attention phase.
+  auto one = [&](int grp, int h) __attribute__((always_inline)) {
+    int r0, r1;  // the group's rows
+    if (a.groups) {
+      r0 = a.groups[1 + grp];
+      r1 = a.groups[2 + grp];
+    } else {
+      const int s0 = grp * a.S;
+      r0 = a.cu[s0];
+      r1 = a.cu[min(s0 + a.S, a.n_seq)];
     }
-  };
-  const int key = swz_key<RB>(l32);
-  const int xrow = (wm * WTM + l32) * RB;
-  const int wrow = (BM + wn * WTN + l32) * RB;
-  int coff[KSTEPS][FCH];
-#pragma unroll
-  for (int j = 0; j < KSTEPS; ++j)
-#pragma unroll
-    for (int f = 0; f < FCH; ++f) coff[j][f] = (((j * KS + hh * FE) / CH + f) ^ key) * 16;
-  int sc[TN];  // E4M3: E8M0 exponents of this lane's weight rows
-#pragma unroll
-  for (int jj = 0; jj < TN; ++jj) sc[jj] = F8 ? a.Eh[h * BN + wn * WTN + jj * 32 + l32] : 127;
+    const int nrows = r1 - r0;                        // <= 256 by the grouping
+    if (r0 < 0 || r1 > M || nrows <= 0 || nrows > BM) return;  // never, with well-formed groups
 
-  f32x16 acc[TM][TN];
+    if (tid < BN) bias_s[tid] = a.bh[h * BN + tid];
+
+    // ---------------------------------------------------------- GEMM phase
+    const char* Xt = static_cast<const char*>(a.X) + (int64_t)r0 * H * ES;
+    const char* Wt = static_cast<const char*>(a.Wh) + (int64_t)h * BN * H * ES;
+    const int64_t xbytes = (int64_t)(M - r0) * H * ES;
+    const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char*>(Xt), (short)0,
+        __builtin_amdgcn_readfirstlane((int)(xbytes > 0x7fffffff ? 0x7fffffff : xbytes)),
+        kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t wr =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(Wt), (short)0, BN * H * ES, kRsrcWord3);
+    const int lrow = lane / CPR;
+    const int lchunk = (lane % CPR) ^ swz_key<RB>(wave * RPI + lrow);
+    const int loff = lrow * H * ES + lchunk * 16;
+    auto issue = [&](char* buf, int k0) __attribute__((always_inline)) {
+      int kb = k0 * ES;
+      asm volatile("" : "+s"(kb));
 #pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-  auto compute = [&](const char* buf) __attribute__((always_inline)) {
-#pragma unroll
-    for (int j = 0; j < KSTEPS; ++j) {
-      typename TRO::frag fx[TM], fw[TN];
-#pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        const char* p = buf + xrow + i * 32 * RB;
-        fx[i] = TRO::load2(reinterpret_cast<const TO*>(p + coff[j][0]),
-                           reinterpret_cast<const TO*>(p + coff[j][FCH - 1]));
+      for (int i = 0; i < IPW; ++i) {
+        const int q = wave + i * NW;
+        char* dst = buf + q * RPI * RB;
+        if (i * NW * RPI < BM)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_ptr_t*)dst, 16, loff,
+                                                   kb + q * RPI * H * ES, 0, 0);
+        else
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (lds_ptr_t*)dst, 16, loff,
+                                                   kb + (q * RPI - BM) * H * ES, 0, 0);
       }
+    };
+    const int key = swz_key<RB>(l32);
+    const int xrow = (wm * WTM + l32) * RB;
+    const int wrow = (BM + wn * WTN + l32) * RB;
+    int coff[KSTEPS][FCH];
 #pragma unroll
-      for (int jj = 0; jj < TN; ++jj) {
-        const char* p = buf + wrow + jj * 32 * RB;
-        fw[jj] = TRO::load2(reinterpret_cast<const TO*>(p + coff[j][0]),
-                            reinterpret_cast<const TO*>(p + coff[j][FCH - 1]));
-      }
+    for (int j = 0; j < KSTEPS; ++j)
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
+      for (int f = 0; f < FCH; ++f) coff[j][f] = (((j * KS + hh * FE) / CH + f) ^ key) * 16;
+    int sc[TN];  // E4M3: E8M0 exponents of this lane's weight rows
+#pragma unroll
+    for (int jj = 0; jj < TN; ++jj) sc[jj] = F8 ? a.Eh[h * BN + wn * WTN + jj * 32 + l32] : 127;
+
+    f32x16 acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+    auto compute = [&](const char* buf) __attribute__((always_inline)) {
+#pragma unroll
+      for (int j = 0; j < KSTEPS; ++j) {
+        typename TRO::frag fx[TM], fw[TN];
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+          const char* p = buf + xrow + i * 32 * RB;
+          fx[i] = TRO::load2(reinterpret_cast<const TO*>(p + coff[j][0]),
+                             reinterpret_cast<const TO*>(p + coff[j][FCH - 1]));
+        }
 #pragma unroll
         for (int jj = 0; jj < TN; ++jj) {
-          if constexpr (F8)
-            TRO::mma_s(acc[i][jj], fw[jj], fx[i], sc[jj]);
-          else
-            TRO::mma(acc[i][jj], fw[jj], fx[i]);
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          const char* p = buf + wrow + jj * 32 * RB;
+          fw[jj] = TRO::load2(reinterpret_cast<const TO*>(p + coff[j][0]),
+                              reinterpret_cast<const TO*>(p + coff[j][FCH - 1]));
+        }
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int jj = 0; jj < TN; ++jj) {
+            if constexpr (F8)
+              TRO::mma_s(acc[i][jj], fw[jj], fx[i], sc[jj]);
+            else
+              TRO::mma(acc[i][jj], fw[jj], fx[i]);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          }
+      }
+    };
+  #define ALBERT_QA_WAIT_BARRIER() asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory")
+    issue(lds0, 0);
+    // kept as a loop: unrolled (six E4M3 slices), loads hoisted across
+    // iterations spill
+  #pragma unroll 1
+    for (int kt = 0; kt < KT; kt += 2) {
+      ALBERT_QA_WAIT_BARRIER();
+      issue(lds1, (kt + 1) * BK);
+      compute(lds0);
+      ALBERT_QA_WAIT_BARRIER();
+      if (kt + 2 < KT) issue(lds0, (kt + 2) * BK);
+      compute(lds1);
+    }
+  #undef ALBERT_QA_WAIT_BARRIER
+    __syncthreads();  // every wave is done with the stage buffers
+
+    // Q and K rows [token][dim] at the start of lds0 / lds1, V^T [dim][token]
+    // after them, dims 0..31 in lds0 and 32..63 in lds1.
+    bf16* Qs = reinterpret_cast<bf16*>(lds0);
+    bf16* Ks = reinterpret_cast<bf16*>(lds1);
+    bf16* Vt0 = reinterpret_cast<bf16*>(lds0 + BM * LDQ * 2);
+    bf16* Vt1 = reinterpret_cast<bf16*>(lds1 + BM * LDQ * 2);
+    // acc[i][j][4q+e]: token wm*64 + 32i + l32, feature wn*96 + 32j + 8q + 4hh + e
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int tok = wm * WTM + i * 32 + l32;
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int f0 = wn * WTN + j * 32 + 8 * q + 4 * hh;  // 4 consecutive features
+          float o[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[e] = acc[i][j][4 * q + e] + bias_s[f0 + e];
+          if (f0 < D) {
+            TR::store4(Qs + tok * LDQ + f0, o[0], o[1], o[2], o[3]);
+          } else if (f0 < 2 * D) {
+            TR::store4(Ks + tok * LDQ + (f0 - D), o[0], o[1], o[2], o[3]);
+          } else {
+            const int d0 = f0 - 2 * D;
+            bf16* vt = d0 < 32 ? Vt0 + d0 * LDV : Vt1 + (d0 - 32) * LDV;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) vt[e * LDV + tok] = (bf16)o[e];
+          }
+        }
+    }
+    __syncthreads();
+
+    // ----------------------------------------------------- attention phase
+    const int qr = wave * 32 + l32;  // this lane's query (tile row)
+    int ks = 0, ke = 0;              // its keys: tile rows [ks, ke)
+    if (qr < nrows) {
+      const int s = a.row_seq[r0 + qr];
+      ks = a.cu[s] - r0;
+      ke = a.cu[s + 1] - r0;
+    }
+    int kmin = qr < nrows ? ks : BM, kmax = ke;
+#pragma unroll
+    for (int off = 16; off >= 1; off >>= 1) {
+      kmin = min(kmin, __shfl_xor(kmin, off, 64));
+      kmax = max(kmax, __shfl_xor(kmax, off, 64));
+    }
+    const int kb0 = kmin / 32 * 32;  // wave-uniform key-block range
+    const int kb1 = (kmax + 31) / 32 * 32;
+
+    bf16x8 fq[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) fq[kk] = TR::load(Qs + qr * LDQ + kk * 16 + hh * 8);
+    f32x16 o[2];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) { o[0][r] = 0.f; o[1][r] = 0.f; }
+    float mrun = kNegInf, lrun = 0.f;
+    // passes of up to 128 keys from the wave's first key block (for a wave
+    // whose queries share one sequence, its start, as in the separate kernel)
+    for (int kc = kb0; kc < kb1; kc += 128) {
+      attend_pass<bf16>(o, mrun, lrun, fq, min(4, (kb1 - kc) / 32), ks - kc, ke - kc, hh,
+                        [&](int b, int kk) { return TR::load(Ks + (kc + b * 32 + l32) * LDQ + hh * 8 + kk * 16); },
+                        [&](int b, int c, int dt) {
+                          const bf16* vp = (dt == 0 ? Vt0 : Vt1) + l32 * LDV + kc + b * 32 + 16 * c + 4 * hh;
+                          return TR::load2x4(vp, vp + 8);
+                        });
+    }
+    lrun += wave_xor(lrun, 32);
+    if (qr < nrows) {
+      const float inv = 1.0f / lrun;
+      const int64_t orow = ((int64_t)r0 + qr) * H + h * D;
+#pragma unroll
+      for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int d = dt * 32 + 8 * q + 4 * hh;
+          store4_as<bf16, F8>(a.ctx, orow + d, o[dt][4 * q + 0] * inv, o[dt][4 * q + 1] * inv,
+                              o[dt][4 * q + 2] * inv, o[dt][4 * q + 3] * inv);
         }
     }
   };
-#define ALBERT_QA_WAIT_BARRIER() asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory")
-  issue(lds0, 0);
-  // kept as a loop: unrolled (six E4M3 slices), loads hoisted across
-  // iterations spill
-#pragma unroll 1
-  for (int kt = 0; kt < KT; kt += 2) {
-    ALBERT_QA_WAIT_BARRIER();
-    issue(lds1, (kt + 1) * BK);
-    compute(lds0);
-    ALBERT_QA_WAIT_BARRIER();
-    if (kt + 2 < KT) issue(lds0, (kt + 2) * BK);
-    compute(lds1);
-  }
-#undef ALBERT_QA_WAIT_BARRIER
-  __syncthreads();  // every wave is done with the stage buffers
 
-  // Q and K rows [token][dim] at the start of lds0 / lds1, V^T [dim][token]
-  // after them, dims 0..31 in lds0 and 32..63 in lds1.
-  bf16* Qs = reinterpret_cast<bf16*>(lds0);
-  bf16* Ks = reinterpret_cast<bf16*>(lds1);
-  bf16* Vt0 = reinterpret_cast<bf16*>(lds0 + BM * LDQ * 2);
-  bf16* Vt1 = reinterpret_cast<bf16*>(lds1 + BM * LDQ * 2);
-  // acc[i][j][4q+e]: token wm*64 + 32i + l32, feature wn*96 + 32j + 8q + 4hh + e
-#pragma unroll
-  for (int i = 0; i < TM; ++i) {
-    const int tok = wm * WTM + i * 32 + l32;
-#pragma unroll
-    for (int j = 0; j < TN; ++j)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int f0 = wn * WTN + j * 32 + 8 * q + 4 * hh;  // 4 consecutive features
-        float o[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) o[e] = acc[i][j][4 * q + e] + bias_s[f0 + e];
-        if (f0 < D) {
-          TR::store4(Qs + tok * LDQ + f0, o[0], o[1], o[2], o[3]);
-        } else if (f0 < 2 * D) {
-          TR::store4(Ks + tok * LDQ + (f0 - D), o[0], o[1], o[2], o[3]);
-        } else {
-          const int d0 = f0 - 2 * D;
-          bf16* vt = d0 < 32 ? Vt0 + d0 * LDV : Vt1 + (d0 - 32) * LDV;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) vt[e * LDV + tok] = (bf16)o[e];
-        }
-      }
-  }
-  __syncthreads();
-
-  // ----------------------------------------------------- attention phase
-  const int qr = wave * 32 + l32;  // this lane's query (tile row)
-  int ks = 0, ke = 0;              // its keys: tile rows [ks, ke)
-  if (qr < nrows) {
-    const int s = a.row_seq[r0 + qr];
-    ks = a.cu[s] - r0;
-    ke = a.cu[s + 1] - r0;
-  }
-  int kmin = qr < nrows ? ks : BM, kmax = ke;
-#pragma unroll
-  for (int off = 16; off >= 1; off >>= 1) {
-    kmin = min(kmin, __shfl_xor(kmin, off, 64));
-    kmax = max(kmax, __shfl_xor(kmax, off, 64));
-  }
-  const int kb0 = kmin / 32 * 32;  // wave-uniform key-block range
-  const int kb1 = (kmax + 31) / 32 * 32;
-
-  bf16x8 fq[4];
-#pragma unroll
-  for (int kk = 0; kk < 4; ++kk) fq[kk] = TR::load(Qs + qr * LDQ + kk * 16 + hh * 8);
-  f32x16 o[2];
-#pragma unroll
-  for (int r = 0; r < 16; ++r) { o[0][r] = 0.f; o[1][r] = 0.f; }
-  float mrun = kNegInf, lrun = 0.f;
-  // passes of up to 128 keys from the wave's first key block (for a wave
-  // whose queries share one sequence, its start, as in the separate kernel)
-  for (int kc = kb0; kc < kb1; kc += 128) {
-    attend_pass<bf16>(o, mrun, lrun, fq, min(4, (kb1 - kc) / 32), ks - kc, ke - kc, hh,
-                      [&](int b, int kk) { return TR::load(Ks + (kc + b * 32 + l32) * LDQ + hh * 8 + kk * 16); },
-                      [&](int b, int c, int dt) {
-                        const bf16* vp = (dt == 0 ? Vt0 : Vt1) + l32 * LDV + kc + b * 32 + 16 * c + 4 * hh;
-                        return TR::load2x4(vp, vp + 8);
-                      });
-  }
-  lrun += wave_xor(lrun, 32);
-  if (qr < nrows) {
-    const float inv = 1.0f / lrun;
-    const int64_t orow = ((int64_t)r0 + qr) * H + h * D;
-#pragma unroll
-    for (int dt = 0; dt < 2; ++dt)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int d = dt * 32 + 8 * q + 4 * hh;
-        store4_as<bf16, F8>(a.ctx, orow + d, o[dt][4 * q + 0] * inv, o[dt][4 * q + 1] * inv,
-                            o[dt][4 * q + 2] * inv, o[dt][4 * q + 3] * inv);
-      }
-  }
+  // One pair per block.  Workgroups are dealt to the 8 XCDs round-robin,
+  // so block b runs on XCD b % 8 as its (b / 8)-th block there.  The pairs
+  // that exist (with greedy groups their count is known on the device only;
+  // the grid covers the S-grouping count, never fewer) are cut into 8
+  // contiguous ranges, one per XCD, taken by that XCD's first blocks: the
+  // 12 heads of a group share one XCD (or two at a range boundary), so its
+  // rows of X are read from that XCD's L2 after the first head, and every
+  // XCD gets the same number of pairs.  (A persistent loop over pairs made
+  // the compiler hold addresses across it, spilling with E4M3 fragments,
+  // and slowed the next kernels.)
+  const int npairs = a.groups ? min(a.groups[0] * NH, a.n_pairs) : a.n_pairs;
+  const int xcd = (int)blockIdx.x % 8;
+  const int plo = (int)((int64_t)npairs * xcd / 8), phi = (int)((int64_t)npairs * (xcd + 1) / 8);
+  const int pair = plo + (int)blockIdx.x / 8;
+  if (pair < phi) one(pair / NH, pair % NH);
 }
 
 }  // namespace albert

@@ -166,10 +166,10 @@ int text_run(albert_text_ctx* c, const int32_t* ids, const int32_t* lens_or_cu, 
 
   if (pad_T)
     hipLaunchKernelGGL(derive_padded_kernel, dim3(1), dim3(1024), 0, s, lens_or_cu, n_seq, pad_T,
-                       cu, status);
+                       cu, status, (int*)nullptr);
   else
     hipLaunchKernelGGL(derive_packed_kernel, dim3(1), dim3(1024), 0, s, lens_or_cu, n_seq,
-                       (int)max_rows, max_len, cu, status);
+                       (int)max_rows, max_len, cu, status, (int*)nullptr);
   hipLaunchKernelGGL(rows_ids_kernel, dim3(n_seq), dim3(256), 0, s, ids, cu, pad_T, cf.vocab,
                      row_seq, row_pos, status);
   ttimed(c, ALBERT_TK_EMBED, s, [&] {

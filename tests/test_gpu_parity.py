@@ -418,3 +418,32 @@ def test_layernorm_pair_handoff(B, T, seed):
     for s in (0, B - 1):
         L = int(wl.lengths[s])
         check(b[s, :L], oracle.encode_sequence(wl.ids[s, :L], W, K), "bf16", f"handoff seq{s}")
+
+
+@pytest.mark.parametrize("n,lo,hi,seed", [(200, 1, 256, 73), (9000, 1, 3, 74)])
+def test_fused_group_packing(n, lo, hi, seed):
+    """The fused kernel's groups: consecutive sequences packed greedily on
+    the device while their rows fit 256 (n = 200, lengths 1..256, so a
+    group may hold one long sequence or many short ones), or, beyond 8,192
+    sequences, S = 256 / longest per group chosen on the host (n = 9,000
+    of 1..3 tokens).  Sampled sequences against the oracle, and every
+    sequence against the separate kernels' run."""
+    import torch
+    import albert_transformer_amd as A
+    enc = encoder("bf16")
+    W = oracle_weights("bf16")
+    rng = np.random.default_rng(seed)
+    lengths = rng.integers(lo, hi + 1, n).astype(np.int32)
+    lengths[0] = hi
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    ids = rng.integers(0, 178, int(cu[-1])).astype(np.int32)
+    outs = []
+    for flags in (0, A.UNFUSED):
+        out = torch.full((int(cu[-1]), 512), float("nan"), device="cuda")
+        ws = enc.new_workspace(n, int(cu[-1]))
+        assert enc.encode_varlen_raw(dev(ids), dev(cu), hi, out, ws, flags=flags) == 0
+        outs.append(out.cpu().numpy().astype(np.float64))
+    check(outs[0], outs[1], "bf16", f"fused vs separate n={n}")
+    for s in (0, 1, n // 2, n - 1):
+        a, b = int(cu[s]), int(cu[s + 1])
+        check(outs[0][a:b], oracle.encode_sequence(ids[a:b], W, K), "bf16", f"grouped seq{s}")
