@@ -46,8 +46,9 @@ void launch_gemm(GemmArgs g, int64_t max_rows, int grid_cap, hipStream_t s) {
 // bf16 tiles use 8 waves (two per SIMD, so one wave's LDS waits hide
 // behind the other's matrix-core work): the bias GEMMs with at least 12
 // (an even number of) K slices as 2 x 4 waves keeping each tile's outputs
-// in registers to store them during the next tile, the GELU GEMM as 4 x 2
-// waves storing directly (the faster pair on the encoder's shapes).  E4M3
+// in registers to store them during the next tile, the GELU GEMM, the
+// short-K bias GEMM and the fp32 output projections as 4 x 2 waves storing
+// directly (the faster pair on the encoder's shapes).  E4M3
 // operands stage 64-byte rows (one 64-deep MFMA step per slice); their
 // bias/GELU GEMMs run as 4 x 2 waves with deferred stores.
 template <typename T, bool F8, int EPI>
@@ -60,13 +61,15 @@ void gemm_big(GemmArgs g, int64_t max_rows, int grid_cap, hipStream_t s) {
   } else if constexpr (bf && EPI == EPI_BIAS) {
     if (slices >= 12 && slices % 2 == 0 && !g.Y8)
       launch_gemm<T, F8, 256, 256, 2, 4, RB, 2, EPI, true>(g, max_rows, grid_cap, s);
-    else
-      launch_gemm<T, F8, 256, 256, 2, 2, RB, 2, EPI, false>(g, max_rows, grid_cap, s);
+    else  // short K (the input projection): 4 x 2 waves, stored directly
+      launch_gemm<T, F8, 256, 256, 4, 2, RB, 2, EPI, false>(g, max_rows, grid_cap, s);
   } else if constexpr (F8 && (EPI == EPI_BIAS || EPI == EPI_GELU)) {
     if (slices >= 12 && slices % 2 == 0 && !g.Y8)
       launch_gemm<T, F8, 256, 256, 4, 2, RB, 2, EPI, true>(g, max_rows, grid_cap, s);
     else
       launch_gemm<T, F8, 256, 256, 2, 2, RB, 2, EPI, false>(g, max_rows, grid_cap, s);
+  } else if constexpr (bf && EPI == EPI_OUT) {  // output projections: 4 x 2 waves
+    launch_gemm<T, F8, 256, 256, 4, 2, RB, 2, EPI, false>(g, max_rows, grid_cap, s);
   } else {
     launch_gemm<T, F8, 256, 256, 2, 2, RB, 2, EPI, false>(g, max_rows, grid_cap, s);
   }
