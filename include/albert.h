@@ -62,13 +62,13 @@ enum albert_dtype { ALBERT_F32 = 0, ALBERT_BF16 = 1, ALBERT_FP8 = 2 };
 /* flags for albert_encode / albert_encode_varlen */
 #define ALBERT_ASYNC 1u /* return after enqueueing; read the status later
                            with albert_read_status()                        */
-#define ALBERT_UNFUSED 2u /* bf16 only: run Q|K|V and attention as separate
-                             kernels (otherwise fused when every sequence
-                             has at most 256 tokens), so that the QKV tap
-                             holds its checkpoint.  Text path: run the LSTM
+#define ALBERT_UNFUSED 2u /* bf16 and FP8: run Q|K|V and attention as
+                             separate kernels (otherwise fused when every
+                             sequence has at most 256 tokens), so that the
+                             QKV tap holds its checkpoint.  Text path: run the LSTM
                              recurrence as one workgroup per direction and
                              32 sequences instead of four cooperating ones */
-#define ALBERT_LN_HANDOFF 4u /* testing aid, bf16: the two workgroups that
+#define ALBERT_LN_HANDOFF 4u /* testing aid, bf16 and FP8: the two workgroups that
                              share each LayerNorm row tile do not wait for
                              each other's row statistics, so the fallback in
                              which one hands its rows to the other runs
@@ -226,8 +226,8 @@ int albert_read_status(const void* ws, void* hip_stream);
  *   4 EMB  [rows, E]   embedding sum after LayerNorm
  *   5 X    [rows, H]   input projection (n_iter = 0) or last layer output
  *   6 QKV  [rows, 3H]  last execution's q/8 | k | v, head h at h*64 (written
- *                      only by the unfused sequence: ALBERT_UNFUSED, fp32,
- *                      FP8, the features entry or sequences over 256)
+ *                      only by the separate kernels: ALBERT_UNFUSED, fp32,
+ *                      or a sequence over 256 tokens)
  *   7 CTX  [rows, H]   last execution's attention context (token-major)
  *   8 X1   [rows, H]   last execution's post-attention LayerNorm output
  *   9 G    [rows, F]   last execution's GELU output
