@@ -38,7 +38,7 @@ EXPORTS = ("albert_default_config", "albert_n_tensors", "albert_tensor_name",
            "albert_text_encode", "albert_text_encode_varlen", "albert_text_tap",
            "albert_text_time_kernel", "albert_text_kernel_time", "albert_text_free")
 TEXT_TAPS = {"status": 0, "cu": 1, "emb": 2, "conv": 3, "xg": 4}
-TEXT_KERNEL_KINDS = ("embed", "unfold", "conv", "lstm_in", "lstm")
+TEXT_KERNEL_KINDS = ("embed", "taps", "conv", "lstm_in", "lstm")
 KERNEL_KINDS = ("embed", "proj", "qkv", "attn", "attn_out_ln", "ffn1_gelu", "ffn2_ln", "out",
                 "qkv_attn")
 

@@ -13,7 +13,13 @@
 //             Layer"); the block tile spans the whole row so the row
 //             statistics never leave the chip
 //   EPI_LN_ACT  store LeakyReLU(LN(Y) * g + beta), no residual (the text
-//             path's convolution blocks)
+//             path's convolution blocks).  X is then the layer input [M, C]
+//             read as the convolution's unfolded input: K = taps * C, and
+//             column j*C + c of row m is channel c of input row
+//             m + j - taps/2 when that row is in m's sequence (bit j of
+//             taps[m]), else zero.  The DMA reads the shifted rows directly
+//             (an absent tap reads past the buffer's range, which returns
+//             zeros), so no unfolded copy is made.
 //   EPI_LN_PAIR as EPI_LN, with the row split over two blocks of BN = N/2
 //             features that run at the same time: each reduces its half of
 //             every row to a mean and a sum of squared deviations, the two
@@ -73,6 +79,7 @@ struct GemmArgs {
   int64_t ldx;
   const void* W;       // [N, K] weights, row stride K
   const unsigned char* wexp;  // F8: [N] E8M0 exponent of each weight row
+  const unsigned char* taps;  // EPI_LN_ACT: [M] the convolution taps inside each row's sequence
   const float* bias;   // [N]
   void* Y;             // [M, N] output (EPI_BIAS / EPI_GELU / EPI_LN), stride ldy
   int64_t ldy;
@@ -149,6 +156,8 @@ gemm_kernel(GemmArgs g) {
   constexpr bool PAIR = EPI == EPI_LN_PAIR;                // LayerNorm row split over two blocks
   constexpr bool LNE = EPI == EPI_LN || EPI == EPI_LN_ACT || PAIR;  // LayerNorm epilogue
   constexpr bool RES = EPI == EPI_LN || PAIR;              // with a residual
+  constexpr bool CONV = EPI == EPI_LN_ACT;                 // convolution taps from shifted rows
+  constexpr int kMaxTaps = 7;
   constexpr int NVEC = LNE ? 3 : 1;          // bias (+ LayerNorm gain, shift)
   constexpr int VPT = (BN + NT - 1) / NT;     // vector elements per thread
   static_assert(NINST % NW == 0, "DMA split");
@@ -159,6 +168,7 @@ gemm_kernel(GemmArgs g) {
   static_assert(STAGES >= 2 && STAGES <= 4, "stages");
   static_assert(KR >= 0 && KR < STAGES, "K slices past the last whole round");
   static_assert(EPI != EPI_LN_PAIR || 2 * BM <= NT, "one thread per row statistic");
+  static_assert(!CONV || BM / RPI == NW, "convolution: one input row per lane and slice");
   static_assert(IPW * (STAGES - 2) <= 63, "vmcnt range");
   static_assert(CPR == 8 ? (NW % 2 == 0) : true, "swizzle key must not depend on i");
   // Deferred stores: bf16 (or E4M3) outputs of tile i are kept in registers
@@ -205,6 +215,7 @@ gemm_kernel(GemmArgs g) {
 
   // ------------------------------------------------------- per-tile state
   int m0 = 0, n0 = 0;
+  int xb0 = 0;  // CONV: first input row of the X resource (taps/2 above the tile)
   __amdgpu_buffer_rsrc_t xr, wr;
   int sc[TN];  // F8: E8M0 exponents of this lane's weight rows
 #pragma unroll
@@ -214,9 +225,10 @@ gemm_kernel(GemmArgs g) {
   auto setup = [&](int t) __attribute__((always_inline)) {
     m0 = (t / g.n_tiles) * BM;
     n0 = (t % g.n_tiles) * BN;
-    const char* Xt = static_cast<const char*>(g.X) + (int64_t)m0 * g.ldx * (int64_t)ES;
+    xb0 = CONV ? max(m0 - (g.K / (int)g.ldx) / 2, 0) : m0;
+    const char* Xt = static_cast<const char*>(g.X) + (int64_t)xb0 * g.ldx * (int64_t)ES;
     const char* Wt = static_cast<const char*>(g.W) + (int64_t)n0 * g.K * (int64_t)ES;
-    const int64_t xbytes = (int64_t)(M - m0) * g.ldx * (int64_t)ES;
+    const int64_t xbytes = (int64_t)(M - xb0) * g.ldx * (int64_t)ES;
     const int64_t wbytes = (int64_t)(g.N - n0) * g.K * (int64_t)ES;
     const int xrec = __builtin_amdgcn_readfirstlane((int)(xbytes > 0x7fffffff ? 0x7fffffff : xbytes));
     const int wrec = __builtin_amdgcn_readfirstlane((int)(wbytes > 0x7fffffff ? 0x7fffffff : wbytes));
@@ -240,6 +252,19 @@ gemm_kernel(GemmArgs g) {
   const int woff = lrow * g.K * ES + lchunk * 16;
   const int xrow_b = (int)g.ldx * ES;  // bytes per X row
   const int wrow_b = g.K * ES;
+  // CONV: this lane's input-row offset for each tap (its X row is
+  // m0 + wave*RPI + lrow), or one past any buffer range for an absent tap
+  int xo[CONV ? kMaxTaps : 1];
+  auto conv_offsets = [&]() __attribute__((always_inline)) {
+    if constexpr (CONV) {
+      const int half = (g.K / (int)g.ldx) / 2;
+      const int r = m0 + wave * RPI + lrow;
+      const unsigned mask = r < M ? (unsigned)g.taps[r] : 0u;
+#pragma unroll
+      for (int j = 0; j < kMaxTaps; ++j)
+        xo[j] = ((mask >> j) & 1u) ? (r + j - half - xb0) * xrow_b + lchunk * 16 : 0x7FFFFFF0;
+    }
+  };
   auto issue = [&](char* buf, int k0) __attribute__((always_inline)) {
     int kb = k0 * ES;
     // keep the per-slice offset opaque so the compiler does not precompute
@@ -249,10 +274,18 @@ gemm_kernel(GemmArgs g) {
     for (int i = 0; i < IPW; ++i) {
       const int q = wave + i * NW;
       char* dst = buf + q * RPI * RB;
-      if (i * NW * RPI < BM)  // compile-time per i (static_assert above)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_ptr_t*)dst, 16, xoff,
-                                                 kb + q * RPI * xrow_b, 0, 0);
-      else
+      if (i * NW * RPI < BM) {  // compile-time per i (static_assert above)
+        if constexpr (CONV) {  // tap j = k0 / C, channels from k0 - j*C (a slice holds one tap)
+          const int C = (int)g.ldx, j = k0 / C;
+          const int vo = j == 0 ? xo[0] : j == 1 ? xo[1] : j == 2 ? xo[2] : j == 3 ? xo[3]
+                       : j == 4 ? xo[4] : j == 5 ? xo[5] : xo[6];
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_ptr_t*)dst, 16, vo, (k0 - j * C) * ES,
+                                                   0, 0);
+        } else {
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_ptr_t*)dst, 16, xoff,
+                                                   kb + q * RPI * xrow_b, 0, 0);
+        }
+      } else
         __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (lds_ptr_t*)dst, 16, woff,
                                                  kb + (q * RPI - BM) * wrow_b, 0, 0);
     }
@@ -726,6 +759,7 @@ gemm_kernel(GemmArgs g) {
 
   // --------------------------------------------------------- tile loop
   setup(tile);
+  conv_offsets();
   vload(n0);
   vstore(0);
   prologue();
@@ -816,6 +850,7 @@ gemm_kernel(GemmArgs g) {
     const int em0 = m0, en0 = n0;
     if (more) {
       setup(next);
+      conv_offsets();
       vload(n0);
     }
     // every wave has finished reading the staging buffers (their reads fed

@@ -3,7 +3,8 @@
 //
 // Launch sequence of one request (all on the caller's stream):
 //   derive (lengths -> offsets, status) -> rows/IDs check -> embedding ->
-//   n_conv x [unfold -> convolution GEMM + LayerNorm + LeakyReLU] ->
+//   convolution taps of each row -> n_conv x [convolution GEMM (shifted
+//   rows read directly) + LayerNorm + LeakyReLU] ->
 //   LSTM input projection GEMM (both directions, fp32) -> LSTM recurrence
 //   -> zeroing of padded rows.
 #include <hip/hip_runtime.h>
@@ -102,7 +103,7 @@ uint16_t bf16_bits(double v) {
 }
 
 struct TextLayout {
-  size_t status, cu, row_seq, row_pos, emb, x1, x2, col, xg, hx, flags, total;
+  size_t status, cu, row_seq, row_pos, emb, x1, x2, taps, xg, hx, flags, total;
   int mc_groups;  // groups of 32 sequences per launch of the four-workgroup recurrence
 };
 
@@ -118,7 +119,7 @@ TextLayout text_plan(const albert_text_ctx* c, int n_seq, int64_t max_rows) {
   L.emb = off; off += align_up(rows * C * 2, kAlign);
   L.x1 = off; off += align_up(rows * C * 2, kAlign);
   L.x2 = off; off += align_up(rows * C * 2, kAlign);
-  L.col = off; off += align_up(rows * K * C * 2, kAlign);
+  L.taps = off; off += align_up(rows, kAlign);  // the convolution taps of each row
   L.xg = off; off += align_up(rows * 8 * H * 4, kAlign);
   // exchange buffers of the four-workgroup recurrence: per launch up to
   // mc_groups groups x 2 directions, each h_t twice (parity) as bf16
@@ -159,7 +160,7 @@ int text_run(albert_text_ctx* c, const int32_t* ids, const int32_t* lens_or_cu, 
   // embedding rows, then the blocks alternate x1 <- emb, x2 <- x1, x1 <- x2, ...
   bf16* X[3] = {reinterpret_cast<bf16*>(w + L.emb), reinterpret_cast<bf16*>(w + L.x1),
                 reinterpret_cast<bf16*>(w + L.x2)};
-  bf16* col = reinterpret_cast<bf16*>(w + L.col);
+  unsigned char* taps = reinterpret_cast<unsigned char*>(w + L.taps);
   float* XG = reinterpret_cast<float*>(w + L.xg);
   const int C = cf.channels, K = cf.kernel, H = cf.hidden;
   const int* m_ptr = cu + n_seq;
@@ -180,15 +181,15 @@ int text_run(albert_text_ctx* c, const int32_t* ids, const int32_t* lens_or_cu, 
   GemmArgs base{};
   base.status = status;
   base.m_ptr = m_ptr;
+  ttimed(c, ALBERT_TK_TAPS, s, [&] {
+    launch_kernel(conv_taps_kernel, dim3((unsigned)((max_rows + 255) / 256)), dim3(256), s,
+                  row_seq, row_pos, cu, m_ptr, K, taps, status);
+  });
   int cur = 0;
   for (int i = 0; i < cf.n_conv; ++i) {
     const int nxt = cur == 1 ? 2 : 1;
-    ttimed(c, ALBERT_TK_UNFOLD, s, [&] {
-      launch_kernel(unfold_kernel, dim3((unsigned)((max_rows * K * (C / 8) + 255) / 256)),
-                    dim3(256), s, X[cur], row_seq, row_pos, cu, m_ptr, C, K, col, status);
-    });
-    GemmArgs g = base;  // convolution as one GEMM over the unfolded input
-    g.X = col; g.ldx = (int64_t)K * C; g.W = c->conv_w[i]; g.bias = c->conv_b[i];
+    GemmArgs g = base;  // convolution as one GEMM over the (virtually) unfolded input
+    g.X = X[cur]; g.ldx = C; g.taps = taps; g.W = c->conv_w[i]; g.bias = c->conv_b[i];
     g.ln_g = c->ln_g[i]; g.ln_b = c->ln_b[i]; g.eps = cf.ln_eps; g.slope = cf.slope;
     g.Y = X[nxt]; g.ldy = C; g.N = C; g.K = K * C;
     ttimed(c, ALBERT_TK_CONV, s, [&] {

@@ -7,8 +7,10 @@
 // encoder.  A convolution of width K over a sequence is one GEMM over the
 // unfolded input col[m, j*C + c] = x[m + j - K/2, c] (zero where that row
 // is outside m's sequence), so zero padding happens at every sequence's own
-// ends and neighbours in the pack never mix; its LayerNorm and LeakyReLU
-// run in the GEMM's full-row epilogue.  The LSTM input projection (both
+// ends and neighbours in the pack never mix.  The unfolded input is never
+// built: the GEMM's DMA reads the shifted rows of x directly, guided by a
+// per-row mask of the taps inside the row's sequence; its LayerNorm and
+// LeakyReLU run in the GEMM's full-row epilogue.  The LSTM input projection (both
 // directions, both biases) is a second GEMM into fp32 gate pre-activations;
 // the recurrence below then only adds W_hh h_{t-1}.
 #pragma once
@@ -36,26 +38,24 @@ text_embed_kernel(const int* __restrict__ ids, int pad_T, const int* __restrict_
       reinterpret_cast<const uint4*>(emb + (int64_t)id * C)[c];
 }
 
-// Unfolded convolution input: col[m, j*C + c] = x[m + j - K/2, c] when that
-// row belongs to m's sequence, else 0.  16 bytes per thread.
+// The convolution taps of each packed row: bit j of taps[m] is set when
+// input row m + j - K/2 belongs to m's sequence (the convolution GEMM reads
+// that row for tap j, and zeros otherwise: zero padding at each sequence's
+// own ends).  One thread per row.
 __global__ void __launch_bounds__(256)
-unfold_kernel(const bf16* __restrict__ x, const int* __restrict__ row_seq,
-              const int* __restrict__ row_pos, const int* __restrict__ cu,
-              const int* __restrict__ m_ptr, int C, int K, bf16* __restrict__ col,
-              const int* __restrict__ status) {
+conv_taps_kernel(const int* __restrict__ row_seq, const int* __restrict__ row_pos,
+                 const int* __restrict__ cu, const int* __restrict__ m_ptr, int K,
+                 unsigned char* __restrict__ taps, const int* __restrict__ status) {
   if (*status != 0) return;
-  const int cpr = C / 8;
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;  // over M * K * cpr
-  if (i >= (int64_t)(*m_ptr) * K * cpr) return;
-  const int c = (int)(i % cpr);
-  const int64_t mj = i / cpr;
-  const int j = (int)(mj % K), m = (int)(mj / K);
-  const int s = row_seq[m];
-  const int p = row_pos[m] + j - K / 2;
-  uint4 v = make_uint4(0, 0, 0, 0);
-  if (p >= 0 && p < cu[s + 1] - cu[s])
-    v = reinterpret_cast<const uint4*>(x + (int64_t)(cu[s] + p) * C)[c];
-  reinterpret_cast<uint4*>(col + ((int64_t)m * K + j) * C)[c] = v;
+  const int m = blockIdx.x * 256 + threadIdx.x;
+  if (m >= *m_ptr) return;
+  const int s = row_seq[m], p = row_pos[m], L = cu[s + 1] - cu[s];
+  unsigned v = 0;
+  for (int j = 0; j < K; ++j) {
+    const int q = p + j - K / 2;
+    if (q >= 0 && q < L) v |= 1u << j;
+  }
+  taps[m] = (unsigned char)v;
 }
 
 struct LstmArgs {

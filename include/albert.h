@@ -388,7 +388,7 @@ int albert_text_tap(const albert_text_ctx* ctx, int n_seq, int64_t max_rows, int
  * contract as albert_time_kernel). */
 enum albert_text_kernel_kind {
   ALBERT_TK_EMBED = 0,    /* embedding gather                               */
-  ALBERT_TK_UNFOLD = 1,   /* unfolded convolution input, once per block     */
+  ALBERT_TK_TAPS = 1,     /* per-row convolution taps, once per request     */
   ALBERT_TK_CONV = 2,     /* convolution GEMM + LayerNorm + LeakyReLU       */
   ALBERT_TK_LSTM_IN = 3,  /* LSTM input projection, both directions         */
   ALBERT_TK_LSTM = 4,     /* LSTM recurrence, both directions               */
