@@ -33,12 +33,12 @@ inline void launch_kernel(void (*kernel)(KArgs...), dim3 grid, dim3 block, hipSt
 // Persistent launch: one block per CU at most (a multiple of 8, so that the
 // kernel's XCD-aware tile numbering is a bijection), each walking its tiles.
 template <typename T, bool F8, int BM, int BN, int WGM, int WGN, int RB, int STAGES, int EPI,
-          bool DEFER>
+          bool DEFER, int KR = 0>
 void launch_gemm(GemmArgs g, int64_t max_rows, int grid_cap, hipStream_t s) {
   g.n_tiles = g.N / BN;
   const int64_t tiles = (max_rows + BM - 1) / BM * g.n_tiles;
   const int64_t grid = std::min<int64_t>((tiles + 7) / 8 * 8, grid_cap);
-  launch_kernel(gemm_kernel<T, F8, BM, BN, WGM, WGN, RB, STAGES, EPI, DEFER>,
+  launch_kernel(gemm_kernel<T, F8, BM, BN, WGM, WGN, RB, STAGES, EPI, DEFER, KR>,
                 dim3((unsigned)grid), dim3(WGM * WGN * 64), s, g);
 }
 
@@ -80,10 +80,25 @@ void gemm_big(GemmArgs g, int64_t max_rows, int grid_cap, hipStream_t s) {
 // low-precision variant always uses the 4-wave one.)
 // The tile spans the whole row of N (768 for the encoder, 512 for the text
 // path's convolutions).
+// The text path's convolutions (bf16, EPI_LN_ACT, K = 2560) run the
+// 128-row tile three stages deep (32-deep slices, the kernel instantiated
+// per K slices mod 3): 10 % faster than two.
 template <typename T, bool F8, int N, int EPI>
 void gemm_ln_n(GemmArgs g, int64_t max_rows, int grid_cap, hipStream_t s) {
   if constexpr (!F8) {
     if ((max_rows + 127) / 128 >= grid_cap) {
+      if constexpr (EPI == EPI_LN_ACT && std::is_same<T, bf16>::value) {
+        if (g.K % 32 == 0 && g.K / 32 >= 5) {
+          const int kr = (g.K / 32) % 3;
+          if (kr == 0)
+            launch_gemm<T, F8, 128, N, 2, 4, 64, 3, EPI, false, 0>(g, max_rows, grid_cap, s);
+          else if (kr == 1)
+            launch_gemm<T, F8, 128, N, 2, 4, 64, 3, EPI, false, 1>(g, max_rows, grid_cap, s);
+          else
+            launch_gemm<T, F8, 128, N, 2, 4, 64, 3, EPI, false, 2>(g, max_rows, grid_cap, s);
+          return;
+        }
+      }
       launch_gemm<T, F8, 128, N, 2, 4, 64, 2, EPI, false>(g, max_rows, grid_cap, s);
       return;
     }
