@@ -126,14 +126,18 @@ attention_kernel(AttnArgs a) {
       __syncthreads();
 
       // this lane's keys in the chunk: all of it up to the sequence's end,
-      // or none when the lane's query belongs to another sequence
+      // or none when the lane's query belongs to another sequence (a pass
+      // with none leaves the lane's state exactly unchanged, so a wave
+      // whose queries all belong to other sequences skips it)
       const int nkb = (nk + 31) / 32;
-      attend_pass<T>(o, mrun, lrun, fq, nkb, 0, mine ? L - c0 : 0, hh,
-                     [&](int b, int kk) { return TR::load(Ks + (b * 32 + l32) * LDKS + hh * 8 + kk * 16); },
-                     [&](int b, int c, int dt) {
-                       const T* vp = Vt + (dt * 32 + l32) * LDVT + b * 32 + 16 * c + 4 * hh;
-                       return TR::load2x4(vp, vp + 8);
-                     });
+      if (__any(mine)) {
+        attend_pass<T>(o, mrun, lrun, fq, nkb, 0, mine ? L - c0 : 0, hh,
+                       [&](int b, int kk) { return TR::load(Ks + (b * 32 + l32) * LDKS + hh * 8 + kk * 16); },
+                       [&](int b, int c, int dt) {
+                         const T* vp = Vt + (dt * 32 + l32) * LDVT + b * 32 + 16 * c + 4 * hh;
+                         return TR::load2x4(vp, vp + 8);
+                       });
+      }
     }
   }
   lrun += wave_xor(lrun, 32);
