@@ -82,12 +82,12 @@ def test_zero_executions_is_projection_chain(dtype):
               f"n_iter=0 seq{b}")
 
 
-def test_config1_single_utterance_fp32():
+def test_single_utterance_t36_fp32():
     wl = synth.make_workload(1)
     enc = encoder("f32")
     out, _ = _run_padded(enc, wl)
     ref = oracle.encode(wl.ids, wl.lengths, oracle_weights("f32"), K)
-    check(out, ref, "f32", "config1 B=1 T=36")
+    check(out, ref, "f32", "single utterance B=1 T=36")
 
 
 def test_fp32_ragged_batch():
@@ -142,14 +142,14 @@ def test_full_size_configs_sampled(k, nsample):
         ref = oracle.encode_varlen(wl.ids, wl.cu_seqlens, W, K, seqs=seqs)
         cu = wl.cu_seqlens
         for s in seqs:
-            check(got[cu[s]:cu[s + 1]], ref[cu[s]:cu[s + 1]], "bf16", f"config{k} seq{s}")
+            check(got[cu[s]:cu[s + 1]], ref[cu[s]:cu[s + 1]], "bf16", f"{wl.name} seq{s}")
     else:
         got, _ = _run_padded(enc, wl)
         assert np.all(np.isfinite(got))
         ref = oracle.encode(wl.ids, wl.lengths, W, K, seqs=seqs)
         for s in seqs:
             L = int(wl.lengths[s])
-            check(got[s, :L], ref[s, :L], "bf16", f"config{k} seq{s}")
+            check(got[s, :L], ref[s, :L], "bf16", f"{wl.name} seq{s}")
         pad = np.arange(wl.T)[None, :] >= wl.lengths[:, None]
         assert np.all(got[pad] == 0.0)
 
