@@ -447,3 +447,44 @@ def test_fused_group_packing(n, lo, hi, seed):
     for s in (0, 1, n // 2, n - 1):
         a, b = int(cu[s]), int(cu[s + 1])
         check(outs[0][a:b], oracle.encode_sequence(ids[a:b], W, K), "bf16", f"grouped seq{s}")
+
+
+def test_concurrent_calls_on_two_streams_match_single_calls():
+    """Every per-request state lives in the caller's workspace, so two calls
+    with their own workspaces may run at the same time on two streams: each
+    output matches the one its batch gives alone (to the bf16 tolerance,
+    not bit for bit: with the other call's blocks on the chip a paired
+    LayerNorm block may find its partner late and hand its rows over, which
+    normalises them from their stored bf16 values)."""
+    import torch
+    import albert_transformer_amd as A
+    enc = encoder("bf16")
+    batches = [synth.random_padded(81, B=48, T=128, lo=1, hi=128),
+               synth.random_padded(82, B=40, T=96, lo=1, hi=96)]
+    alone = []
+    for wl in batches:
+        B, T = wl.ids.shape
+        out = torch.full((B, T, 512), float("nan"), device="cuda")
+        ws = enc.new_workspace(B, B * T)
+        assert enc.encode_raw(dev(wl.ids), dev(wl.lengths), out, ws) == 0
+        alone.append(out.cpu().numpy())
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs, wss, args = [], [], []
+    for wl in batches:
+        B, T = wl.ids.shape
+        outs.append(torch.full((B, T, 512), float("nan"), device="cuda"))
+        wss.append(enc.new_workspace(B, B * T))
+        args.append((dev(wl.ids), dev(wl.lengths)))
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for i in range(2):
+            assert enc.encode_raw(args[i][0], args[i][1], outs[i], wss[i], stream=streams[i],
+                                  flags=A.ASYNC) == 0
+        torch.cuda.synchronize()
+        for i in range(2):
+            assert A.read_status(wss[i]) == A.OK
+            T = batches[i].ids.shape[1]
+            valid = np.arange(T)[None, :] < batches[i].lengths[:, None]
+            got = outs[i].cpu().numpy()
+            check(got[valid], alone[i][valid], "bf16", f"concurrent batch {i} repeat {rep}")
+            assert np.all(got[~valid] == 0), "pad slots"
