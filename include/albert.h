@@ -177,7 +177,9 @@ size_t albert_workspace_bytes(const albert_ctx* ctx, int n_seq, int64_t max_rows
  * for the stream and returns the device status; with it, the call returns
  * ALBERT_OK after enqueueing and the device status is read with
  * albert_read_status(ws, stream).  Calls that share a workspace must be
- * ordered on one stream. */
+ * ordered on one stream; calls with distinct workspaces (and outputs) may
+ * run concurrently on different streams, since the context is only read
+ * while encoding (kernel timing aside). */
 int albert_encode(albert_ctx* ctx, const int32_t* ids, const int32_t* lengths,
                   int B, int T, float* out, void* ws, size_t ws_bytes,
                   void* hip_stream, unsigned flags);
