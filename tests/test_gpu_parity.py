@@ -420,13 +420,15 @@ def test_layernorm_pair_handoff(B, T, seed):
         check(b[s, :L], oracle.encode_sequence(wl.ids[s, :L], W, K), "bf16", f"handoff seq{s}")
 
 
-@pytest.mark.parametrize("n,lo,hi,seed", [(200, 1, 256, 73), (9000, 1, 3, 74)])
+@pytest.mark.parametrize("n,lo,hi,seed", [(200, 1, 256, 73), (8192, 1, 3, 77), (8193, 1, 3, 78),
+                                          (9000, 1, 3, 74)])
 def test_fused_group_packing(n, lo, hi, seed):
     """The fused kernel's groups: consecutive sequences packed greedily on
     the device while their rows fit 256 (n = 200, lengths 1..256, so a
-    group may hold one long sequence or many short ones), or, beyond 8,192
-    sequences, S = 256 / longest per group chosen on the host (n = 9,000
-    of 1..3 tokens).  Sampled sequences against the oracle, and every
+    group may hold one long sequence or many short ones; n = 8,192, the
+    most the device grouping takes), or, beyond 8,192 sequences, S = 256 /
+    longest per group chosen on the host (n = 8,193 and 9,000 of 1..3
+    tokens).  Sampled sequences against the oracle, and every
     sequence against the separate kernels' run."""
     import torch
     import albert_transformer_amd as A
