@@ -166,6 +166,24 @@ def _ptr(t) -> int:
     return 0 if t is None else int(t.data_ptr())
 
 
+def _need(t, name: str, dtype=None, numel: int | None = None):
+    """Refuse a tensor the library would misread: wrong element type, not on
+    the GPU, not contiguous, or fewer elements than the call will touch.
+    (The library sees only a pointer, so an int64 ID tensor would be read as
+    pairs of int32 values that are all in range.)"""
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch tensor, got {type(t).__name__}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name}: expected {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name}: expected a device (cuda) tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: expected a contiguous tensor")
+    if numel is not None and t.numel() < numel:
+        raise ValueError(f"{name}: {t.numel()} elements, the call needs {numel}")
+
+
 def _stream(stream):
     import torch
     s = torch.cuda.current_stream() if stream is None else stream
@@ -257,15 +275,27 @@ class Encoder:
     # ------------------------------------------------------------- encode --
     def encode_raw(self, ids, lengths, out, ws, stream=None, flags=0, ws_bytes=None) -> int:
         """Padded call on caller tensors; returns the status code."""
+        import torch
+        if ids.dim() != 2:
+            raise ValueError(f"ids: expected [B, T], got {tuple(ids.shape)}")
         B, T = ids.shape
+        _need(ids, "ids", torch.int32)
+        _need(lengths, "lengths", torch.int32, B)
+        _need(out, "out", torch.float32, B * T * self.cfg.out_dim)
+        _need(ws, "ws")
         nb = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
         return lib().albert_encode(self.handle, _ptr(ids), _ptr(lengths), B, T, _ptr(out),
                                    _ptr(ws), nb, _stream(stream), flags)
 
     def encode_varlen_raw(self, ids, cu, max_len, out, ws, stream=None, flags=0,
                           ws_bytes=None, n=None, total=None) -> int:
+        import torch
         n = cu.numel() - 1 if n is None else n
         total = ids.numel() if total is None else total
+        _need(ids, "ids", torch.int32, total)
+        _need(cu, "cu_seqlens", torch.int32, n + 1)
+        _need(out, "out", torch.float32, total * self.cfg.out_dim)
+        _need(ws, "ws")
         nb = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
         return lib().albert_encode_varlen(self.handle, _ptr(ids), _ptr(cu), n, total, max_len,
                                           _ptr(out), _ptr(ws), nb, _stream(stream), flags)
@@ -273,8 +303,13 @@ class Encoder:
     def encode_features_raw(self, x, cu, max_len, out, ws, stream=None, flags=0,
                             ws_bytes=None, n=None, total=None) -> int:
         """Packed call from embedding LayerNorm output x fp32 [total, 128]."""
+        import torch
         n = cu.numel() - 1 if n is None else n
         total = x.shape[0] if total is None else total
+        _need(x, "x", torch.float32, total * self.cfg.emb)
+        _need(cu, "cu_seqlens", torch.int32, n + 1)
+        _need(out, "out", torch.float32, total * self.cfg.out_dim)
+        _need(ws, "ws")
         nb = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
         return lib().albert_encode_features(self.handle, _ptr(x), _ptr(cu), n, total, max_len,
                                             _ptr(out), _ptr(ws), nb, _stream(stream), flags)
@@ -323,8 +358,10 @@ def durations(logits, speed: float = 1.0, dur=None, stream=None):
     """Durations from duration logits [total, K] (CUDA fp32) -> int32 [total]."""
     import torch
     total, K = logits.shape
+    _need(logits, "logits", torch.float32)
     if dur is None:
         dur = torch.empty(total, dtype=torch.int32, device="cuda")
+    _need(dur, "dur", torch.int32, total)
     rc = lib().albert_durations(_ptr(logits), total, K, float(speed), _ptr(dur), _stream(stream))
     if rc != OK:
         raise AlbertError(rc, "albert_durations")
@@ -338,7 +375,14 @@ def expand_workspace_bytes(total: int) -> int:
 def expand_raw(feat, dur, cu_tok, max_frames, out, cu_frames, ws, stream=None, flags=0,
                ws_bytes=None) -> int:
     """Length regulation on caller tensors; returns the status code."""
+    import torch
     total, C = feat.shape
+    _need(feat, "feat", torch.float32)
+    _need(dur, "dur", torch.int32, total)
+    _need(cu_tok, "cu_tok", torch.int32)
+    _need(out, "out", torch.float32, int(max_frames) * C)
+    _need(cu_frames, "cu_frames", torch.int32, cu_tok.numel())
+    _need(ws, "ws")
     nb = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
     return lib().albert_expand(_ptr(feat), _ptr(dur), _ptr(cu_tok), cu_tok.numel() - 1, total, C,
                                _ptr(out), int(max_frames), _ptr(cu_frames), _ptr(ws), nb,
@@ -445,13 +489,25 @@ class TextEncoder:
         return n.value, ms.value
 
     def encode_raw(self, ids, lengths, out, ws, stream=None, flags=0, ws_bytes=None) -> int:
+        import torch
+        if ids.dim() != 2:
+            raise ValueError(f"ids: expected [B, T], got {tuple(ids.shape)}")
         B, T = ids.shape
+        _need(ids, "ids", torch.int32)
+        _need(lengths, "lengths", torch.int32, B)
+        _need(out, "out", torch.float32, B * T * self.out_dim)
+        _need(ws, "ws")
         nb = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
         return lib().albert_text_encode(self.handle, _ptr(ids), _ptr(lengths), B, T, _ptr(out),
                                         _ptr(ws), nb, _stream(stream), flags)
 
     def encode_varlen_raw(self, ids, cu, max_len, out, ws, stream=None, flags=0,
                           ws_bytes=None) -> int:
+        import torch
+        _need(ids, "ids", torch.int32)
+        _need(cu, "cu_seqlens", torch.int32)
+        _need(out, "out", torch.float32, ids.numel() * self.out_dim)
+        _need(ws, "ws")
         nb = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
         return lib().albert_text_encode_varlen(self.handle, _ptr(ids), _ptr(cu), cu.numel() - 1,
                                                ids.numel(), max_len, _ptr(out), _ptr(ws), nb,

@@ -42,9 +42,11 @@ enum albert_status {
   ALBERT_E_ID = 4,        /* an ID at a valid slot outside [0, vocab-1]      */
   ALBERT_E_ALIAS = 5,     /* `out` overlaps an input or the workspace        */
   ALBERT_E_HIP = 6,       /* a HIP runtime call failed                       */
-  ALBERT_E_SYNC = 7       /* the text path's multi-workgroup LSTM recurrence:
-                             a workgroup waited too long for its partners
-                             (they were not resident together)            */
+  ALBERT_E_SYNC = 7       /* cooperating workgroups did not meet: the two
+                             halves of a LayerNorm row tile (bf16, FP8) or
+                             the text path's multi-workgroup LSTM
+                             recurrence; a workgroup waited too long for a
+                             partner that was not resident                 */
 };
 
 /* Compute/storage type of tables, weight matrices and activations.
@@ -155,7 +157,11 @@ int albert_load_weights(albert_ctx** ctx, const albert_config* cfg,
 
 /* Bytes of workspace for a request of n_seq sequences and max_rows token
  * rows: padded calls use (B, B*T); packed calls use (n, total).
- * Returns 0 for invalid arguments.  Size is linear in max_rows. */
+ * Returns 0 for invalid arguments.  Size is linear in max_rows.
+ * The workspace is the caller-owned arena of the page "ALBERT: How Kokoro's
+ * Phoneme Encoder Works", section "How CKE Represents It": every
+ * intermediate buffer of a request sits at an offset planned here from the
+ * request's sizes, and nothing is allocated while encoding. */
 size_t albert_workspace_bytes(const albert_ctx* ctx, int n_seq, int64_t max_rows);
 
 /* Padded batch.
@@ -185,6 +191,11 @@ int albert_encode(albert_ctx* ctx, const int32_t* ids, const int32_t* lengths,
                   void* hip_stream, unsigned flags);
 
 /* Packed (varlen) batch of n sequences with no padding.
+ * This entry point is the library's own (the pages compile one static
+ * length with padding); it serves packed workloads such as 1,024
+ * utterances of geometric lengths, and drops pad rows outright where the
+ * "Kokoro-82M-LiteRT" card trims pad outputs after the fact.  The
+ * arithmetic per sequence is that of albert_encode.
  * ids        dev int32 [total]; sequence s occupies rows cu[s] .. cu[s+1]-1.
  * cu_seqlens dev int32 [n + 1]; cu[0] = 0, cu[n] = total, and every length
  *            cu[s+1]-cu[s] in [1, max_len]; positions restart at 0 per
@@ -213,12 +224,17 @@ int albert_encode_features(albert_ctx* ctx, const float* x, const int32_t* cu_se
 
 /* Wait for hip_stream and return the device status word that the last
  * request enqueued with this workspace left there (ALBERT_E_HIP if the read
- * fails). */
+ * fails).  This is the integer status of the "checked" kernel contracts
+ * (validate before write) of the page "ALBERT: How Kokoro's Phoneme Encoder
+ * Works", section "How CKE Represents It", read back for requests enqueued
+ * with ALBERT_ASYNC. */
 int albert_read_status(const void* ws, void* hip_stream);
 
 /* Debug taps: where a request's intermediate tensors sit in the workspace
  * after it completes (checkpoints at fixed boundaries of the graph, in graph
- * order).  Rows are packed tokens (sequence s at rows cu[s]..cu[s+1]-1);
+ * order: the connected X-Ray checkpoints of the page "ALBERT: How Kokoro's
+ * Phoneme Encoder Works", section "Evidence and the Open Edges", which
+ * compare a running chain at declared boundaries).  Rows are packed tokens (sequence s at rows cu[s]..cu[s+1]-1);
  * elements are the context's dtype (fp32 or bf16) unless noted.  Under
  * ALBERT_FP8, EMB, CTX and G hold E4M3 codes (one byte each), X, QKV and X1
  * are bf16, and taps 10 and 11 are the E4M3 copies of X and X1 that feed

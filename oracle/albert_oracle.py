@@ -278,7 +278,8 @@ def group_schedule(n_iter: int, n_groups: int) -> list:
     """Which weight set each of the n_iter layer executions uses.
 
     [ALBERT] "What ALBERT Changed", part 2: besides full sharing, ALBERT can
-    keep several distinct weight sets, each reused over a block of layers.
+    keep several distinct weight sets, each one serving a contiguous run of
+    the layer executions.
     Reading: the blocks are contiguous and as equal as integers allow,
     execution i (from 0) using set floor(i * G / n_iter); G = 1 is full
     sharing and G = n_iter gives every execution its own set.

@@ -30,7 +30,8 @@ from .albert_oracle import OracleError, bf16_round, layer_norm
 def weight_norm(v, g) -> np.ndarray:
     """Weight normalization: W = g * v / ||v|| per output channel.
 
-    [TTS] "weight-normalized convolutions"; the reparameterization of
+    [TTS] (component list: the text path's convolutions carry weight
+    normalization); the reparameterization of
     Salimans and Kingma (2016), the norm taken over all of an output
     channel's weights (input channels and taps).
     """

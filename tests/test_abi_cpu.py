@@ -138,3 +138,17 @@ def test_text_encoder_tensor_table(L):
     assert L.albert_text_workspace_bytes(None, 1, 1) == 0
     assert L.albert_text_encode(None, None, None, 1, 8, None, None, 0, None, 0) == A.E_ARG
     L.albert_text_free(None)
+
+
+def test_binding_refuses_tensors_the_library_would_misread():
+    """The library sees bare pointers: the binding checks element type,
+    device and contiguity first (an int64 ID tensor would otherwise be read
+    as pairs of in-range int32 values and return OK)."""
+    import torch
+    from albert_transformer_amd._lib import _need
+    with pytest.raises(ValueError, match="int32"):
+        _need(torch.zeros(4, dtype=torch.int64), "ids", torch.int32)
+    with pytest.raises(ValueError, match="device"):
+        _need(torch.zeros(4, dtype=torch.int32), "ids", torch.int32)
+    with pytest.raises(TypeError):
+        _need(np.zeros(4, np.int32), "ids", torch.int32)

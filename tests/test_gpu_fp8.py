@@ -367,6 +367,8 @@ def test_features_entry_rejections():
     assert torch.equal(out, canary)
     assert enc.encode_features_raw(x, cu, 513, out, ws) == A.E_ARG
     assert enc.encode_features_raw(x, cu, 6, out, ws, ws_bytes=64) == A.E_WORKSPACE
-    assert enc.encode_features_raw(x, cu, 6, x, ws) == A.E_ALIAS
+    buf = torch.zeros(10 * 512, device="cuda")   # an output that overlaps the input rows
+    assert enc.encode_features_raw(buf[:1280].view(10, 128), cu, 6, buf.view(10, 512),
+                                   ws) == A.E_ALIAS
     with pytest.raises(A.AlbertError):
         enc.tap(2, 10, "x8")   # E4M3 copies exist only under FP8

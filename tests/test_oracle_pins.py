@@ -536,3 +536,219 @@ def test_fp8_variant_fidelity_by_the_hailo_method():
     got = oracle.encode_fp8_features(x, W8, K)
     cos = float((got * ref).sum() / np.linalg.norm(got) / np.linalg.norm(ref))
     assert 0.99 < cos < 0.99999, cos
+
+
+# ------------------------------------------- FP8 storage points, weight roles ----
+#
+# The low-precision variant's reading (the rounding points of "FP8 GEMM
+# operands", scored by the method of the Hailo card's "Eval results"): every
+# matrix-product input is an E4M3 value, rounded from the exact value it comes
+# from; the residual stream and Q|K|V are stored as bf16; weights are E4M3
+# codes per output row times a power of two.  The checker below records the
+# oracle's products, attention calls, LayerNorms and GELU in order, and checks
+# each input against that rule from the exact value it came from.
+
+_TABLES = ("emb.word", "emb.pos", "emb.type")
+_MATRICES = ("proj.w", "q.w", "k.w", "v.w", "o.w", "ffn1.w", "ffn2.w", "out.w")
+_VECTORS = ("emb.ln.g", "emb.ln.b", "proj.b", "q.b", "k.b", "v.b", "o.b", "attn_ln.g",
+            "attn_ln.b", "ffn1.b", "ffn2.b", "ffn_ln.g", "ffn_ln.b", "out.b")
+
+
+def _torch_bf16(a):
+    return torch.from_numpy(np.asarray(a, np.float32)).to(torch.bfloat16).double().numpy()
+
+
+def _role(name):
+    head, _, rest = name.partition(".")
+    return rest if head[:1] == "g" and head[1:].isdigit() else name
+
+
+class _Recorder:
+    def __init__(self, ao):
+        self.events = []
+        self._dense, self._attn, self._ln, self._gelu = ao.dense, ao.attention, ao.layer_norm, ao.gelu_tanh
+
+    def install(self, monkeypatch, ao):
+        def dense(x, w, b):
+            y = self._dense(x, w, b)
+            self.events.append(("dense", np.array(x, np.float64), np.asarray(w), y))
+            return y
+
+        def attention(q, k, v, heads):
+            o = self._attn(q, k, v, heads)
+            self.events.append(("attn", (np.array(q), np.array(k), np.array(v)), None, o))
+            return o
+
+        def layer_norm(x, g, b, eps):
+            y = self._ln(x, g, b, eps)
+            self.events.append(("ln", np.array(x, np.float64), None, y))
+            return y
+
+        def gelu(x):
+            y = self._gelu(x)
+            self.events.append(("gelu", np.array(x, np.float64), None, y))
+            return y
+        monkeypatch.setattr(ao, "dense", dense)
+        monkeypatch.setattr(ao, "attention", attention)
+        monkeypatch.setattr(ao, "layer_norm", layer_norm)
+        monkeypatch.setattr(ao, "gelu_tanh", gelu)
+
+
+def _storage_violations(events, x_ln, n_iter):
+    """Every place where the recorded run breaks the FP8 variant's rule."""
+    E8 = oracle.e4m3_round
+    bad = []
+    ev = list(events)
+    if len(ev) != 1 + 10 * n_iter + 1:
+        return [f"{len(ev)} recorded steps"]
+
+    def take(kind):
+        e = ev.pop(0)
+        if e[0] != kind:
+            bad.append(f"expected {kind}, got {e[0]}")
+        return e
+
+    def weights_on_grid(w, what):
+        m = np.abs(w).max(axis=1)
+        k = np.floor(np.log2(448.0 / np.where(m > 0, m, 1.0)))
+        k += (m * 2.0 ** (k + 1) <= 448.0)
+        k -= (m * 2.0 ** k > 448.0)
+        s = w * 2.0 ** k[:, None]
+        if not np.array_equal(E8(s), s):
+            bad.append(f"{what}: weights off the per-row E4M3 grid")
+
+    def product_input(e, exact, what):
+        if not np.array_equal(e[1], E8(exact)):
+            bad.append(f"{what}: input is not the E4M3 rounding of its source")
+        weights_on_grid(e[2], what)
+
+    d = take("dense")
+    product_input(d, x_ln, "projection")
+    prev = d[3]
+    for it in range(n_iter):
+        dq, dk, dv = take("dense"), take("dense"), take("dense")
+        for e, nm in ((dq, "q"), (dk, "k"), (dv, "v")):
+            product_input(e, prev, f"layer {it} {nm} projection")
+        a = take("attn")
+        for t, e, nm in zip(a[1], (dq, dk, dv), "qkv"):
+            if not np.array_equal(t, _torch_bf16(e[3])):
+                bad.append(f"layer {it} attention {nm}: not the bf16 rounding of the projection")
+        do = take("dense")
+        product_input(do, a[3], f"layer {it} output projection")
+        ln1 = take("ln")
+        if not np.array_equal(ln1[1], _torch_bf16(prev) + do[3]):
+            bad.append(f"layer {it} attention residual: not the bf16 residual stream")
+        f1 = take("dense")
+        product_input(f1, ln1[3], f"layer {it} ffn1")
+        ge = take("gelu")
+        if not np.array_equal(ge[1], f1[3]):
+            bad.append(f"layer {it} gelu: input is not the ffn1 output")
+        f2 = take("dense")
+        product_input(f2, ge[3], f"layer {it} ffn2")
+        ln2 = take("ln")
+        if not np.array_equal(ln2[1], _torch_bf16(ln1[3]) + f2[3]):
+            bad.append(f"layer {it} ffn residual: not the bf16 residual stream")
+        prev = ln2[3]
+    d = take("dense")
+    product_input(d, prev, "output projection")
+    return bad
+
+
+def _fp8_run(monkeypatch, mutate=None):
+    from oracle import albert_oracle as ao
+    cfg = synth.Config(n_iter=2)
+    W8 = _w64(cfg, dtype="fp8")
+    x = np.random.default_rng(5).normal(0, 1, (7, 128))
+    with monkeypatch.context() as mp:
+        if mutate is not None:
+            mutate(mp, ao)
+        rec = _Recorder(ao)
+        rec.install(mp, ao)
+        ao.encode_fp8_features(x, W8, cfg)
+    return _storage_violations(rec.events, x, cfg.n_iter)
+
+
+def test_fp8_emulation_rounds_at_every_storage_point(monkeypatch):
+    """Each product input of the FP8 emulation is the E4M3 rounding of the
+    exact value it comes from, Q|K|V and the residual stream are its bf16
+    rounding, and every weight row is E4M3 after its power-of-two scale."""
+    assert _fp8_run(monkeypatch) == []
+
+
+def _skip_call(name, index, replacement=None):
+    """Mutation: the index-th call of ao.<name> returns its input unrounded
+    (or `replacement(input)`), every other call is unchanged."""
+    def mutate(mp, ao):
+        orig = getattr(ao, name)
+        count = [0]
+
+        def f(v):
+            i = count[0]
+            count[0] += 1
+            if i == index:
+                return np.asarray(v, np.float64) if replacement is None else replacement(v)
+            return orig(v)
+        mp.setattr(ao, name, f)
+    return mutate
+
+
+@pytest.mark.parametrize("index", range(10))
+def test_fp8_checker_catches_a_missing_operand_rounding(monkeypatch, index):
+    """Removing any one E4M3 rounding (there are 2 + 4 per execution at two
+    executions: the input, the projection output, and per execution the
+    context, both LayerNorm outputs and the GELU output) breaks the rule."""
+    assert _fp8_run(monkeypatch, _skip_call("fp8_operand", index)) != []
+
+
+@pytest.mark.parametrize("index", range(10))
+def test_fp8_checker_catches_a_missing_storage_rounding(monkeypatch, index):
+    """Removing any one bf16 storage rounding that has a consumer (the
+    projection output, and per execution q, k, v and both LayerNorm outputs;
+    the last execution's bf16 output is the eleventh call and feeds nothing,
+    since only its E4M3 copy enters the output projection) breaks the rule."""
+    assert _fp8_run(monkeypatch, _skip_call("fp8_store", index)) != []
+
+
+@pytest.mark.parametrize("index", (1, 2, 3))
+def test_fp8_checker_catches_qkv_rounded_to_e4m3(monkeypatch, index):
+    """Q, K or V rounded to E4M3 instead of bf16 (E4M3 values are also bf16
+    values, so this is caught by comparing with the rounding of the source)."""
+    assert _fp8_run(monkeypatch, _skip_call("fp8_store", index, oracle.e4m3_round)) != []
+
+
+@pytest.mark.parametrize("G", (1, 3))
+def test_prepare_weights_role_rule(G):
+    """bf16 storage rounds exactly the three tables and eight weight matrices
+    (torch's bfloat16 conversion) and keeps the fourteen bias and LayerNorm
+    vectors bit-identical to float32; the FP8 variant also keeps tables bf16
+    and vectors exact, and puts each matrix row on the E4M3 grid after its
+    power-of-two scale."""
+    cfg = synth.Config(n_groups=G)
+    w = synth.make_weights(cfg)
+    seen = {"table": 0, "matrix": 0, "vector": 0}
+    Wb = oracle.prepare_weights(w, "bf16")
+    W8 = oracle.prepare_weights(w, "fp8")
+    for name, t in w.items():
+        t32 = np.asarray(t, np.float32)
+        role = _role(name)
+        if role in _TABLES or role in _MATRICES:
+            seen["table" if role in _TABLES else "matrix"] += 1
+            ref = _torch_bf16(t32)
+            assert np.array_equal(Wb[name], ref), name
+            assert not np.array_equal(ref, t32.astype(np.float64)), name  # rounding happened
+        else:
+            assert role in _VECTORS, name
+            seen["vector"] += 1
+            assert Wb[name].dtype == np.float64 and np.array_equal(Wb[name], t32.astype(np.float64)), name
+            assert np.array_equal(W8[name], t32.astype(np.float64)), name
+        if role in _TABLES:
+            assert np.array_equal(W8[name], _torch_bf16(t32)), name
+        if role in _MATRICES:
+            m = np.abs(t32.astype(np.float64)).max(axis=1)
+            k = np.floor(np.log2(448.0 / m))
+            k += (m * 2.0 ** (k + 1) <= 448.0)
+            k -= (m * 2.0 ** k > 448.0)
+            s = W8[name] * 2.0 ** k[:, None]
+            assert np.array_equal(oracle.e4m3_round(s), s), name
+            assert np.max(np.abs(W8[name] - t32)) <= np.max(np.abs(t32)) * 2.0 ** -4, name
+    assert seen == {"table": 3, "matrix": 2 + 6 * G, "vector": 4 + 10 * G}, seen
