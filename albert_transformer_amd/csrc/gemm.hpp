@@ -106,7 +106,19 @@ struct GemmArgs {
   unsigned long long* xch;
   int xtag;
   int pair_spin;
+  // EPI_LN_PAIR: [M, 2, BN] fp32, where a half that hands its rows over
+  // leaves its values before normalisation (row m, half h at (2m + h) * BN;
+  // both halves may try to hand over, and only one of them wins), so that
+  // the partner normalises exactly the values the half itself would have
+  float* hand;
 };
+
+// LayerNorm output of one value: (v - mean) * rstd * gain + shift, written
+// once here so that every path that normalises a value (a block's own
+// columns, or a partner's handed-over columns) rounds it the same way.
+__device__ __forceinline__ float ln_out(float v, float mean, float rstd, float gain, float shift) {
+  return __builtin_fmaf((v - mean) * rstd, gain, shift);
+}
 
 // Polls (each after a short sleep) of a block that is known to be running
 // before giving up and reporting ALBERT_E_SYNC.
@@ -220,8 +232,11 @@ gemm_kernel(GemmArgs g) {
   int sc[TN];  // F8: E8M0 exponents of this lane's weight rows
 #pragma unroll
   for (int j = 0; j < TN; ++j) sc[j] = 127;
-  // Buffer resources over the tile's rows: the hardware range check turns
-  // reads of X rows at or past M into zeros (their results are never stored).
+  // Buffer resources over the tile's rows.  The range check covers only the
+  // per-lane offset (the row offset of a DMA instruction is in its scalar
+  // offset), so X rows at or past M read whatever the buffer holds there;
+  // each token is one column of the product, and those columns are never
+  // stored.
   auto setup = [&](int t) __attribute__((always_inline)) {
     m0 = (t / g.n_tiles) * BM;
     n0 = (t % g.n_tiles) * BN;
@@ -531,7 +546,8 @@ gemm_kernel(GemmArgs g) {
       asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
       T* __restrict__ Y = static_cast<T*>(g.Y);
       // This block's columns: normalised from registers, or (raw, EPI_LN_PAIR
-      // handing its half over) the values before normalisation.
+      // handing its half over) the fp32 values before normalisation, into
+      // the handoff rows.
       auto store_own = [&](bool raw) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
@@ -542,17 +558,22 @@ gemm_kernel(GemmArgs g) {
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
               const int nl = wn * WTN + j * 32 + 8 * q + 4 * hh;
+              if constexpr (PAIR) {
+                if (raw) {
+                  *reinterpret_cast<f32x4*>(g.hand + ((int64_t)m * 2 + en0 / BN) * BN + nl) =
+                      f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                            acc[i][j][4 * q + 3]};
+                  continue;
+                }
+              }
               float o[4];
 #pragma unroll
               for (int e = 0; e < 4; ++e) {
-                o[e] = raw ? acc[i][j][4 * q + e]
-                           : (acc[i][j][4 * q + e] - mean[i]) * rstd[i] * g_s[nl + e] + b_s[nl + e];
+                o[e] = ln_out(acc[i][j][4 * q + e], mean[i], rstd[i], g_s[nl + e], b_s[nl + e]);
                 if constexpr (EPI == EPI_LN_ACT) o[e] = o[e] >= 0.f ? o[e] : o[e] * g.slope;
               }
               TS::store4(Y + (int64_t)m * g.ldy + en0 + nl, o[0], o[1], o[2], o[3]);
-              if constexpr (F8) {
-                if (!raw) store4_as<T, true>(g.Y8, (int64_t)m * g.ldy8 + en0 + nl, o[0], o[1], o[2], o[3]);
-              }
+              if constexpr (F8) store4_as<T, true>(g.Y8, (int64_t)m * g.ldy8 + en0 + nl, o[0], o[1], o[2], o[3]);
             }
         }
       };
@@ -563,8 +584,11 @@ gemm_kernel(GemmArgs g) {
       // A block publishes its statistics and polls the partner's for a short
       // while.  If they all came, it normalises its own half and then learns
       // whether the partner does the same or handed its half over.  If not
-      // (the partner is late, or not resident), it leaves its values before
-      // normalisation in Y and claims the handoff word: the partner, whenever
+      // (the partner is late, or not resident), it leaves its fp32 values
+      // before normalisation in the handoff rows and claims the handoff word
+      // (the partner then normalises those very values with the same
+      // statistics and the same ln_out, so the output bits do not depend on
+      // which block normalised them): the partner, whenever
       // it runs, normalises both halves.  If the partner claimed first, this
       // block normalises both.  Each remaining wait is for a block that has
       // already published its statistics, so it is running and ends.
@@ -676,7 +700,7 @@ gemm_kernel(GemmArgs g) {
             help = true;
           }
         }
-        if (help) {  // the partner's values before normalisation are in Y
+        if (help) {  // the partner's values before normalisation are in the handoff rows
           const int n0p = (half ^ 1) * BN;
 #pragma unroll
           for (int i = 0; i < TM; ++i) {
@@ -686,13 +710,14 @@ gemm_kernel(GemmArgs g) {
             for (int j = 0; j < TN; ++j)
 #pragma unroll
               for (int q = 0; q < 4; ++q) {
-                const int c = n0p + wn * WTN + j * 32 + 8 * q + 4 * hh;
+                const int nl = wn * WTN + j * 32 + 8 * q + 4 * hh;
+                const int c = n0p + nl;
                 T* const y = Y + (int64_t)m * g.ldy + c;
-                const f32x4 pv = TS::load4f(y);
+                const f32x4 pv =
+                    *reinterpret_cast<const f32x4*>(g.hand + ((int64_t)m * 2 + (half ^ 1)) * BN + nl);
                 float o[4];
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                  o[e] = (pv[e] - mean[i]) * rstd[i] * g.ln_g[c + e] + g.ln_b[c + e];
+                for (int e = 0; e < 4; ++e) o[e] = ln_out(pv[e], mean[i], rstd[i], g.ln_g[c + e], g.ln_b[c + e]);
                 TS::store4(y, o[0], o[1], o[2], o[3]);
                 if constexpr (F8)
                   store4_as<T, true>(g.Y8, (int64_t)m * g.ldy8 + c, o[0], o[1], o[2], o[3]);

@@ -10,6 +10,7 @@
 #include <type_traits>
 
 #include "gemm.hpp"
+#include "host.hpp"
 
 namespace albert {
 
@@ -143,11 +144,6 @@ inline int ln_pair_rows(int64_t max_rows, int grid_cap, bool f8) {
 // them; E4M3, an even number of 64-deep slices
 inline bool ln_pair_k_ok(int K, bool f8) {
   return f8 ? K % 128 == 0 && K > 0 : K % 32 == 0 && K / 32 >= 5;
-}
-// exchange words the pair launches need for up to max_rows rows: 4*BM + 8
-// per row tile, for either tile height
-inline size_t ln_pair_words(int64_t max_rows) {
-  return (size_t)std::max((max_rows + 127) / 128 * (4 * 128 + 8), (max_rows + 255) / 256 * (4 * 256 + 8));
 }
 template <bool F8>
 inline hipError_t gemm_ln_pair(GemmArgs g, int64_t max_rows, int grid_cap, hipStream_t s) {

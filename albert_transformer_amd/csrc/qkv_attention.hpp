@@ -18,9 +18,12 @@
 // DMA (two stages), 8 waves as 4 (rows) x 2 (features) of 64 x 96; weights
 // are the MFMA A operand, tokens B (lane = token), as in gemm.hpp.  E4M3
 // weight rows carry an E8M0 exponent that the matrix core applies as A's
-// scale; Q, K and V are stored as bf16 either way.  Rows of the tile past the group belong to the
-// next group (or past M, where the range check reads zeros): their results
-// are never used.
+// scale; Q, K and V are stored as bf16 either way.  Rows of the tile past
+// the group belong to the next group, or lie past M: the DMA's row offset is
+// in the scalar offset, which the buffer range check does not cover, so
+// those rows read whatever the workspace holds there.  Their queries are
+// never stored, their keys are masked (the score is replaced, not added
+// to), and their V^T columns are written as zeros.
 //
 // Attention phase: the stage buffers are reused for Q and K (row-major) and
 // V^T; wave w owns queries 32w .. 32w+31 of the tile, one per lane, as in
@@ -220,10 +223,13 @@ qkv_attention_kernel(QkvAttnArgs a) {
           } else if (f0 < 2 * D) {
             TR::store4(Ks + tok * LDQ + (f0 - D), o[0], o[1], o[2], o[3]);
           } else {
+            // V^T columns of rows past the group are zero: their keys get
+            // probability 0, and 0 times a stale non-finite value would not
+            // be 0 (rows past M hold whatever the workspace held)
             const int d0 = f0 - 2 * D;
             bf16* vt = d0 < 32 ? Vt0 + d0 * LDV : Vt1 + (d0 - 32) * LDV;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) vt[e * LDV + tok] = (bf16)o[e];
+            for (int e = 0; e < 4; ++e) vt[e * LDV + tok] = tok < nrows ? (bf16)o[e] : (bf16)0.0f;
           }
         }
     }

@@ -45,9 +45,6 @@ struct albert_text_ctx {
 
 namespace {
 
-constexpr size_t kAlign = 256;
-inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
-
 bool text_config_ok(const albert_text_config& c) {
   return c.vocab >= 1 && c.channels == 512 && c.kernel >= 1 && c.kernel <= 7 &&
          c.kernel % 2 == 1 && c.n_conv >= 1 && c.n_conv <= 8 && c.hidden == kLstmH && std::isfinite(c.ln_eps) &&
@@ -130,11 +127,6 @@ TextLayout text_plan(const albert_text_ctx* c, int n_seq, int64_t max_rows) {
   return L;
 }
 
-bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
-  if (!a || !b || !na || !nb) return false;
-  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
-  return x < y + nb && y < x + na;
-}
 
 template <typename Fn>
 void ttimed(albert_text_ctx* c, int kind, hipStream_t s, Fn&& fn) {

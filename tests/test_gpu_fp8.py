@@ -243,10 +243,10 @@ def test_fp8_full_depth_parity():
 def test_fp8_layernorm_pair_handoff():
     """E4M3 LayerNorm products split each row tile between two workgroups
     that swap row statistics; ALBERT_LN_HANDOFF makes one half of every
-    tile hand its rows over (before normalisation, as bf16) instead of
-    waiting.  Both runs meet the full-depth bar against the emulation, and
-    agree with each other to it (E4M3 codes decided from the bf16 hand-over
-    may flip)."""
+    tile hand its rows over (its fp32 values before normalisation) instead
+    of waiting.  The partner normalises exactly those values, so both runs
+    give the same bits; both meet the full-depth bar against the
+    emulation."""
     import albert_transformer_amd as A
     enc = _enc("fp8")
     rng = np.random.default_rng(10)
@@ -259,6 +259,7 @@ def test_fp8_layernorm_pair_handoff():
         cos = float(np.min(row_cosines(a, b)))
         print(f"[fp8] handoff vs default run{rep} max_abs={err:.3e} min_cos={cos:.6f}", flush=True)
         assert err <= FP8_MAX_ABS and cos >= FP8_MIN_COS
+        assert np.array_equal(a, b), f"handoff run {rep}: bits differ from the default run"
     for s in (0, 1):
         sl = slice(int(cu[s]), int(cu[s + 1]))
         ref = oracle.encode_fp8_features(x[sl], _w8(), K)

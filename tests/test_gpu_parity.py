@@ -398,10 +398,12 @@ def test_layernorm_pair_handoff(B, T, seed):
     """bf16 LayerNorm products split each 768-wide row tile between two
     workgroups that swap row statistics.  ALBERT_LN_HANDOFF stops them from
     waiting for each other, so in every row tile one half hands its rows
-    over (before normalisation, as bf16) and the other normalises both:
-    the fallback for a partner that is late or not resident.  Outputs agree
-    with the default run and, on sampled sequences, with the oracle, to the
-    bf16 tolerance.  B=6 runs 128-row tiles, B=256 x T=128 256-row tiles."""
+    over (its fp32 values before normalisation) and the other normalises
+    both: the fallback for a partner that is late or not resident.  Outputs
+    equal the default run bit for bit (the same values, statistics and
+    arithmetic, whichever block normalises them) and, on sampled sequences,
+    match the oracle.  B=6 runs 128-row tiles, B=256 x T=128 256-row
+    tiles."""
     import albert_transformer_amd as A
     enc = encoder("bf16")
     W = oracle_weights("bf16")
@@ -413,6 +415,7 @@ def test_layernorm_pair_handoff(B, T, seed):
         for s in range(B):
             L = int(wl.lengths[s])
             check(b[s, :L], a[s, :L], "bf16", f"handoff vs default seq{s} run{rep}")
+        assert np.array_equal(a, b), f"handoff run {rep}: bits differ from the default run"
         pad = np.arange(T)[None, :] >= wl.lengths[:, None]
         assert np.all(b[pad] == 0.0)
     for s in (0, B - 1):
@@ -454,10 +457,10 @@ def test_fused_group_packing(n, lo, hi, seed):
 def test_concurrent_calls_on_two_streams_match_single_calls():
     """Every per-request state lives in the caller's workspace, so two calls
     with their own workspaces may run at the same time on two streams: each
-    output matches the one its batch gives alone (to the bf16 tolerance,
-    not bit for bit: with the other call's blocks on the chip a paired
-    LayerNorm block may find its partner late and hand its rows over, which
-    normalises them from their stored bf16 values)."""
+    output equals, bit for bit, the one its batch gives alone.  (With the
+    other call's blocks on the chip a paired LayerNorm block may find its
+    partner late and hand its rows over; the partner then normalises the
+    same fp32 values with the same statistics, so the bits do not change.)"""
     import torch
     import albert_transformer_amd as A
     enc = encoder("bf16")
@@ -489,4 +492,37 @@ def test_concurrent_calls_on_two_streams_match_single_calls():
             valid = np.arange(T)[None, :] < batches[i].lengths[:, None]
             got = outs[i].cpu().numpy()
             check(got[valid], alone[i][valid], "bf16", f"concurrent batch {i} repeat {rep}")
+            assert np.array_equal(got, alone[i]), f"concurrent batch {i} repeat {rep}: bits differ"
             assert np.all(got[~valid] == 0), "pad slots"
+
+
+@pytest.mark.parametrize("flags_name", ["fused", "unfused", "handoff"])
+def test_poisoned_workspace_ragged_tail(flags_name):
+    """The workspace's contents on entry are ignored.  Filled with 0xFF bytes
+    (NaN in bf16 and fp32) before a packed call whose last group ends inside
+    a 32-row block, the rows past the last token stay stale: products read
+    them (the buffer range check does not cover a DMA's row offset), the
+    fused attention must not let them reach a valid context (0 times NaN is
+    not 0).  Outputs must be finite and match the oracle."""
+    import torch
+    import albert_transformer_amd as A
+    enc = encoder("bf16")
+    W = oracle_weights("bf16")
+    flags = {"fused": 0, "unfused": A.UNFUSED, "handoff": A.LN_HANDOFF}[flags_name]
+    rng = np.random.default_rng(91)
+    lengths = np.array([100, 90, 37, 5], np.int32)   # 232 rows: one group, ends mid-block
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    ids = rng.integers(0, 178, int(cu[-1])).astype(np.int32)
+    n, total = len(lengths), int(cu[-1])
+    ws = enc.new_workspace(n, total)
+    ws.fill_(0xFF)
+    for call in range(2):   # the second call reuses the workspace the first wrote
+        out = torch.full((total, 512), float("nan"), device="cuda")
+        print(f"[poison] {flags_name} call {call}", flush=True)
+        assert enc.encode_varlen_raw(dev(ids), dev(cu), 128, out, ws, flags=flags) == 0
+        got = out.cpu().numpy().astype(np.float64)
+        assert np.all(np.isfinite(got))
+        for s in range(n):
+            a, b = int(cu[s]), int(cu[s + 1])
+            check(got[a:b], oracle.encode_sequence(ids[a:b], W, K), "bf16",
+                  f"poisoned workspace {flags_name} seq{s}")
