@@ -15,10 +15,11 @@ import numpy as np
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libalbert.so")
 
-OK, E_ARG, E_WORKSPACE, E_LENGTH, E_ID, E_ALIAS, E_HIP, E_SYNC = range(8)
+OK, E_ARG, E_WORKSPACE, E_LENGTH, E_ID, E_ALIAS, E_HIP, E_SYNC, E_SCRATCH = range(9)
 STATUS_NAMES = {OK: "OK", E_ARG: "E_ARG", E_WORKSPACE: "E_WORKSPACE",
                 E_LENGTH: "E_LENGTH", E_ID: "E_ID", E_ALIAS: "E_ALIAS", E_HIP: "E_HIP",
-                E_SYNC: "E_SYNC"}
+                E_SYNC: "E_SYNC", E_SCRATCH: "E_SCRATCH"}
+SCRATCH_BYTES = 64 << 20   # ALBERT_SCRATCH_BYTES
 F32, BF16, FP8 = 0, 1, 2
 DTYPES = {"f32": F32, "bf16": BF16, "fp8": FP8}
 ASYNC = 1
@@ -30,6 +31,7 @@ TAPS = {"status": 0, "cu": 1, "row_seq": 2, "row_pos": 3, "emb": 4, "x": 5,
 
 EXPORTS = ("albert_default_config", "albert_n_tensors", "albert_tensor_name",
            "albert_tensor_shape", "albert_load_weights", "albert_workspace_bytes", "albert_encode",
+           "albert_encode_noalloc",
            "albert_encode_varlen", "albert_encode_features", "albert_read_status", "albert_tap", "albert_free",
            "albert_status_str", "albert_time_kernel", "albert_kernel_time",
            "albert_durations", "albert_expand_workspace_bytes", "albert_expand",
@@ -88,6 +90,8 @@ def lib():
     L.albert_workspace_bytes.restype = sz
     L.albert_encode.argtypes = [vp, vp, vp, i32, i32, vp, vp, sz, vp, ctypes.c_uint]
     L.albert_encode.restype = i32
+    L.albert_encode_noalloc.argtypes = [vp, vp, vp, i32, i32, vp, vp, vp, ctypes.c_uint]
+    L.albert_encode_noalloc.restype = i32
     L.albert_encode_varlen.argtypes = [vp, vp, vp, i32, i32, i32, vp, vp, sz, vp,
                                        ctypes.c_uint]
     L.albert_encode_varlen.restype = i32
@@ -286,6 +290,20 @@ class Encoder:
         nb = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
         return lib().albert_encode(self.handle, _ptr(ids), _ptr(lengths), B, T, _ptr(out),
                                    _ptr(ws), nb, _stream(stream), flags)
+
+    def encode_noalloc_raw(self, ids, lengths, out, status, stream=None, flags=0) -> int:
+        """Padded call on the library's static scratch (no workspace); the
+        device status lands in status (int32 [1]).  Returns the host status."""
+        import torch
+        if ids.dim() != 2:
+            raise ValueError(f"ids: expected [B, T], got {tuple(ids.shape)}")
+        B, T = ids.shape
+        _need(ids, "ids", torch.int32)
+        _need(lengths, "lengths", torch.int32, B)
+        _need(out, "out", torch.float32, B * T * self.cfg.out_dim)
+        _need(status, "status", torch.int32, 1)
+        return lib().albert_encode_noalloc(self.handle, _ptr(ids), _ptr(lengths), B, T,
+                                           _ptr(out), _ptr(status), _stream(stream), flags)
 
     def encode_varlen_raw(self, ids, cu, max_len, out, ws, stream=None, flags=0,
                           ws_bytes=None, n=None, total=None) -> int:

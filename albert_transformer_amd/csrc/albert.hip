@@ -16,6 +16,7 @@
 #include <cstdint>
 #include <algorithm>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <type_traits>
 #include <vector>
@@ -42,10 +43,18 @@ struct LayerW {
   const float *qkv_b, *o_b, *ln1_g, *ln1_b, *ffn1_b, *ffn2_b, *ln2_g, *ln2_b;
 };
 
+// Scratch of albert_encode_noalloc: the workspace of a request, in the
+// library's own device memory, for callers that cannot allocate.  Every GPU
+// the library runs on holds one copy of it until the process ends.  In host
+// code its name is only a stand-in: the device address of each GPU's copy is
+// taken once per device (scratch_address) and used everywhere instead.
+static __device__ __align__(256) unsigned char scratch[ALBERT_SCRATCH_BYTES];
+
 struct albert_ctx {
   albert_config cfg;
   int dtype;
   int device;
+  void* scratch = nullptr;  // this device's copy of `scratch`
   int grid_cap;  // persistent GEMM grid: CUs rounded down to a multiple of 8
   bool ln_pair = false;  // LayerNorm GEMMs on block pairs (bf16 storage)
   void* mem;
@@ -66,6 +75,23 @@ __global__ void clear_u64_kernel(unsigned long long* __restrict__ p, int64_t n) 
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i < n) p[i] = 0ull;
 }
+
+// Device address of `scratch` on `device` (the current device), looked up
+// once per device and kept; null if the lookup fails.
+void* scratch_address(int device) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  if (device < 0 || device >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[device]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) == hipSuccess) addr[device] = p;
+  }
+  return addr[device];
+}
+
+__global__ void copy_status_kernel(const int* __restrict__ src, int* __restrict__ dst) { *dst = *src; }
 
 
 // Launch `fn` on stream s; when `kind` is the kernel kind selected with
@@ -315,6 +341,12 @@ int albert_load_weights(albert_ctx** out_ctx, const albert_config* cfg,
     delete ctx;
     return ALBERT_E_HIP;
   }
+  ctx->scratch = scratch_address(ctx->device);
+  if (!ctx->scratch) {
+    (void)hipFree(ctx->mem);
+    delete ctx;
+    return ALBERT_E_HIP;
+  }
   ctx->grid_cap = std::max(8, n_cu / 8 * 8);
   {  // paired LayerNorm blocks: shapes they take, and one block per CU fits
     const bool f8 = dtype == ALBERT_FP8;
@@ -393,6 +425,34 @@ int albert_encode(albert_ctx* ctx, const int32_t* ids, const int32_t* lengths, i
   const int rc = run_any(ctx, ids, lengths, B, T, rows, T, out, ws, s, (const float*)nullptr,
                          flags);
   return finish(rc, ws, s, flags);
+}
+
+int albert_encode_noalloc(albert_ctx* ctx, const int32_t* ids, const int32_t* lengths, int B,
+                          int T, float* out, int32_t* status, void* stream, unsigned flags) {
+  if (ctx && B == 0) return ALBERT_OK;  // empty batch: nothing to do
+  if (!ctx || !ids || !lengths || !out || !status || B < 1 || T < 1 || T > ctx->cfg.max_pos ||
+      (int64_t)B * T > INT32_MAX || !ctx->scratch || !device_matches(ctx))
+    return ALBERT_E_ARG;
+  const int64_t rows = (int64_t)B * T;
+  const Layout L = plan(ctx->cfg, ctx->dtype, B, rows);
+  if (L.total > (size_t)ALBERT_SCRATCH_BYTES) return ALBERT_E_SCRATCH;
+  const size_t out_bytes = (size_t)rows * ctx->cfg.out_dim * 4;
+  if (overlaps(out, out_bytes, ids, (size_t)rows * 4) ||
+      overlaps(out, out_bytes, lengths, (size_t)B * 4) ||
+      overlaps(out, out_bytes, status, 4) || overlaps(status, 4, ids, (size_t)rows * 4) ||
+      overlaps(status, 4, lengths, (size_t)B * 4))
+    return ALBERT_E_ALIAS;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // the same launch sequence as albert_encode, on this device's scratch
+  int rc = run_any(ctx, ids, lengths, B, T, rows, T, out, ctx->scratch, s, (const float*)nullptr,
+                   flags);
+  if (rc == ALBERT_OK) {
+    hipLaunchKernelGGL(copy_status_kernel, dim3(1), dim3(1), 0, s,
+                       reinterpret_cast<const int*>(static_cast<char*>(ctx->scratch) + L.status),
+                       status);
+    if (hipGetLastError() != hipSuccess) rc = ALBERT_E_HIP;
+  }
+  return rc;
 }
 
 int albert_encode_varlen(albert_ctx* ctx, const int32_t* ids, const int32_t* cu_seqlens, int n,
@@ -593,6 +653,7 @@ const char* albert_status_str(int status) {
     case ALBERT_E_ID: return "phoneme id outside the vocabulary";
     case ALBERT_E_ALIAS: return "output overlaps an input or the workspace";
     case ALBERT_E_HIP: return "HIP runtime error";
+    case ALBERT_E_SCRATCH: return "request larger than the static scratch (ALBERT_SCRATCH_BYTES)";
     case ALBERT_E_SYNC:
       return "cooperating workgroups did not meet (LayerNorm row halves or LSTM quad not co-resident)";
     default: return "unknown status";

@@ -42,11 +42,13 @@ enum albert_status {
   ALBERT_E_ID = 4,        /* an ID at a valid slot outside [0, vocab-1]      */
   ALBERT_E_ALIAS = 5,     /* `out` overlaps an input or the workspace        */
   ALBERT_E_HIP = 6,       /* a HIP runtime call failed                       */
-  ALBERT_E_SYNC = 7       /* cooperating workgroups did not meet: the two
+  ALBERT_E_SYNC = 7,      /* cooperating workgroups did not meet: the two
                              halves of a LayerNorm row tile (bf16, FP8) or
                              the text path's multi-workgroup LSTM
                              recurrence; a workgroup waited too long for a
                              partner that was not resident                 */
+  ALBERT_E_SCRATCH = 8    /* albert_encode_noalloc: the request needs more
+                             workspace than ALBERT_SCRATCH_BYTES           */
 };
 
 /* Compute/storage type of tables, weight matrices and activations.
@@ -189,6 +191,32 @@ size_t albert_workspace_bytes(const albert_ctx* ctx, int n_seq, int64_t max_rows
 int albert_encode(albert_ctx* ctx, const int32_t* ids, const int32_t* lengths,
                   int B, int T, float* out, void* ws, size_t ws_bytes,
                   void* hip_stream, unsigned flags);
+
+/* Bytes of the static device scratch behind albert_encode_noalloc (64 MiB
+ * on every GPU the library runs on, held until the process ends). */
+#define ALBERT_SCRATCH_BYTES (64u << 20)
+
+/* albert_encode for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * The workspace is the library's own static device scratch instead of a
+ * caller buffer; the call allocates nothing, frees nothing and never waits
+ * for the stream (ALBERT_ASYNC is implied; ALBERT_UNFUSED and
+ * ALBERT_LN_HANDOFF work as for albert_encode).
+ * ids, lengths, B, T, out, hip_stream: as albert_encode (same kernels, same
+ * results bit for bit).
+ * status     dev int32 [1] (caller-owned output): after the request's
+ *            kernels, the device status (ALBERT_OK, ALBERT_E_LENGTH or
+ *            ALBERT_E_ID; on an error `out` is unchanged).
+ * Host-side errors as albert_encode, plus ALBERT_E_SCRATCH (nothing
+ * enqueued) when albert_workspace_bytes(ctx, B, B*T) > ALBERT_SCRATCH_BYTES:
+ * about 3,800 token rows B*T in bf16 (4,300 with FP8 operands, 2,300 in
+ * fp32), e.g. one utterance of up to 512 tokens or 30 of 128.
+ * Every call on one GPU uses that GPU's one scratch, which keeps the last
+ * call's contents (each request sets up what it needs): calls that overlap
+ * on one GPU race, so order them on one stream. */
+int albert_encode_noalloc(albert_ctx* ctx, const int32_t* ids, const int32_t* lengths,
+                          int B, int T, float* out, int32_t* status, void* hip_stream,
+                          unsigned flags);
 
 /* Packed (varlen) batch of n sequences with no padding.
  * This entry point is the library's own (the pages compile one static

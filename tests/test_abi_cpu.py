@@ -152,3 +152,11 @@ def test_binding_refuses_tensors_the_library_would_misread():
         _need(torch.zeros(4, dtype=torch.int32), "ids", torch.int32)
     with pytest.raises(TypeError):
         _need(np.zeros(4, np.int32), "ids", torch.int32)
+
+
+def test_scratch_size_matches_the_header():
+    import albert_transformer_amd as A
+    text = open(HEADER).read()
+    m = re.search(r"#define ALBERT_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == A.SCRATCH_BYTES
+    assert re.search(r"ALBERT_E_SCRATCH = (\d+)", text).group(1) == str(A.E_SCRATCH)
