@@ -184,4 +184,54 @@ __device__ __forceinline__ float gelu_tanh(float x) {
 
 __device__ __forceinline__ float wave_xor(float v, int m) { return __shfl_xor(v, m, 64); }
 
+// 16-byte row pieces of a 32x32 accumulator tile.
+//
+// In the MFMA result layout, lane (l32, hh) holds row l32 of the tile at
+// columns 8q + 4hh + e (q, e = 0..3): four runs of 4 columns, so a store or
+// load of one run covers 8 bytes (bf16) and one instruction touches 32 rows
+// with 16 bytes each.  Lanes l and l + 32 can swap whole runs with
+// v_permlane32_swap (lanes 32..63 of its first operand trade places with
+// lanes 0..31 of its second): after swapping lane l's run q = 1 with lane
+// l + 32's run q = 0 (and likewise runs 3 and 2), lane (l32, hh) holds
+// columns 8hh .. 8hh + 7 and 16 + 8hh .. 16 + 8hh + 7, two 16-byte pieces, so
+// one instruction covers 32 contiguous bytes of each of 32 rows and the
+// tile's traffic takes half the memory instructions.  The same swap maps
+// 16-byte pieces read from memory back to the accumulator layout.
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+// Runs q = 0..3 of a tile row as bf16 pairs (w[q][0] = columns 0-1 of the
+// run, w[q][1] = columns 2-3) -> the lane's two 16-byte pieces (columns
+// 8hh.. and 16 + 8hh..).
+__device__ __forceinline__ void swap_runs_to_pieces(const uint32_t (&w)[4][2], uint4& p0, uint4& p1) {
+  const u32x2 a = __builtin_amdgcn_permlane32_swap(w[0][0], w[1][0], false, false);
+  const u32x2 b = __builtin_amdgcn_permlane32_swap(w[0][1], w[1][1], false, false);
+  const u32x2 c = __builtin_amdgcn_permlane32_swap(w[2][0], w[3][0], false, false);
+  const u32x2 d = __builtin_amdgcn_permlane32_swap(w[2][1], w[3][1], false, false);
+  p0 = uint4{a[0], b[0], a[1], b[1]};
+  p1 = uint4{c[0], d[0], c[1], d[1]};
+}
+
+// The inverse: the lane's two 16-byte pieces of bf16 -> runs q = 0..3 as fp32.
+__device__ __forceinline__ void pieces_to_runs(const uint4& p0, const uint4& p1, f32x4 (&r)[4]) {
+  const u32x2 a = __builtin_amdgcn_permlane32_swap(p0.x, p0.z, false, false);
+  const u32x2 b = __builtin_amdgcn_permlane32_swap(p0.y, p0.w, false, false);
+  const u32x2 c = __builtin_amdgcn_permlane32_swap(p1.x, p1.z, false, false);
+  const u32x2 d = __builtin_amdgcn_permlane32_swap(p1.y, p1.w, false, false);
+  const uint32_t w[4][2] = {{a[0], b[0]}, {a[1], b[1]}, {c[0], d[0]}, {c[1], d[1]}};
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    r[q][0] = __uint_as_float(w[q][0] << 16);
+    r[q][1] = __uint_as_float(w[q][0] & 0xFFFF0000u);
+    r[q][2] = __uint_as_float(w[q][1] << 16);
+    r[q][3] = __uint_as_float(w[q][1] & 0xFFFF0000u);
+  }
+}
+
+// Two fp32 values as one bf16 pair (round to nearest even), low half first.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 p = {(bf16)a, (bf16)b};
+  return __builtin_bit_cast(uint32_t, p);
+}
+
 }  // namespace albert

@@ -169,6 +169,9 @@ gemm_kernel(GemmArgs g) {
   constexpr bool LNE = EPI == EPI_LN || EPI == EPI_LN_ACT || PAIR;  // LayerNorm epilogue
   constexpr bool RES = EPI == EPI_LN || PAIR;              // with a residual
   constexpr bool CONV = EPI == EPI_LN_ACT;                 // convolution taps from shifted rows
+  // bf16 rows are read and written as 16-byte pieces (swap_runs_to_pieces);
+  // E4M3 outputs keep one 4-byte store per run
+  constexpr bool P16 = std::is_same<T, bf16>::value;
   constexpr int kMaxTaps = 7;
   constexpr int NVEC = LNE ? 3 : 1;          // bias (+ LayerNorm gain, shift)
   constexpr int VPT = (BN + NT - 1) / NT;     // vector elements per thread
@@ -492,17 +495,22 @@ gemm_kernel(GemmArgs g) {
       for (int i = 0; i < TM; ++i) {
         const int m = em0 + wm * WTM + i * 32 + l32;
         const int mr = m < M ? m : M - 1;  // rows past M compute on a valid row, never stored
-        const int64_t roff = (int64_t)mr * g.ldr + en0 + wn * WTN + 4 * hh;
+        const int64_t roff = (int64_t)mr * g.ldr + en0 + wn * WTN;
         float s = 0.f;
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
           f32x4 rv[4];  // this column group's residual loads first, then one wait
+          if constexpr (RES && P16) {
+            const T* rp = R + roff + j * 32 + 8 * hh;
+            pieces_to_runs(*reinterpret_cast<const uint4*>(rp), *reinterpret_cast<const uint4*>(rp + 16), rv);
+          } else {
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            if constexpr (RES)
-              rv[q] = TS::load4f(R + roff + j * 32 + 8 * q);
-            else
-              rv[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int q = 0; q < 4; ++q) {
+              if constexpr (RES)
+                rv[q] = TS::load4f(R + roff + j * 32 + 8 * q + 4 * hh);
+              else
+                rv[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
           }
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
@@ -549,6 +557,7 @@ gemm_kernel(GemmArgs g) {
       // handing its half over) the fp32 values before normalisation, into
       // the handoff rows.
       auto store_own = [&](bool raw) __attribute__((always_inline)) {
+        uint32_t pk[4][2];  // P16: one tile row's runs as bf16 pairs
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
           const int m = em0 + wm * WTM + i * 32 + l32;
@@ -572,8 +581,22 @@ gemm_kernel(GemmArgs g) {
                 o[e] = ln_out(acc[i][j][4 * q + e], mean[i], rstd[i], g_s[nl + e], b_s[nl + e]);
                 if constexpr (EPI == EPI_LN_ACT) o[e] = o[e] >= 0.f ? o[e] : o[e] * g.slope;
               }
-              TS::store4(Y + (int64_t)m * g.ldy + en0 + nl, o[0], o[1], o[2], o[3]);
+              if constexpr (P16) {
+                pk[q][0] = pack_bf16x2(o[0], o[1]);
+                pk[q][1] = pack_bf16x2(o[2], o[3]);
+              } else {
+                TS::store4(Y + (int64_t)m * g.ldy + en0 + nl, o[0], o[1], o[2], o[3]);
+              }
               if constexpr (F8) store4_as<T, true>(g.Y8, (int64_t)m * g.ldy8 + en0 + nl, o[0], o[1], o[2], o[3]);
+              if constexpr (P16) {
+                if (q == 3) {
+                  uint4 p0, p1;
+                  swap_runs_to_pieces(pk, p0, p1);
+                  T* yp = Y + (int64_t)m * g.ldy + en0 + wn * WTN + j * 32 + 8 * hh;
+                  *reinterpret_cast<uint4*>(yp) = p0;
+                  *reinterpret_cast<uint4*>(yp + 16) = p1;
+                }
+              }
             }
         }
       };
@@ -759,6 +782,7 @@ gemm_kernel(GemmArgs g) {
           }
       }
     } else {
+      uint32_t pk[4][2];  // P16: one tile row's runs as bf16 pairs
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
         const int m = em0 + wm * WTM + i * 32 + l32;
@@ -780,6 +804,16 @@ gemm_kernel(GemmArgs g) {
             }
             if constexpr (EPI == EPI_OUT) {
               *reinterpret_cast<f32x4*>(g.out + orow * g.N + en0 + nl) = f32x4{o[0], o[1], o[2], o[3]};
+            } else if constexpr (P16 && !F8) {
+              pk[q][0] = pack_bf16x2(o[0], o[1]);
+              pk[q][1] = pack_bf16x2(o[2], o[3]);
+              if (q == 3) {
+                uint4 p0, p1;
+                swap_runs_to_pieces(pk, p0, p1);
+                T* yp = static_cast<T*>(g.Y) + orow * g.ldy + en0 + wn * WTN + j * 32 + 8 * hh;
+                *reinterpret_cast<uint4*>(yp) = p0;
+                *reinterpret_cast<uint4*>(yp + 16) = p1;
+              }
             } else {
               store4_as<T, YF8>(g.Y, orow * g.ldy + en0 + nl, o[0], o[1], o[2], o[3]);
               if constexpr (F8 && EPI == EPI_BIAS) {

@@ -270,17 +270,36 @@ qkv_attention_kernel(QkvAttnArgs a) {
                         });
     }
     lrun += wave_xor(lrun, 32);
-    if (qr < nrows) {
-      const float inv = 1.0f / lrun;
-      const int64_t orow = ((int64_t)r0 + qr) * H + h * D;
+    // (every lane takes part in the swap of 16-byte pieces; only lanes with
+    // a query of the group store)
+    const float inv = qr < nrows ? 1.0f / lrun : 0.f;
+    const int64_t orow = ((int64_t)r0 + qr) * H + h * D;
 #pragma unroll
-      for (int dt = 0; dt < 2; ++dt)
+    for (int dt = 0; dt < 2; ++dt) {
+      if constexpr (F8) {
+        if (qr < nrows) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int d = dt * 32 + 8 * q + 4 * hh;
+            store4_as<bf16, F8>(a.ctx, orow + d, o[dt][4 * q + 0] * inv, o[dt][4 * q + 1] * inv,
+                                o[dt][4 * q + 2] * inv, o[dt][4 * q + 3] * inv);
+          }
+        }
+      } else {
+        uint32_t pk[4][2];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int d = dt * 32 + 8 * q + 4 * hh;
-          store4_as<bf16, F8>(a.ctx, orow + d, o[dt][4 * q + 0] * inv, o[dt][4 * q + 1] * inv,
-                              o[dt][4 * q + 2] * inv, o[dt][4 * q + 3] * inv);
+          pk[q][0] = pack_bf16x2(o[dt][4 * q + 0] * inv, o[dt][4 * q + 1] * inv);
+          pk[q][1] = pack_bf16x2(o[dt][4 * q + 2] * inv, o[dt][4 * q + 3] * inv);
         }
+        uint4 p0, p1;
+        swap_runs_to_pieces(pk, p0, p1);
+        if (qr < nrows) {
+          bf16* cp = static_cast<bf16*>(a.ctx) + orow + dt * 32 + 8 * hh;
+          *reinterpret_cast<uint4*>(cp) = p0;
+          *reinterpret_cast<uint4*>(cp + 16) = p1;
+        }
+      }
     }
   };
 

@@ -86,6 +86,20 @@ def traffic_for(kind: str, config: int):
     return rec["fetch_bytes"] + rec["write_bytes"]
 
 
+def host_cpu() -> dict:
+    """The host the oracle runs on: CPU model and logical CPU count."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu_model": model, "host_cpus": os.cpu_count()}
+
+
 def cpu_baseline(wl, got, budget_s: float, cfg=synth.KOKORO, weights=None, dtype=None):
     """Time the float64 oracle on this host over whole sequences of the same
     workload until `budget_s` seconds have passed; compare the GPU rows."""
@@ -120,7 +134,7 @@ def cpu_baseline(wl, got, budget_s: float, cfg=synth.KOKORO, weights=None, dtype
     dt = time.perf_counter() - t0
     base = {"value": tokens / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{done} of {wl.n_seq} sequences ({tokens} tokens), float64 NumPy/BLAS, "
-                      f"{dt:.1f} s"}
+                      f"{dt:.1f} s", **host_cpu()}
     parity = {"sequences": done, "max_abs": max_abs, "min_token_cosine": min_cos}
     return base, parity
 
@@ -231,13 +245,17 @@ def bench_text(args) -> int:
                           "ms_per_launch": ms / max(n, 1)}
     enc.time_kernel(None)
     dominant = max(per_kind, key=lambda k: per_kind[k]["ms_per_step"])
-    enc.time_kernel(dominant, max_launches=max(per_kind[dominant]["launches_per_step"] * args.steps, 1))
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
+    enc.time_kernel(dominant, max_launches=max(
+        per_kind[dominant]["launches_per_step"] * args.steps * args.batches, 1))
+    batch_s = []
+    for _ in range(args.batches):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            step()
+        torch.cuda.synchronize()
+        batch_s.append(time.perf_counter() - t0)
+    elapsed = float(np.median(batch_s))
     n_dom, ms_dom = enc.kernel_time()
     enc.time_kernel(None)
     if A.read_status(ws) != A.OK:
@@ -270,11 +288,13 @@ def bench_text(args) -> int:
         dt = time.perf_counter() - t0
         base = {"value": tok / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
                 "sample": f"{done} of {wl.n_seq} sequences ({tok} tokens), float64 NumPy, "
-                          f"{dt:.1f} s", "parity_max_abs": worst}
+                          f"{dt:.1f} s", "parity_max_abs": worst, **host_cpu()}
     line = {
         "metric": TEXT_METRIC, "value": round(tokens * args.steps / elapsed, 1),
         "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
+        "ms_per_step": round(ms_step, 4), "batches": args.batches,
+        "ms_per_step_batches": [round(1e3 * t / args.steps, 4) for t in batch_s],
+        "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (seeded text-encoder weights, uniform phoneme ids)",
         "config": {"workload": f"text encoder, {wl.name}", "sequences": wl.n_seq, "T": wl.T,
@@ -307,6 +327,10 @@ def main(argv=None) -> int:
                     help="albert: the phoneme encoder (default); text: the parallel text path")
     ap.add_argument("--groups", type=int, default=1,
                     help="distinct layer weight sets (1 = Kokoro's full sharing)")
+    ap.add_argument("--batches", type=int, default=5,
+                    help="timed batches of --steps steps each; the median is reported")
+    ap.add_argument("--graph", action="store_true",
+                    help="replay the step from a captured HIP graph (launch-bound small batches)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run one plain device copy of this size first (counter scaling)")
     args = ap.parse_args(argv)
@@ -369,22 +393,48 @@ def main(argv=None) -> int:
     enc.time_kernel(None)
     dominant = max(per_kind, key=lambda k: per_kind[k]["ms_per_step"])
 
-    # timed region: K steps, the dominant kernel bracketed by events
-    launches = per_kind[dominant]["launches_per_step"] * args.steps
-    enc.time_kernel(dominant, max_launches=max(launches, 1))
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    n_dom, ms_dom = enc.kernel_time()
-    enc.time_kernel(None)
+    # With --graph the step's whole launch sequence is captured once into a
+    # HIP graph and replayed (small batches are bound by launch overhead).
+    graph = None
+    if args.graph:
+        cap = torch.cuda.Stream()
+        cap.wait_stream(torch.cuda.current_stream())
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(cap):
+            with torch.cuda.graph(graph, stream=cap):
+                step()
+        torch.cuda.synchronize()
+        run_step = graph.replay
+    else:
+        run_step = step
+
+    # timed region: `batches` batches of exactly K steps, each bracketed by a
+    # synchronisation on both sides; the median batch is reported.  The
+    # dominant kernel is bracketed by events in every batch (not in graph
+    # mode, where the per-kind breakdown above stands).
+    batch_s = []
+    n_dom = ms_dom = 0
+    if graph is None:
+        launches = per_kind[dominant]["launches_per_step"] * args.steps * args.batches
+        enc.time_kernel(dominant, max_launches=max(launches, 1))
+    for _ in range(args.batches):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            run_step()
+        torch.cuda.synchronize()
+        batch_s.append(time.perf_counter() - t0)
+    if graph is None:
+        n_dom, ms_dom = enc.kernel_time()
+        enc.time_kernel(None)
+    else:
+        n_dom = per_kind[dominant]["launches_per_step"]
+        ms_dom = per_kind[dominant]["ms_per_step"]
     st = A.read_status(ws)
     if st != A.OK:
         raise SystemExit(f"encoder failed during timing: {A.STATUS_NAMES.get(st, st)}")
 
-    elapsed = t1 - t0
+    elapsed = float(np.median(batch_s))
     ms_step = 1e3 * elapsed / args.steps
     tokens = wl.tokens
     value = tokens * args.steps / elapsed
@@ -408,6 +458,9 @@ def main(argv=None) -> int:
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
+        "batches": args.batches,
+        "ms_per_step_batches": [round(1e3 * t / args.steps, 4) for t in batch_s],
+        "graph": bool(args.graph),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
