@@ -173,10 +173,36 @@ int run(albert_ctx* c, const int32_t* ids, const int32_t* lens_or_cu, int n_seq,
   base.m_ptr = m_ptr;
   base.eps = cf.ln_eps;
 
+  // A product of the request: over K splits for very small batches (the
+  // partial sums in the workspace, then a reduce kernel with the epilogue),
+  // else the one-pass kernels one_pass() launches.
+  float* part = reinterpret_cast<float*>(w + L.part);
+  auto product = [&](auto epi, GemmArgs& ga, int kind, auto&& one_pass) {
+    constexpr int EPI = decltype(epi)::value;
+    const int S = split_factor(max_rows, ga.N, split_slices<T, F8>(ga.K));
+    if (S > 0) {
+      ga.part = part;
+      SplitArgs r{};
+      r.bias = ga.bias; r.Y = ga.Y; r.ldy = ga.ldy; r.Y8 = ga.Y8; r.ldy8 = ga.ldy8;
+      r.R = ga.R; r.ldr = ga.ldr; r.ln_g = ga.ln_g; r.ln_b = ga.ln_b; r.eps = ga.eps;
+      r.out = ga.out; r.row_seq = ga.row_seq; r.row_pos = ga.row_pos; r.out_T = ga.out_T;
+      r.status = status; r.m_ptr = m_ptr;
+      timed(c, kind, s, [&] { launch_split<T, F8, EPI>(ga, r, S, max_rows, c->grid_cap, s); });
+    } else {
+      one_pass();
+    }
+  };
+  using Bias = std::integral_constant<int, EPI_BIAS>;
+  using Gelu = std::integral_constant<int, EPI_GELU>;
+  using Ln = std::integral_constant<int, EPI_LN>;
+  using Out = std::integral_constant<int, EPI_OUT>;
+
   GemmArgs g = base;  // input projection E -> H
   g.X = emb; g.ldx = cf.emb; g.W = c->proj_w; g.wexp = c->proj_e; g.bias = c->proj_b;
   g.Y = X; g.ldy = H; g.Y8 = Y8; g.ldy8 = H; g.N = H; g.K = cf.emb;
-  timed(c, ALBERT_K_PROJ, s, [&] { gemm_big<T, F8, EPI_BIAS>(g, max_rows, c->grid_cap, s); });
+  product(Bias{}, g, ALBERT_K_PROJ, [&] {
+    timed(c, ALBERT_K_PROJ, s, [&] { gemm_big<T, F8, EPI_BIAS>(g, max_rows, c->grid_cap, s); });
+  });
 
   // LayerNorm GEMMs: bf16 rows (bf16 or E4M3 operands) split over two
   // blocks that swap row statistics (full rows in one block otherwise).
@@ -223,14 +249,18 @@ int run(albert_ctx* c, const int32_t* ids, const int32_t* lens_or_cu, int n_seq,
                      S, (int)pairs};
       timed(c, ALBERT_K_QKV_ATTN, s, [&] {
         if constexpr (can_fuse)
-          launch_kernel(qkv_attention_kernel<F8>, dim3((unsigned)((pairs + 7) / 8 * 8)),
+          launch_kernel(qkv_attention_kernel<F8>,  // persistent with bf16 operands
+                        dim3((unsigned)(F8 ? (pairs + 7) / 8 * 8
+                                           : std::min<int64_t>((pairs + 7) / 8 * 8, c->grid_cap))),
                         dim3(512), s, qa);
       });
     } else {
       g = base;  // fused Q|K|V projection
       g.X = X8; g.ldx = H; g.W = lw.qkv_w; g.wexp = lw.qkv_e; g.bias = lw.qkv_b; g.Y = QKV;
       g.ldy = 3 * H; g.N = 3 * H; g.K = H;
-      timed(c, ALBERT_K_QKV, s, [&] { gemm_big<T, F8, EPI_BIAS>(g, max_rows, c->grid_cap, s); });
+      product(Bias{}, g, ALBERT_K_QKV, [&] {
+        timed(c, ALBERT_K_QKV, s, [&] { gemm_big<T, F8, EPI_BIAS>(g, max_rows, c->grid_cap, s); });
+      });
 
       // short sequences on average (many per 128 rows): packed query blocks;
       // otherwise query tiles aligned to each sequence
@@ -245,24 +275,28 @@ int run(albert_ctx* c, const int32_t* ids, const int32_t* lens_or_cu, int n_seq,
     g.X = CTX; g.ldx = H; g.W = lw.o_w; g.wexp = lw.o_e; g.bias = lw.o_b; g.R = X; g.ldr = H;
     g.ln_g = lw.ln1_g; g.ln_b = lw.ln1_b; g.Y = X1; g.ldy = H; g.Y8 = Y18; g.ldy8 = H;
     g.N = H; g.K = H;
-    gemm_layernorm(g, ALBERT_K_ATTN_OUT_LN);
+    product(Ln{}, g, ALBERT_K_ATTN_OUT_LN, [&] { gemm_layernorm(g, ALBERT_K_ATTN_OUT_LN); });
 
     g = base;  // FFN 768 -> 2048 + GELU
     g.X = X18; g.ldx = H; g.W = lw.ffn1_w; g.wexp = lw.ffn1_e; g.bias = lw.ffn1_b; g.Y = G;
     g.ldy = F; g.N = F; g.K = H;
-    timed(c, ALBERT_K_FFN1_GELU, s, [&] { gemm_big<T, F8, EPI_GELU>(g, max_rows, c->grid_cap, s); });
+    product(Gelu{}, g, ALBERT_K_FFN1_GELU, [&] {
+      timed(c, ALBERT_K_FFN1_GELU, s, [&] { gemm_big<T, F8, EPI_GELU>(g, max_rows, c->grid_cap, s); });
+    });
 
     g = base;  // FFN 2048 -> 768 + residual + LayerNorm
     g.X = G; g.ldx = F; g.W = lw.ffn2_w; g.wexp = lw.ffn2_e; g.bias = lw.ffn2_b; g.R = X1;
     g.ldr = H; g.ln_g = lw.ln2_g; g.ln_b = lw.ln2_b; g.Y = X; g.ldy = H; g.Y8 = Y8; g.ldy8 = H;
     g.N = H; g.K = F;
-    gemm_layernorm(g, ALBERT_K_FFN2_LN);
+    product(Ln{}, g, ALBERT_K_FFN2_LN, [&] { gemm_layernorm(g, ALBERT_K_FFN2_LN); });
   }
 
   g = base;  // output projection H -> 512, fp32, into the caller's rows
   g.X = X8; g.ldx = H; g.W = c->out_w; g.wexp = c->out_e; g.bias = c->out_b; g.out = out;
   g.row_seq = row_seq; g.row_pos = row_pos; g.out_T = pad_T; g.N = cf.out_dim; g.K = H;
-  timed(c, ALBERT_K_OUT, s, [&] { gemm_big<T, F8, EPI_OUT>(g, max_rows, c->grid_cap, s); });
+  product(Out{}, g, ALBERT_K_OUT, [&] {
+    timed(c, ALBERT_K_OUT, s, [&] { gemm_big<T, F8, EPI_OUT>(g, max_rows, c->grid_cap, s); });
+  });
   if (pad_T)
     hipLaunchKernelGGL(zero_pad_rows_kernel, dim3(n_seq), dim3(256), 0, s, out, cu, pad_T,
                        cf.out_dim, status);
@@ -358,10 +392,12 @@ int albert_load_weights(albert_ctx** out_ctx, const albert_config* cfg,
       for (int kr = 0; kr < 3; ++kr) {
         ks.push_back(ln_pair_pick<256>(kr));
         ks.push_back(ln_pair_pick<128>(kr));
+        ks.push_back(ln_pair_pick<64>(kr));
       }
-    for (const void* k : ks) {
+    for (size_t i = 0; i < ks.size(); ++i) {
+      const unsigned threads = f8 ? 256 : ln_pair_threads(i % 3 == 2 ? 64 : 128);
       int per_cu = 0;
-      ok = ok && hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, f8 ? 256 : 512, 0) ==
+      ok = ok && hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, ks[i], threads, 0) ==
                      hipSuccess &&
            per_cu >= 1;
     }

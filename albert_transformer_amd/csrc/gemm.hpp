@@ -28,6 +28,11 @@
 //             so the row statistics are identical in both halves
 //   EPI_OUT   store Y as fp32 into the caller's output, packed row m going to
 //             out row seq(m) * T + pos(m) (padded) or m (packed)
+//   EPI_PART  split K: tile (s, m, n) sums K slices [s*K/S, (s+1)*K/S) and
+//             stores the fp32 sum, without bias, at part[s][m][n]; a second
+//             kernel (splitk.hpp) adds the S partial sums in order and applies
+//             the epilogue.  For very small batches, whose tiles would
+//             otherwise occupy a few CUs.
 //
 // Tiling.  A block computes BM token rows x BN output features with WGM x WGN
 // waves; each wave owns a (BM/WGM) x (BN/WGN) sub-tile of 32x32 MFMA tiles.
@@ -72,7 +77,8 @@
 
 namespace albert {
 
-enum Epi { EPI_BIAS = 0, EPI_GELU = 1, EPI_LN = 2, EPI_OUT = 3, EPI_LN_ACT = 4, EPI_LN_PAIR = 5 };
+enum Epi { EPI_BIAS = 0, EPI_GELU = 1, EPI_LN = 2, EPI_OUT = 3, EPI_LN_ACT = 4, EPI_LN_PAIR = 5,
+           EPI_PART = 6 };
 
 struct GemmArgs {
   const void* X;       // [M, K] activations, row stride ldx (elements)
@@ -111,6 +117,10 @@ struct GemmArgs {
   // both halves may try to hand over, and only one of them wins), so that
   // the partner normalises exactly the values the half itself would have
   float* hand;
+  // EPI_PART: S splits of K; partial sums [S][ldp][N] fp32
+  int ksplit;
+  float* part;
+  int64_t ldp;
 };
 
 // LayerNorm output of one value: (v - mean) * rstd * gain + shift, written
@@ -214,7 +224,10 @@ gemm_kernel(GemmArgs g) {
 
   if (*g.status != 0) return;
   const int M = *g.m_ptr;
-  const int ntiles = ((M + BM - 1) / BM) * g.n_tiles;
+  constexpr bool PART = EPI == EPI_PART;
+  const int S = PART ? g.ksplit : 1;
+  const int mn_tiles = ((M + BM - 1) / BM) * g.n_tiles;
+  const int ntiles = mn_tiles * S;
   const int G = gridDim.x;  // the host launches a multiple of 8 blocks (EPI_LN_PAIR: of 16)
   int tile = (blockIdx.x % 8) * (G / 8) + blockIdx.x / 8;
   if (tile >= ntiles) return;
@@ -230,6 +243,8 @@ gemm_kernel(GemmArgs g) {
 
   // ------------------------------------------------------- per-tile state
   int m0 = 0, n0 = 0;
+  int ks0 = 0;  // EPI_PART: this tile's split of K, and its first K element
+  int kbase = 0;
   int xb0 = 0;  // CONV: first input row of the X resource (taps/2 above the tile)
   __amdgpu_buffer_rsrc_t xr, wr;
   int sc[TN];  // F8: E8M0 exponents of this lane's weight rows
@@ -241,6 +256,9 @@ gemm_kernel(GemmArgs g) {
   // each token is one column of the product, and those columns are never
   // stored.
   auto setup = [&](int t) __attribute__((always_inline)) {
+    ks0 = PART ? t / mn_tiles : 0;
+    kbase = PART ? ks0 * (g.K / S) : 0;
+    t = PART ? t % mn_tiles : t;
     m0 = (t / g.n_tiles) * BM;
     n0 = (t % g.n_tiles) * BN;
     xb0 = CONV ? max(m0 - (g.K / (int)g.ldx) / 2, 0) : m0;
@@ -284,6 +302,7 @@ gemm_kernel(GemmArgs g) {
     }
   };
   auto issue = [&](char* buf, int k0) __attribute__((always_inline)) {
+    k0 += kbase;
     int kb = k0 * ES;
     // keep the per-slice offset opaque so the compiler does not precompute
     // (and keep live) every slice's per-instruction offsets
@@ -484,9 +503,25 @@ gemm_kernel(GemmArgs g) {
   // ------------------------------------------------------------ epilogue
   // acc[i][j][4q+e] holds token m0 + wm*WTM + i*32 + l32 and feature
   // n0 + wn*WTN + j*32 + 8q + 4hh + e.
-  auto epilogue = [&](int em0, int en0, int vb) __attribute__((always_inline)) -> bool {
+  auto epilogue = [&](int em0, int en0, int eks, int vb) __attribute__((always_inline)) -> bool {
     const float* __restrict__ bias_s = vecs[vb][0];
-    if constexpr (LNE) {
+    if constexpr (PART) {
+      // runs of 4 fp32 sums: 16-byte stores, 32 bytes of a row per instruction
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const int m = em0 + wm * WTM + i * 32 + l32;
+        if (m >= M) continue;
+        float* prow = g.part + ((int64_t)eks * g.ldp + m) * g.N + en0;
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int nl = wn * WTN + j * 32 + 8 * q + 4 * hh;
+            *reinterpret_cast<f32x4*>(prow + nl) =
+                f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+          }
+      }
+    } else if constexpr (LNE) {
       const float* __restrict__ g_s = vecs[vb][1 % NVEC];
       const float* __restrict__ b_s = vecs[vb][2 % NVEC];
       const int N = g.N;
@@ -833,7 +868,7 @@ gemm_kernel(GemmArgs g) {
   vstore(0);
   prologue();
   int vb = 0;
-  const int KT = g.K / BK;  // KR more than a multiple of STAGES, at least STAGES + KR (host)
+  const int KT = g.K / S / BK;  // KR more than a multiple of STAGES, at least STAGES + KR (host)
   for (;;) {
 #pragma unroll
     for (int i = 0; i < TM; ++i)
@@ -916,7 +951,7 @@ gemm_kernel(GemmArgs g) {
 
     const int next = tile + G;
     const bool more = next < ntiles;
-    const int em0 = m0, en0 = n0;
+    const int em0 = m0, en0 = n0, eks = ks0;
     if (more) {
       setup(next);
       conv_offsets();
@@ -926,7 +961,7 @@ gemm_kernel(GemmArgs g) {
     // the MFMAs above), so the next tile's first slices may land there
     asm volatile("s_barrier" ::: "memory");
     if (more) prologue();
-    if (!epilogue(em0, en0, vb)) {
+    if (!epilogue(em0, en0, eks, vb)) {
       // EPI_LN_PAIR: the partner never delivered its statistics; report it
       // and stop (nothing of this tile is stored)
       if (tid == 0) __hip_atomic_store(const_cast<int*>(g.status), kStatusSync, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

@@ -113,14 +113,38 @@ inline int e4m3_row_exp(const float* row, int64_t n, float scale) {
 }
 
 // Exchange words the paired LayerNorm launches need for up to max_rows rows:
-// 4*BM + 8 per row tile, for either tile height (128 or 256 rows).
+// 4*BM + 8 per row tile, for any tile height (64, 128 or 256 rows).
 inline size_t ln_pair_words(int64_t max_rows) {
-  return (size_t)std::max((max_rows + 127) / 128 * (4 * 128 + 8), (max_rows + 255) / 256 * (4 * 256 + 8));
+  return (size_t)std::max({(max_rows + 63) / 64 * (4 * 64 + 8), (max_rows + 127) / 128 * (4 * 128 + 8),
+                           (max_rows + 255) / 256 * (4 * 256 + 8)});
+}
+
+// Split K (very small batches): requests of at most kSplitRows token rows
+// (one utterance, or a few short ones) run their products as S partial
+// products over 64-row tiles, whose fp32 partial sums [S][rows][N] take at
+// most kSplitRows x kSplitCols x 4 bytes of the workspace.  S depends on the
+// product alone (never on the batch), so two requests in this regime give
+// every row the same bits, padded or packed.
+constexpr int64_t kSplitRows = 256;
+constexpr int64_t kSplitCols = 32768;  // S x N
+
+// Splits of K for a product of max_rows x N x K over 64 x 256 tiles whose K
+// slices number kslices, or 0 for the one-pass product: the largest S of a
+// fixed ladder that divides the slices into an even number (at least 2) per
+// split, with S x N <= kSplitCols.
+inline int split_factor(int64_t max_rows, int N, int kslices) {
+  if (max_rows > kSplitRows || N % 256 != 0) return 0;
+  int best = 0;
+  for (int S : {2, 3, 4, 6, 8, 12, 16}) {
+    if (kslices % S != 0 || (kslices / S) % 2 != 0 || (int64_t)S * N > kSplitCols) continue;
+    best = S;
+  }
+  return best;
 }
 
 // Byte offsets of a request's buffers in its workspace.
 struct Layout {
-  size_t status, cu, groups, row_seq, row_pos, emb, x, x1, x8, x18, qkv, ctx, g, xch, hand, total;
+  size_t status, cu, groups, row_seq, row_pos, emb, x, x1, x8, x18, qkv, ctx, g, xch, hand, part, total;
   int64_t rows_cap;
 };
 
@@ -153,6 +177,8 @@ inline Layout plan(const albert_config& cfg, int dtype, int n_seq, int64_t max_r
   // fp32 values a LayerNorm half hands to its partner (per row, a slot for
   // each half)
   L.hand = off; off += dtype != ALBERT_F32 ? align_up((size_t)rows * H * 4, kAlign) : 0;
+  // partial sums of split-K products (very small batches)
+  L.part = off; off += rows <= kSplitRows ? (size_t)rows * kSplitCols * 4 : 0;
   // the fused kernel's sequence groups (last: the activations keep the
   // offsets they have without it)
   L.groups = off; off += align_up((size_t)(n_seq + 2) * 4, kAlign);

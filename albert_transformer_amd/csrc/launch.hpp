@@ -11,6 +11,7 @@
 
 #include "gemm.hpp"
 #include "host.hpp"
+#include "splitk.hpp"
 
 namespace albert {
 
@@ -41,6 +42,36 @@ void launch_gemm(GemmArgs g, int64_t max_rows, int grid_cap, hipStream_t s) {
   const int64_t grid = std::min<int64_t>((tiles + 7) / 8 * 8, grid_cap);
   launch_kernel(gemm_kernel<T, F8, BM, BN, WGM, WGN, RB, STAGES, EPI, DEFER, KR>,
                 dim3((unsigned)grid), dim3(WGM * WGN * 64), s, g);
+}
+
+// Split-K product for very small batches (split_factor() > 0): S partial
+// products over 64 x 256 tiles of 4 waves (one per SIMD), walked by at most
+// grid_cap workgroups, then the reduce kernel with the product's epilogue.
+// A caller timing the launch gets the start of the first kernel and the end
+// of the second.
+template <typename T, bool F8, int EPI>
+void launch_split(GemmArgs g, SplitArgs r, int S, int64_t max_rows, int grid_cap, hipStream_t s) {
+  constexpr int RB = F8 ? 64 : 128;
+  g.ksplit = S;
+  g.ldp = max_rows;
+  g.n_tiles = g.N / 256;
+  r.part = g.part;
+  r.S = S;
+  r.ldp = max_rows;
+  r.N = g.N;
+  const int64_t tiles = (max_rows + 63) / 64 * g.n_tiles * S;
+  const int64_t grid = std::min<int64_t>((tiles + 7) / 8 * 8, grid_cap);
+  const LaunchEvents ev = g_launch_events;
+  g_launch_events = LaunchEvents{};
+  hipExtLaunchKernelGGL(gemm_kernel<T, F8, 64, 256, 1, 4, RB, 2, EPI_PART, false>, dim3((unsigned)grid),
+                        dim3(256), 0, s, ev.start, nullptr, 0, g);
+  hipExtLaunchKernelGGL(splitk_reduce_kernel<T, F8, EPI>, dim3((unsigned)max_rows), dim3(256), 0, s,
+                        nullptr, ev.stop, 0, r);
+}
+// K slices of the split-K tile for a product of depth K
+template <typename T, bool F8>
+constexpr int split_slices(int K) {
+  return F8 ? K / 64 : K * (int)sizeof(T) / 128;
 }
 
 // Large tiles for plain and GELU epilogues; full-row tiles for LayerNorm.
@@ -125,7 +156,10 @@ void gemm_ln(GemmArgs g, int64_t max_rows, int grid_cap, hipStream_t s) {
 // its own g.xtag.
 template <int BM, int KR>
 constexpr auto ln_pair_kernel =
-    gemm_kernel<bf16, false, BM, 384, BM / 64, 8 / (BM / 64), 64, 3, EPI_LN_PAIR, false, KR>;
+    gemm_kernel<bf16, false, BM, 384, BM == 64 ? 1 : BM / 64, BM == 64 ? 4 : 8 / (BM / 64), 64, 3,
+                EPI_LN_PAIR, false, KR>;
+// threads of the bf16 pair kernel with BM-row tiles
+constexpr unsigned ln_pair_threads(int BM) { return BM == 64 ? 256 : 512; }
 constexpr auto ln_pair_kernel_f8 = gemm_kernel<bf16, true, 128, 384, 2, 2, 64, 2, EPI_LN_PAIR, false, 0>;
 template <int BM>
 inline const void* ln_pair_pick(int kr) {
@@ -137,8 +171,14 @@ inline const void* ln_pair_pick(int kr) {
 // (each poll is a device-scope load plus a short sleep, about a
 // microsecond: the halves of a tile normally finish within a few).
 constexpr int kPairPolls = 64;
+// Tile height: the tallest whose tiles (two per row tile) fill grid_cap
+// CUs; 64-row tiles (4 waves of 64 x 96) below that: smaller batches spread
+// over more CUs.
 inline int ln_pair_rows(int64_t max_rows, int grid_cap, bool f8) {
-  return !f8 && (max_rows + 255) / 256 * 2 >= grid_cap ? 256 : 128;
+  if (f8) return 128;
+  if ((max_rows + 255) / 256 * 2 >= grid_cap) return 256;
+  if ((max_rows + 127) / 128 * 2 >= grid_cap) return 128;
+  return 64;
 }
 // K the pair kernels accept: bf16, whole 32-deep slices, at least 3 + 2 of
 // them; E4M3, an even number of 64-deep slices
@@ -153,8 +193,9 @@ inline hipError_t gemm_ln_pair(GemmArgs g, int64_t max_rows, int grid_cap, hipSt
   const int64_t tiles = (max_rows + BM - 1) / BM * 2;
   const int64_t grid = std::min<int64_t>((tiles + 15) / 16 * 16, grid_cap / 16 * 16);
   const void* k = F8 ? reinterpret_cast<const void*>(ln_pair_kernel_f8)
-                     : BM == 256 ? ln_pair_pick<256>((g.K / 32) % 3) : ln_pair_pick<128>((g.K / 32) % 3);
-  const unsigned threads = F8 ? 256 : 512;
+                     : BM == 256 ? ln_pair_pick<256>((g.K / 32) % 3)
+                     : BM == 128 ? ln_pair_pick<128>((g.K / 32) % 3) : ln_pair_pick<64>((g.K / 32) % 3);
+  const unsigned threads = F8 ? 256 : ln_pair_threads(BM);
   const LaunchEvents ev = g_launch_events;
   g_launch_events = LaunchEvents{};
   void* args[] = {&g};

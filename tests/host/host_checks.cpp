@@ -112,7 +112,8 @@ static void check_plan() {
             {L.x8, f8 ? (size_t)R * c.hidden : 0}, {L.x18, f8 ? (size_t)R * c.hidden : 0},
             {L.qkv, (size_t)R * 3 * c.hidden * es}, {L.ctx, (size_t)R * c.hidden * eo},
             {L.g, (size_t)R * c.ffn * eo}, {L.xch, pair ? ln_pair_words(R) * 8 : 0},
-            {L.hand, pair ? (size_t)R * c.hidden * 4 : 0}, {L.groups, (size_t)(n + 2) * 4}};
+            {L.hand, pair ? (size_t)R * c.hidden * 4 : 0}, {L.groups, (size_t)(n + 2) * 4},
+            {L.part, R <= kSplitRows ? (size_t)R * kSplitCols * 4 : 0}};
         for (size_t i = 0; i < bufs.size(); ++i) {
           CHECK(bufs[i].off % 256 == 0);
           CHECK(bufs[i].off + bufs[i].bytes <= L.total);
@@ -121,6 +122,23 @@ static void check_plan() {
                   bufs[i].off + bufs[i].bytes <= bufs[j].off || bufs[j].off + bufs[j].bytes <= bufs[i].off);
         }
       }
+}
+
+static void check_split_factor() {
+  // every split leaves whole, even slice counts within the partial-sum bytes,
+  // and depends on the product only
+  for (int N : {512, 768, 2048, 2304})
+    for (int ks : {4, 12, 24, 32, 64}) {
+      const int S = split_factor(36, N, ks);
+      for (int64_t rows : {(int64_t)1, (int64_t)200, (int64_t)256})
+        CHECK(split_factor(rows, N, ks) == S);
+      CHECK(split_factor(257, N, ks) == 0 && split_factor(32768, N, ks) == 0);
+      if (S == 0) continue;
+      CHECK(S >= 2 && ks % S == 0 && (ks / S) % 2 == 0 && (int64_t)S * N <= kSplitCols);
+    }
+  CHECK(split_factor(36, 768, 64) == 16);   // fp32 2048-deep: 16 splits of 4 slices
+  CHECK(split_factor(36, 2304, 24) == 12);  // fp32 Q|K|V: 12 splits of 2 slices
+  CHECK(split_factor(36, 2048, 12) == 6);   // bf16 FFN1: 6 splits of 2 slices
 }
 
 static void check_overlaps() {
@@ -253,6 +271,7 @@ int main() {
   check_e4m3();
   check_bf16();
   check_plan();
+  check_split_factor();
   check_overlaps();
   for (int dtype : {ALBERT_F32, ALBERT_BF16, ALBERT_FP8})
     for (int G : {1, 3}) check_image(G, dtype);

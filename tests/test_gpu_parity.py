@@ -174,28 +174,39 @@ def test_packed_equals_padded_bitwise():
 
 def test_pad_slots_and_more_padding_do_not_change_real_tokens():
     """Pad-slot contents never matter (bit for bit).  More padding (a larger
-    T) is bit-for-bit invisible to the separate Q|K|V and attention kernels;
-    the fused kernel groups 256 // T sequences per tile, so a larger T can
-    regroup them and reorder the softmax's rounding: there the outputs agree
-    to the bf16 tolerance."""
+    T) is bit-for-bit invisible to the separate Q|K|V and attention kernels
+    as long as the request stays on the same side of the split-K boundary
+    (at most 256 token rows B*T: products split over K; more: one pass),
+    which changes the products' summation order: across it the outputs agree
+    to the bf16 tolerance.  The fused kernel groups 256 // T sequences per
+    tile, so a larger T can regroup them and reorder the softmax's rounding:
+    there the outputs agree to the bf16 tolerance as well."""
     import albert_transformer_amd as A
     enc = encoder("bf16")
-    wl = synth.random_padded(36, B=3, T=64, lo=5, hi=60)
-    wl2 = synth.Workload(wl.name, wl.dtype, wl.ids.copy(), wl.lengths, wl.T)
-    for b, L in enumerate(wl.lengths):
-        wl2.ids[b, L:] = 999  # pad slots are never read, even out of range
-    ids3 = np.concatenate([wl.ids, np.zeros((3, 100), np.int32)], axis=1)
-    wl3 = synth.Workload(wl.name, wl.dtype, ids3, wl.lengths, 164)
-    for flags in (0, A.UNFUSED):
-        a, _ = _run_padded(enc, wl, flags)
-        b_, _ = _run_padded(enc, wl2, flags)
-        c, _ = _run_padded(enc, wl3, flags)
+    for B, T, T_more, T_split in ((3, 64, 164, 80), (5, 64, 164, None)):
+        wl = synth.random_padded(36, B=B, T=T, lo=5, hi=60)
+        wl2 = synth.Workload(wl.name, wl.dtype, wl.ids.copy(), wl.lengths, wl.T)
         for b, L in enumerate(wl.lengths):
-            assert np.array_equal(a[b, :L], b_[b, :L])
-            if flags:
-                assert np.array_equal(a[b, :L], c[b, :L])
-            else:
-                check(c[b, :L], a[b, :L], "bf16", f"T=164 vs T=64 seq{b}")
+            wl2.ids[b, L:] = 999  # pad slots are never read, even out of range
+        more = []
+        for T2 in (T_more, T_split):
+            if T2 is None:
+                continue
+            ids3 = np.concatenate([wl.ids, np.zeros((B, T2 - T), np.int32)], axis=1)
+            more.append(synth.Workload(wl.name, wl.dtype, ids3, wl.lengths, T2))
+        for flags in (0, A.UNFUSED):
+            a, _ = _run_padded(enc, wl, flags)
+            b_, _ = _run_padded(enc, wl2, flags)
+            for b, L in enumerate(wl.lengths):
+                assert np.array_equal(a[b, :L], b_[b, :L])
+            for wl3 in more:
+                c, _ = _run_padded(enc, wl3, flags)
+                same_side = (B * T <= 256) == (B * wl3.T <= 256)
+                for b, L in enumerate(wl.lengths):
+                    if flags and same_side:
+                        assert np.array_equal(a[b, :L], c[b, :L]), (B, wl3.T, b)
+                    else:
+                        check(c[b, :L], a[b, :L], "bf16", f"T={wl3.T} vs T={T} seq{b}")
 
 
 def test_determinism_and_no_carry_over():
@@ -526,3 +537,29 @@ def test_poisoned_workspace_ragged_tail(flags_name):
             a, b = int(cu[s]), int(cu[s + 1])
             check(got[a:b], oracle.encode_sequence(ids[a:b], W, K), "bf16",
                   f"poisoned workspace {flags_name} seq{s}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_tiny_batches_split_k(dtype):
+    """Requests of at most 256 token rows run their products split over K
+    (partial sums, then a reduce kernel with the epilogue).  The split depends
+    on the product only, so padded and packed give the same bits there too,
+    and the outputs match the oracle (one utterance of 36 tokens, and three
+    short sequences padded to 80)."""
+    import torch
+    enc = encoder(dtype)
+    W = oracle_weights(dtype)
+    for seed, B, T in ((140, 1, 36), (141, 3, 80)):
+        wl = synth.random_padded(seed, B=B, T=T, lo=1, hi=T)
+        wl.lengths[0] = T
+        out_pad, _ = _run_padded(enc, wl)
+        packed = np.concatenate([wl.ids[b, :L] for b, L in enumerate(wl.lengths)]).astype(np.int32)
+        cu = np.concatenate([[0], np.cumsum(wl.lengths)]).astype(np.int32)
+        out = torch.empty((int(cu[-1]), K.out_dim), device="cuda")
+        ws = enc.new_workspace(B, int(cu[-1]))
+        assert enc.encode_varlen_raw(dev(packed), dev(cu), T, out, ws) == 0
+        got = out.cpu().numpy()
+        for b, L in enumerate(wl.lengths):
+            assert np.array_equal(got[cu[b]:cu[b + 1]], out_pad[b, :L].astype(np.float32)), (seed, b)
+            check(out_pad[b, :L], oracle.encode_sequence(wl.ids[b, :L], W, K), dtype,
+                  f"split-K B={B} T={T} seq{b}")
