@@ -199,7 +199,10 @@ gemm_kernel(GemmArgs g) {
   // Deferred stores: bf16 (or E4M3) outputs of tile i are kept in registers
   // and written in NB batches of SB stores during the first NB K-slices of
   // tile i+1.
-  constexpr int NST = TM * TN * 4;            // 8- (4-) byte stores per lane per tile
+  // bf16 outputs are held as 16-byte pieces (swap_runs_to_pieces, two per
+  // 32x32 tile); E4M3 outputs as one 4-byte word per run of 4
+  constexpr bool DP16 = DEFER && !YF8;
+  constexpr int NST = TM * TN * (DP16 ? 2 : 4);  // stores per lane per tile
   constexpr int NB = 8, SB = NST / NB;
   constexpr int HW = YF8 ? 1 : 2;             // 32-bit words per store
   static_assert(!DEFER || (std::is_same<T, bf16>::value && STAGES == 2 &&
@@ -378,12 +381,18 @@ gemm_kernel(GemmArgs g) {
   // they belong to (rows at or past M fall outside it and are dropped by the
   // hardware range check, so every batch issues the same number of stores),
   // and per-row byte offsets.  Before the first tile the resource is empty.
-  uint32_t held[DEFER ? TM : 1][DEFER ? TN : 1][4][HW];
+  uint32_t held[DEFER && !DP16 ? TM : 1][DEFER && !DP16 ? TN : 1][4][HW];
+  uint4 hp[DP16 ? TM : 1][DP16 ? TN : 1][2];
   __amdgpu_buffer_rsrc_t yr = __builtin_amdgcn_make_buffer_rsrc(g.Y, (short)0, 0, kRsrcWord3);
   int hoff[TM];
 #pragma unroll
   for (int i = 0; i < TM; ++i) hoff[i] = 0;
-  if constexpr (DEFER) {
+  if constexpr (DP16) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) hp[i][j][0] = hp[i][j][1] = uint4{0u, 0u, 0u, 0u};
+  } else if constexpr (DEFER) {
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -395,7 +404,18 @@ gemm_kernel(GemmArgs g) {
   }
   // batch b: token tile i = b / (NB/TM), column tiles j in [jb, jb + TN/(NB/TM))
   auto store_batch = [&](int b) __attribute__((always_inline)) {
-    if constexpr (DEFER) {
+    if constexpr (DP16) {
+      constexpr int JPB = TN / (NB / TM);
+      const int i = b / (NB / TM), jb = (b % (NB / TM)) * JPB;
+      typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+#pragma unroll
+      for (int jj = 0; jj < JPB; ++jj) {
+        const int off = hoff[i] + (jb + jj) * 32 * YES;
+        const uint4 a = hp[i][jb + jj][0], c = hp[i][jb + jj][1];
+        __builtin_amdgcn_raw_buffer_store_b128(u32x4{a.x, a.y, a.z, a.w}, yr, off, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(u32x4{c.x, c.y, c.z, c.w}, yr, off + 16 * YES, 0, 0);
+      }
+    } else if constexpr (DEFER) {
       constexpr int JPB = TN / (NB / TM);
       const int i = b / (NB / TM), jb = (b % (NB / TM)) * JPB;
 #pragma unroll
@@ -794,9 +814,10 @@ gemm_kernel(GemmArgs g) {
           __builtin_amdgcn_readfirstlane((int)(ybytes > 0x7fffffff ? 0x7fffffff : ybytes)), kRsrcWord3);
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
-        hoff[i] = ((wm * WTM + i * 32 + l32) * (int)g.ldy + wn * WTN + 4 * hh) * YES;
+        hoff[i] = ((wm * WTM + i * 32 + l32) * (int)g.ldy + wn * WTN + (DP16 ? 8 : 4) * hh) * YES;
 #pragma unroll
-        for (int j = 0; j < TN; ++j)
+        for (int j = 0; j < TN; ++j) {
+          uint32_t pk[4][2];  // DP16: the tile row's runs as bf16 pairs
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const int nl = wn * WTN + j * 32 + 8 * q + 4 * hh;
@@ -806,15 +827,15 @@ gemm_kernel(GemmArgs g) {
               o[e] = acc[i][j][4 * q + e] + bias_s[nl + e];
               if constexpr (EPI == EPI_GELU) o[e] = gelu_tanh(o[e]);
             }
-            if constexpr (YF8) {
-              held[i][j][q][0] = pack_e4m3x4(o[0], o[1], o[2], o[3]);
+            if constexpr (DP16) {
+              pk[q][0] = pack_bf16x2(o[0], o[1]);
+              pk[q][1] = pack_bf16x2(o[2], o[3]);
             } else {
-              typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-              bf16x2 p0 = {(bf16)o[0], (bf16)o[1]}, p1 = {(bf16)o[2], (bf16)o[3]};
-              held[i][j][q][0] = __builtin_bit_cast(uint32_t, p0);
-              held[i][j][q][HW - 1] = __builtin_bit_cast(uint32_t, p1);
+              held[i][j][q][0] = pack_e4m3x4(o[0], o[1], o[2], o[3]);
             }
           }
+          if constexpr (DP16) swap_runs_to_pieces(pk, hp[i][j][0], hp[i][j][1]);
+        }
       }
     } else {
       uint32_t pk[4][2];  // P16: one tile row's runs as bf16 pairs
