@@ -205,6 +205,21 @@ gemm_kernel(GemmArgs g) {
   constexpr int NST = TM * TN * (DP16 ? 2 : 4);  // stores per lane per tile
   constexpr int NB = 8, SB = NST / NB;
   constexpr int HW = YF8 ? 1 : 2;             // 32-bit words per store
+  // LayerNorm residual rows by LDS DMA (bf16 storage): between the K loop
+  // and the next tile's prologue the staging buffers are free, and each wave
+  // loads its own 16-byte residual pieces into a private region of them (one
+  // 1 KB instruction per 32-column tile and piece, each lane's piece at its
+  // own slot) and reads back its own slots.  So every residual load of the
+  // region is in flight at once and holds no registers while it is; loaded
+  // into registers, the compiler (at its register limit with the LayerNorm
+  // tile's accumulators) waited for each 16 bytes in turn.  Both 32-row
+  // halves of a wave's rows at once when the regions fit, else one half
+  // after the other.
+  constexpr int RWB = TN * 2 * 1024;                       // one half's pieces per wave
+  constexpr bool RBOTH = STAGE / (TM * RWB) >= 1 && NW <= STAGES * (STAGE / (TM * RWB));
+  constexpr int RREG = RBOTH ? TM * RWB : RWB;             // bytes of a wave's region
+  constexpr int WPA = STAGE / RREG;                        // regions per staging buffer
+  constexpr bool RDMA = RES && P16 && WPA >= 1 && NW <= STAGES * WPA;
   static_assert(!DEFER || (std::is_same<T, bf16>::value && STAGES == 2 &&
                            (EPI == EPI_BIAS || EPI == EPI_GELU) && NST % NB == 0 &&
                            SB <= 63 && TN % (NB / TM) == 0),
@@ -498,14 +513,29 @@ gemm_kernel(GemmArgs g) {
         } else {
           ld(j, 0);
         }
+        if constexpr (PF == 1 && LNE) {
+          // LayerNorm tiles (six weight fragments a step): every read of the
+          // step first, then its MFMAs weight tile by weight tile, so that
+          // one LDS latency per step is exposed instead of one per MFMA
+          // (3 % on FFN2+LN; the bias/GELU tiles do better alternating)
+          __builtin_amdgcn_sched_group_barrier(0x100, TM + TN, 0);
 #pragma unroll
-        for (int i = 0; i < TM; ++i)
+          for (int jj = 0; jj < TN; ++jj)
 #pragma unroll
-          for (int jj = 0; jj < TN; ++jj) {
-            TR::mma(acc[i][jj], fw[j % PF][jj], fx[j % PF][i]);
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // then one LDS read
-          }
+            for (int i = 0; i < TM; ++i) {
+              TR::mma(acc[i][jj], fw[0][jj], fx[0][i]);
+              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            }
+        } else {
+#pragma unroll
+          for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int jj = 0; jj < TN; ++jj) {
+              TR::mma(acc[i][jj], fw[j % PF][jj], fx[j % PF][i]);
+              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+              __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // then one LDS read
+            }
+        }
       }
     }
   };
@@ -523,7 +553,8 @@ gemm_kernel(GemmArgs g) {
   // ------------------------------------------------------------ epilogue
   // acc[i][j][4q+e] holds token m0 + wm*WTM + i*32 + l32 and feature
   // n0 + wn*WTN + j*32 + 8q + 4hh + e.
-  auto epilogue = [&](int em0, int en0, int eks, int vb) __attribute__((always_inline)) -> bool {
+  auto epilogue = [&](int em0, int en0, int eks, int vb, auto&& next_prologue)
+                      __attribute__((always_inline)) -> bool {
     const float* __restrict__ bias_s = vecs[vb][0];
     if constexpr (PART) {
       // runs of 4 fp32 sums: 16-byte stores, 32 bytes of a row per instruction
@@ -546,16 +577,55 @@ gemm_kernel(GemmArgs g) {
       const float* __restrict__ b_s = vecs[vb][2 % NVEC];
       const int N = g.N;
       const T* __restrict__ R = static_cast<const T*>(g.R);
+      // RDMA: this wave's region, and the DMA of the residual pieces of its
+      // rows of half i (rows past M read row M - 1: computed, never stored)
+      char* rreg = nullptr;
+      __amdgpu_buffer_rsrc_t rr;
+      auto res_issue = [&](int i) __attribute__((always_inline)) {
+        if constexpr (RDMA) {
+          const int m = em0 + wm * WTM + i * 32 + l32;
+          const int mr = m < M ? m : M - 1;
+          const int vo = ((mr - em0) * (int)g.ldr + wn * WTN + 8 * hh) * (int)sizeof(T);
+          char* dst = rreg + (RBOTH ? i * RWB : 0);
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int pc = 0; pc < 2; ++pc)
+              __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, (lds_ptr_t*)(dst + (2 * j + pc) * 1024), 16, vo,
+                                                       (j * 32 + pc * 16) * (int)sizeof(T), 0, 0);
+        }
+      };
+      if constexpr (RDMA) {
+        const int a = wave / WPA;
+        rreg = (a == 0 ? lds0 : a == 1 ? lds1 : a == 2 ? lds2 : lds3) + (wave % WPA) * RREG;
+        const int64_t rbytes = ((int64_t)(M - em0) * g.ldr - en0) * (int64_t)sizeof(T);
+        rr = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<T*>(R + (int64_t)em0 * g.ldr + en0), (short)0,
+            __builtin_amdgcn_readfirstlane((int)(rbytes > 0x7fffffff ? 0x7fffffff : rbytes)), kRsrcWord3);
+#pragma unroll
+        for (int i = 0; i < (RBOTH ? TM : 1); ++i) res_issue(i);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's pieces have landed
+      }
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
         const int m = em0 + wm * WTM + i * 32 + l32;
         const int mr = m < M ? m : M - 1;  // rows past M compute on a valid row, never stored
         const int64_t roff = (int64_t)mr * g.ldr + en0 + wn * WTN;
         float s = 0.f;
+        if constexpr (RDMA && !RBOTH) {
+          if (i > 0) {  // the region's previous half has been read
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            res_issue(i);
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+          }
+        }
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
           f32x4 rv[4];  // this column group's residual loads first, then one wait
-          if constexpr (RES && P16) {
+          if constexpr (RDMA) {
+            const char* sp = rreg + (RBOTH ? i * RWB : 0) + 2 * j * 1024 + lane * 16;
+            pieces_to_runs(*reinterpret_cast<const uint4*>(sp), *reinterpret_cast<const uint4*>(sp + 1024), rv);
+          } else if constexpr (RES && P16) {
             const T* rp = R + roff + j * 32 + 8 * hh;
             pieces_to_runs(*reinterpret_cast<const uint4*>(rp), *reinterpret_cast<const uint4*>(rp + 16), rv);
           } else {
@@ -582,6 +652,9 @@ gemm_kernel(GemmArgs g) {
         if (hh == 0) red[wn * BM + wm * WTM + i * 32 + l32] = s;
       }
       asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      // every wave has read its residual region: the next tile's first
+      // slices may land in the staging buffers
+      if constexpr (RDMA) next_prologue();
       constexpr float inv_cols = 1.0f / (PAIR ? BN : 1);  // the block's share of the row (PAIR)
       constexpr int R2 = PAIR ? WGN * BM : 0;             // where the squared deviations go
       float mean[TM], rstd[TM];
@@ -981,8 +1054,13 @@ gemm_kernel(GemmArgs g) {
     // every wave has finished reading the staging buffers (their reads fed
     // the MFMAs above), so the next tile's first slices may land there
     asm volatile("s_barrier" ::: "memory");
-    if (more) prologue();
-    if (!epilogue(em0, en0, eks, vb)) {
+    auto next_prologue = [&]() __attribute__((always_inline)) {
+      if (more) prologue();
+    };
+    // (the LayerNorm epilogue reading its residual through the staging
+    // buffers issues the prologue itself, once it has read them)
+    if constexpr (!RDMA) next_prologue();
+    if (!epilogue(em0, en0, eks, vb, next_prologue)) {
       // EPI_LN_PAIR: the partner never delivered its statistics; report it
       // and stop (nothing of this tile is stored)
       if (tid == 0) __hip_atomic_store(const_cast<int*>(g.status), kStatusSync, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
