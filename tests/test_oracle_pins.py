@@ -716,6 +716,68 @@ def test_fp8_checker_catches_qkv_rounded_to_e4m3(monkeypatch, index):
     assert _fp8_run(monkeypatch, _skip_call("fp8_store", index, oracle.e4m3_round)) != []
 
 
+def _fp8_full_depth(x, lengths, mutate=None):
+    """Full-depth FP8 outputs of the sequences of x (rows cut by lengths),
+    with the oracle's two rounding hooks optionally replaced."""
+    from oracle import albert_oracle as ao
+    W8 = _w64(dtype="fp8")
+    cu = np.concatenate([[0], np.cumsum(lengths)])
+    out = []
+    for s in range(len(lengths)):
+        saved = ao.fp8_operand, ao.fp8_store
+        if mutate is not None:
+            ao.fp8_operand, ao.fp8_store = mutate(ao)
+        try:
+            out.append(ao.encode_fp8_features(x[cu[s]:cu[s + 1]], W8, K))
+        finally:
+            ao.fp8_operand, ao.fp8_store = saved
+    return out
+
+
+def _deviation(a, b):
+    d = np.concatenate([p - q for p, q in zip(a, b)])
+    A, B = np.concatenate(a), np.concatenate(b)
+    cos = np.sum(A * B, 1) / (np.linalg.norm(A, axis=1) * np.linalg.norm(B, axis=1))
+    return float(np.abs(d).max()), float(np.sqrt(np.mean(d * d))), float(cos.min())
+
+
+def test_fp8_full_depth_noise_floor():
+    """Why the full-depth FP8 bound of the GPU tests is what it is.
+
+    Perturbing every rounding input of the FP8 emulation by a relative
+    2^-22 (the size of an fp32 accumulation-order difference) flips some
+    E4M3 codes, and over 12 executions the flips grow to a floor: max |err|
+    about 0.1, RMS about 0.02, per-token cosine about 0.999.  The GPU bound
+    (max |err| <= 0.2, cosine >= 0.997) is about twice that floor.  The
+    floor also swallows a misplaced rounding: dropping every E4M3 operand
+    rounding after the projection moves the output no further than the
+    perturbation does, so full depth cannot tell rounding placements apart;
+    the one-execution stage checks (codes exact up to near-ties) and the
+    storage-point checks above are what pin the placement."""
+    rng = np.random.default_rng(9)
+    lengths = [128, 64, 1]
+    x = rng.normal(0, 1, (sum(lengths), 128))
+    ref = _fp8_full_depth(x, lengths)
+    prng = np.random.default_rng(1)
+
+    def perturb(ao):
+        def wrap(f):
+            return lambda v: f(np.asarray(v, np.float64) * (1 + 2.0 ** -22 * prng.uniform(-1, 1, np.shape(v))))
+        return wrap(ao.e4m3_round), wrap(ao._bf16_of)
+    mx, rms, cos = _deviation(_fp8_full_depth(x, lengths, perturb), ref)
+    assert 0.02 < mx <= 0.12 and 0.005 < rms <= 0.04 and cos >= 0.998, (mx, rms, cos)
+
+    def no_operand_rounding(ao):
+        n = [0]
+
+        def op(v):
+            n[0] += 1
+            return ao.e4m3_round(v) if n[0] <= 2 else np.asarray(v, np.float64)
+        return op, ao._bf16_of
+    mx2, rms2, cos2 = _deviation(_fp8_full_depth(x, lengths, no_operand_rounding), ref)
+    assert rms2 <= 2 * rms and mx2 <= 0.2 and cos2 >= 0.997, (mx2, rms2, cos2)
+
+
 @pytest.mark.parametrize("G", (1, 3))
 def test_prepare_weights_role_rule(G):
     """bf16 storage rounds exactly the three tables and eight weight matrices
