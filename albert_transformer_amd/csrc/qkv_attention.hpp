@@ -340,17 +340,22 @@ qkv_attention_kernel(QkvAttnArgs a) {
         }
       }
     };
+    // weight tile by weight tile: both token tiles of a weight tile share
+    // its bias reads
+    if (wn == 0) {
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      if (wn == 0) {
-        put(i, 0, 0, 0);
-        put(i, 1, 0, 32);
-        put(i, 2, 1, 0);
-      } else {
-        put(i, 0, 1, 32);
-        put(i, 1, 2, 0);
-        put(i, 2, 2, 32);
-      }
+      for (int i = 0; i < TM; ++i) put(i, 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < TM; ++i) put(i, 1, 0, 32);
+#pragma unroll
+      for (int i = 0; i < TM; ++i) put(i, 2, 1, 0);
+    } else {
+#pragma unroll
+      for (int i = 0; i < TM; ++i) put(i, 0, 1, 32);
+#pragma unroll
+      for (int i = 0; i < TM; ++i) put(i, 1, 2, 0);
+#pragma unroll
+      for (int i = 0; i < TM; ++i) put(i, 2, 2, 32);
     }
 
     // the next pair: its first slice and bias, in flight during the attention
