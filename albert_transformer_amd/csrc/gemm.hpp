@@ -233,7 +233,7 @@ gemm_kernel(GemmArgs g) {
   __shared__ __attribute__((aligned(1024))) char lds3[STAGES > 3 ? STAGE : 16];
   // Epilogue vectors, double-buffered across consecutive tiles, and the
   // LayerNorm cross-wave row reduction.
-  __shared__ float vecs[2][NVEC][BN];
+  __shared__ __attribute__((aligned(16))) float vecs[2][NVEC][BN];
   __shared__ float red[LNE ? (PAIR ? 2 : 1) * WGN * BM : 1];
   // EPI_LN_PAIR: per row, mean and squared deviations of the first half of
   // the features, then of the second
@@ -642,7 +642,7 @@ gemm_kernel(GemmArgs g) {
             const int nl = wn * WTN + j * 32 + 8 * q + 4 * hh;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              const float v = acc[i][j][4 * q + e] + bias_s[nl + e] + rv[q][e];
+              const float v = acc[i][j][4 * q + e] + rv[q][e];  // acc started at the bias
               acc[i][j][4 * q + e] = v;
               s += v;
             }
@@ -970,6 +970,23 @@ gemm_kernel(GemmArgs g) {
       for (int j = 0; j < TN; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+    if constexpr (LNE) {
+      // LayerNorm tiles start their accumulators at the bias: their
+      // epilogue, which holds every accumulator and waits for each LDS read
+      // in turn, then reads no bias, and these reads overlap the first
+      // slice's DMA (about 1 % on both LayerNorm products)
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");  // this tile's vectors are in LDS
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x4 b4 = *reinterpret_cast<const f32x4*>(&vecs[vb][0][wn * WTN + j * 32 + 8 * q + 4 * hh]);
+#pragma unroll
+          for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[i][j][4 * q + e] = b4[e];
+        }
+    }
 
     if constexpr (DEFER) {
       // Two stages; step t waits for slice t, issues slice t+1, then (t < NB)
